@@ -1,0 +1,210 @@
+"""Benchmark: training tokens/s of one forward+backward step of the dense
+decoder (libnc.nc_step_fwd_bwd) on one MI355X, on synthetic inputs.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d20]
+
+Prints ONE JSON line on stdout.  A step is the whole hot path (embedding,
+every layer forward and backward, softcap cross entropy, all parameter
+gradients) over one batch; inputs and weights are resident in HBM before the
+timed region.  Besides the throughput it reports
+  * roofline: the dominant kernel's achieved TFLOP/s against the bf16 matrix
+    peak, timed live with HIP events on the stream it runs on;
+  * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
+    sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/sec (fwd+bwd) at d20 seq 2048 on 1 MI355X; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_device_inputs(cfg, torch, nc):
+    from synthetic import make_inputs
+    inp = make_inputs(cfg)
+    dev = "cuda"
+    names = ("embed", "w_qkv", "w_o", "w_fc", "w_proj", "unembed")
+    if cfg.dtype == "bf16":
+        params = {k: torch.from_numpy(inp["weights_bf16"][k].view(np.int16)).view(torch.bfloat16).to(dev) for k in names}
+    else:
+        params = {k: torch.from_numpy(inp["weights"][k]).to(dev) for k in names}
+    grads = {k: torch.zeros(params[k].shape, dtype=torch.float32, device=dev) for k in names}
+    ids = torch.from_numpy(inp["ids"]).to(dev)
+    tgt = torch.from_numpy(inp["targets"]).to(dev)
+    tb = torch.from_numpy(inp["token_bytes"]).to(dev)
+    ccfg = nc.make_config(cfg)
+    ws = torch.empty(nc.nc_step_workspace_bytes(ccfg), dtype=torch.uint8, device=dev)
+    return inp, ccfg, params, grads, ids, tgt, tb, ws
+
+
+def time_dominant_kernel(cfg, torch, nc, reps=20):
+    """The forward MLP up-projection GEMM with its fused relu^2 epilogue
+    (M = B*T, N = d_ff, K = d_model) -- the largest single launch of the step
+    -- timed with HIP events on the stream it is launched on."""
+    M, d, F = cfg.tokens, cfg.d_model, cfg.d_ff
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(0)
+    m = torch.randn(M, d, device=dev, generator=g).to(torch.bfloat16)
+    w = (torch.randn(F, d, device=dev, generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    u = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    a2 = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    s = torch.cuda.current_stream()
+    for _ in range(3):
+        nc.nc_gemm_bf16(0, 1, M, F, d, m, d, w, d, u, F, epilogue=nc.NC_EPI_RELU2, aux_out=a2, stream=s)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        nc.nc_gemm_bf16(0, 1, M, F, d, m, d, w, d, u, F, epilogue=nc.NC_EPI_RELU2, aux_out=a2, stream=s)
+    e1.record(s)
+    e1.synchronize()
+    avg_s = e0.elapsed_time(e1) / 1e3 / reps
+    flops = 2.0 * M * F * d
+    achieved = flops / avg_s / 1e12
+    return {
+        "kernel": "gemm_mfma_kernel<NT, relu2> (MLP up-projection)",
+        "shape": {"M": M, "N": F, "K": d},
+        "avg_launch_us": avg_s * 1e6,
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": None,
+    }
+
+
+def cpu_baseline(cfg, inp, budget_tokens=None):
+    """The fp64 oracle, untouched, on a bounded sample: forward+backward of the
+    first `n` tokens of sequence 0 with the full model."""
+    import oracle
+    from dense_decoder_only_amd import accounting
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    n = budget_tokens or (256 if cfg.d_model >= 768 else cfg.seq_len)
+    p = oracle.to_f64_params(inp["weights"])
+    ids = inp["ids"][:1, :n]
+    tg = inp["targets"][:1, :n]
+    t0 = time.perf_counter()
+    oracle.step(cfg, p, ids, tg, inp["token_bytes"])
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(n / dt, 3),
+        "unit": "tokens/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle, forward+backward of the first {n} tokens of one sequence, "
+                  f"full {cfg.name} model ({cfg.n_layer} layers, vocab {cfg.vocab}); {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="d20", choices=["tiny", "small", "d12", "d20", "d26"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=None)
+    a = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", a.gpus))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for {a.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synthetic import CONFIGS
+    from dense_decoder_only_amd import accounting, nc
+    nc.load()
+    cfg = CONFIGS[a.config]
+    log(f"[bench] config {cfg.name}: building inputs")
+    inp, ccfg, params, grads, ids, tgt, tb, ws = build_device_inputs(cfg, torch, nc)
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    bpb = torch.empty(1, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+
+    def step():
+        nc.nc_step_fwd_bwd(ccfg, params, grads, 0, ids, tgt, tb, ws, loss, bpb, None, stream=s)
+
+    for i in range(a.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{a.warmup} loss {float(loss):.4f}")
+    if nc.nc_sync_status(ws) != nc.NC_OK:
+        raise RuntimeError("device flag raised during warmup")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(a.steps):
+        step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = e0.elapsed_time(e1) / 1e3
+    elapsed = max(wall, gpu_s)
+    tokens = cfg.tokens * a.steps
+    value = tokens / elapsed
+    flops = accounting.flops_per_step(cfg) * a.steps
+    tflops = flops / elapsed / 1e12
+    log(f"[bench] {a.steps} steps in {elapsed:.3f} s: {value:.0f} tok/s, {tflops:.1f} TFLOP/s "
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.2f}% of bf16 peak), loss {float(loss):.4f} bpb {float(bpb):.4f}")
+
+    roof = time_dominant_kernel(cfg, torch, nc)
+    log(f"[bench] dominant kernel: {roof['achieved']} TFLOP/s ({roof['avg_launch_us']:.0f} us/launch)")
+    base = None
+    if not a.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        base = cpu_baseline(cfg, inp, a.cpu_tokens)
+        log(f"[bench] cpu baseline {base['value']} tok/s on {base['cores']} threads")
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(1e3 * elapsed / a.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Zipf(1.1) token ids, random-init weights)",
+        "config": {
+            "workload": f"{cfg.name}: depth {cfg.n_layer}, d_model {cfg.d_model}, {cfg.n_head} heads x "
+                        f"{cfg.head_dim}, 1 KV head, MLP {cfg.d_ff}, vocab {cfg.vocab}, seq {cfg.seq_len}, "
+                        f"batch {cfg.batch} ({cfg.tokens} tokens/step), fwd+bwd",
+            "global_batch": cfg.batch,
+            "seq_len": cfg.seq_len,
+            "parallelism": "single GPU",
+        },
+        "tflops": round(tflops, 2),
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "roofline_kernel": roof["kernel"],
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

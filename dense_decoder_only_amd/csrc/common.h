@@ -1,0 +1,87 @@
+// Shared device/host helpers for libnc (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <algorithm>
+#include <vector>
+
+#include "../../include/nc.h"
+
+namespace nc {
+
+// ---------------------------------------------------------------------------
+// Element types.  bf16 values travel as raw 16-bit patterns (uint16_t) so that
+// host and device agree bit for bit; conversions round to nearest even.
+// ---------------------------------------------------------------------------
+typedef uint16_t bf16;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(bf16 b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ bf16 f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16)(u >> 16);
+}
+
+// Pack two floats into a 32-bit word of two bf16 (lo = a, hi = b).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<bf16> {
+  __device__ __forceinline__ static float load(const bf16* p) { return bf2f(*p); }
+  __device__ __forceinline__ static void store(bf16* p, float v) { *p = f2bf(v); }
+};
+template <typename T> __device__ __forceinline__ float ld(const T* p) { return Elem<T>::load(p); }
+template <typename T> __device__ __forceinline__ void st(T* p, float v) { Elem<T>::store(p, v); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// Host-side error reporting: every entry point returns an nc_status and leaves
+// a message for nc_last_error() (thread-local).
+// ---------------------------------------------------------------------------
+int set_error(int code, const char* fmt, ...);
+int check_launch(const char* what);
+
+}  // namespace nc
+
+#define NC_REQUIRE(cond, code, ...)                         \
+  do {                                                      \
+    if (!(cond)) return ::nc::set_error((code), __VA_ARGS__); \
+  } while (0)
+
+#define NC_CHECK_HIP(expr)                                                         \
+  do {                                                                             \
+    hipError_t e_ = (expr);                                                        \
+    if (e_ != hipSuccess)                                                          \
+      return ::nc::set_error(NC_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+#define NC_TRY(expr)                 \
+  do {                               \
+    int rc_ = (expr);                \
+    if (rc_ != NC_OK) return rc_;    \
+  } while (0)

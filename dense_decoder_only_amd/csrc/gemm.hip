@@ -1,0 +1,492 @@
+// GEMMs of the training step: every bias-free projection, the relu^2 MLP and
+// the unembedding's weight/activation gradients (release-news page
+// "Karpathy再放大招…", section 技術細節與問答: linear layers carry no bias; the
+// MLP uses relu^2).
+//
+// bf16 path (gfx950 matrix cores): C[M,N] = sum_k A'[m,k] B'[k,n] with fp32
+// accumulation in v_mfma_f32_32x32x16_bf16.
+//   * Block tile 256 x 256 x 64, 256 threads = 4 waves in a 2 x 2 grid, each
+//     wave owning a 128 x 128 sub-tile = 4 x 4 MFMA tiles (256 accumulators
+//     per lane, held in AGPRs).
+//   * Both operands are staged into LDS as [256 rows][64 k] bf16 tiles with
+//     the 16-byte chunk index XOR-swizzled by (row & 7), so the MFMA fragment
+//     reads (one 16-byte ds_read per fragment) and the staging writes are
+//     free of bank conflicts.  Two LDS buffers (128 KB) let the global loads
+//     of tile k+1 overlap the MFMAs of tile k with one barrier per k-tile.
+//   * K-contiguous operands are copied 16 bytes at a time.  M/N-contiguous
+//     operands (the transposed forms used by the backward) are read as 8x8
+//     bf16 blocks (eight 16-byte loads along m), transposed in registers and
+//     written as eight 16-byte LDS rows.
+//   * Epilogues are fused: bf16 or fp32 store, fp32 accumulate (residual
+//     add / gradient accumulation), relu^2 forward (u and relu(u)^2) and
+//     relu^2 backward (acc * 2 relu(u)).
+//   * Tall-K problems with few output tiles (the weight gradients, K = B*T)
+//     split K over blockIdx.z into fp32 partials reduced in a fixed order, so
+//     results are bitwise reproducible.
+#include "common.h"
+#include "gemm.h"
+
+#include <algorithm>
+
+namespace nc {
+
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int NT = 256;
+
+enum { E_STORE_F32 = 0, E_ACC_F32 = 1, E_STORE_BF16 = 2, E_RELU2 = 3, E_RELU2_BWD = 4, E_PARTIAL = 5 };
+
+struct MfmaParams {
+  const bf16* A;
+  const bf16* B;
+  int64_t lda, ldb;
+  int M, N, K;
+  int k_per_split;
+  int tiles_m, tiles_n;
+  void* C;
+  int64_t ldc;
+  const bf16* aux;
+  bf16* aux_out;
+};
+
+// Global -> registers: one 256 x 64 tile of an operand.
+template <bool KC>
+__device__ __forceinline__ void load_tile(const bf16* __restrict__ P, int64_t ld, int r0, int R, int k0,
+                                          int kend, int tid, uint4 (&v)[8]) {
+  if constexpr (KC) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int id = tid + NT * i;
+      const int row = id >> 3, kc = id & 7;
+      int r = r0 + row;
+      r = r < R ? r : R - 1;
+      const int k = k0 + kc * 8;
+      if (k < kend)
+        v[i] = *reinterpret_cast<const uint4*>(P + (int64_t)r * ld + k);
+      else
+        v[i] = make_uint4(0, 0, 0, 0);
+    }
+  } else {
+    const int kb = tid & 7, rb = tid >> 3;
+    int r = r0 + rb * 8;
+    r = r < R ? r : R - 8;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int k = k0 + kb * 8 + kk;
+      if (k < kend)
+        v[kk] = *reinterpret_cast<const uint4*>(P + (int64_t)k * ld + r);
+      else
+        v[kk] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& q, int w) {
+  return w == 0 ? q.x : (w == 1 ? q.y : (w == 2 ? q.z : q.w));
+}
+
+// Registers -> LDS tile [256][64] with the chunk index swizzled by (row & 7).
+template <bool KC>
+__device__ __forceinline__ void store_tile(bf16* __restrict__ S, int tid, const uint4 (&v)[8]) {
+  if constexpr (KC) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int id = tid + NT * i;
+      const int row = id >> 3, kc = id & 7;
+      *reinterpret_cast<uint4*>(S + row * BK + ((kc ^ (row & 7)) << 3)) = v[i];
+    }
+  } else {
+    // v[kk] holds rows rb*8 + 0..7 at k = kb*8 + kk; write row rb*8 + mm with
+    // its eight k values (kk = 0..7) as one 16-byte chunk.
+    const int kb = tid & 7, rb = tid >> 3;
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) {
+      const int w = mm >> 1;
+      uint32_t o[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t a = word_of(v[2 * p], w), b = word_of(v[2 * p + 1], w);
+        o[p] = (mm & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      }
+      const int row = rb * 8 + mm;
+      *reinterpret_cast<uint4*>(S + row * BK + ((kb ^ mm) << 3)) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+// Applies the epilogue to four consecutive columns (col % 4 == 0) of one row.
+template <int EPI>
+__device__ __forceinline__ void epilogue4(const MfmaParams& p, float4 v, int row, int col) {
+  const int64_t off = (int64_t)row * p.ldc + col;
+  if constexpr (EPI == E_STORE_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(p.C) + off) = v;
+  } else if constexpr (EPI == E_ACC_F32) {
+    float4* c = reinterpret_cast<float4*>(static_cast<float*>(p.C) + off);
+    const float4 o = *c;
+    *c = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+  } else if constexpr (EPI == E_STORE_BF16) {
+    *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + off) =
+        make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  } else if constexpr (EPI == E_RELU2) {
+    *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + off) =
+        make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    const float a = fmaxf(v.x, 0.f), b = fmaxf(v.y, 0.f), c = fmaxf(v.z, 0.f), d = fmaxf(v.w, 0.f);
+    *reinterpret_cast<uint2*>(p.aux_out + off) = make_uint2(pack_bf16x2(a * a, b * b), pack_bf16x2(c * c, d * d));
+  } else if constexpr (EPI == E_RELU2_BWD) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p.aux + off);
+    const float u0 = bf2f((bf16)(u.x & 0xffffu)), u1 = bf2f((bf16)(u.x >> 16));
+    const float u2 = bf2f((bf16)(u.y & 0xffffu)), u3 = bf2f((bf16)(u.y >> 16));
+    *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + off) =
+        make_uint2(pack_bf16x2(v.x * 2.f * fmaxf(u0, 0.f), v.y * 2.f * fmaxf(u1, 0.f)),
+                   pack_bf16x2(v.z * 2.f * fmaxf(u2, 0.f), v.w * 2.f * fmaxf(u3, 0.f)));
+  } else {  // E_PARTIAL: [split][M][N] fp32
+    *reinterpret_cast<float4*>(static_cast<float*>(p.C) + (int64_t)blockIdx.z * p.M * p.N +
+                               (int64_t)row * p.N + col) = v;
+  }
+}
+
+template <bool AK, bool BKC, int EPI>
+__global__ __launch_bounds__(NT) void gemm_mfma_kernel(MfmaParams p) {
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * BM * BK];
+  // LDS: A buffers at [0, 2) * BM*BK, B buffers at [2, 4) * BM*BK.
+  bf16* const As = lds;
+  bf16* const Bs = lds + 2 * BM * BK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Consecutive blocks walk down M for a fixed N column of tiles.
+  const int bid = blockIdx.x;
+  const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = blockIdx.z * p.k_per_split;
+  int kend = kbeg + p.k_per_split;
+  kend = kend < p.K ? kend : p.K;
+  const int nk = (kend - kbeg + BK - 1) / BK;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  uint4 ra[8], rb[8];
+  load_tile<AK>(p.A, p.lda, m0, p.M, kbeg, kend, tid, ra);
+  load_tile<BKC>(p.B, p.ldb, n0, p.N, kbeg, kend, tid, rb);
+  store_tile<AK>(As, tid, ra);
+  store_tile<BKC>(Bs, tid, rb);
+  __syncthreads();
+
+  const int frow = lane & 31, fhalf = lane >> 5, fsw = lane & 7;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {
+      load_tile<AK>(p.A, p.lda, m0, p.M, kbeg + (kt + 1) * BK, kend, tid, ra);
+      load_tile<BKC>(p.B, p.ldb, n0, p.N, kbeg + (kt + 1) * BK, kend, tid, rb);
+    }
+    const bf16* a_s = As + cur * (BM * BK) + (wm * 128 + frow) * BK;
+    const bf16* b_s = Bs + cur * (BN * BK) + (wn * 128 + frow) * BK;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = ((ks * 2 + fhalf) ^ fsw) << 3;
+      bf16x8_t fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(a_s + i * 32 * BK + ch);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8_t*>(b_s + j * 32 * BK + ch);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      store_tile<AK>(As + (cur ^ 1) * (BM * BK), tid, ra);
+      store_tile<BKC>(Bs + (cur ^ 1) * (BN * BK), tid, rb);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue, staged through LDS (free after the last barrier) so global
+  // traffic is row-contiguous: per 32-row slab each wave writes its
+  // accumulators into its own [32][SROW] fp32 region and reads them back as
+  // float4 rows.  Lane l of a 32x32 MFMA tile holds column (l & 31) and rows
+  // 8 * (r >> 2) + 4 * (l >> 5) + (r & 3), r = 0..15.
+  constexpr int SROW = 136;  // 128 columns + pad: the two half-waves land on disjoint banks
+  float* stage = reinterpret_cast<float*>(lds) + wave * (32 * SROW);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        stage[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * SROW + j * 32 + (lane & 31)] = acc[i][j][r];
+    __syncthreads();
+    for (int it = 0; it < 16; ++it) {
+      const int idx = it * 64 + lane;
+      const int row = idx >> 5, c4 = (idx & 31) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(stage + row * SROW + c4);
+      const int grow = m0 + wm * 128 + i * 32 + row, gcol = n0 + wn * 128 + c4;
+      if (grow < p.M && gcol < p.N) epilogue4<EPI>(p, v, grow, gcol);
+    }
+    __syncthreads();
+  }
+}
+
+// C[m, n] (+)= sum_z partial[z][m][n], z in increasing order.
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
+                                     float* __restrict__ C, int64_t ldc, int beta) {
+  const int64_t total = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float s = 0.f;
+    for (int z = 0; z < splits; ++z) s += part[(int64_t)z * total + i];
+    const int64_t m = i / N, n = i - m * N;
+    float* c = C + m * ldc + n;
+    *c = beta ? *c + s : s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: a plain LDS-tiled SIMT kernel over generic strides (the fp32
+// configuration is small; this path is about exactness, not speed).
+// A'(m, k) = A[m * sam + k * sak], B'(k, n) = B[k * sbk + n * sbn].
+// ---------------------------------------------------------------------------
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int64_t sam,
+                                                       int64_t sak, const float* __restrict__ B,
+                                                       int64_t sbk, int64_t sbn, int M, int N, int K,
+                                                       float* C, int64_t ldc, const float* aux,
+                                                       float* aux_out) {
+  __shared__ float As[16][65];
+  __shared__ float Bs[16][65];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
+      const int kk = e >> 6, x = e & 63;
+      const int k = k0 + kk;
+      const int m = m0 + x, n = n0 + x;
+      As[kk][x] = (k < K && m < M) ? A[(int64_t)m * sam + (int64_t)k * sak] : 0.f;
+      Bs[kk][x] = (k < K && n < N) ? B[(int64_t)k * sbk + (int64_t)n * sbn] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= N) continue;
+      const int64_t off = (int64_t)m * ldc + n;
+      const float v = acc[i][j];
+      if constexpr (EPI == E_STORE_F32) {
+        C[off] = v;
+      } else if constexpr (EPI == E_ACC_F32) {
+        C[off] += v;
+      } else if constexpr (EPI == E_RELU2) {
+        C[off] = v;
+        const float rl = fmaxf(v, 0.f);
+        aux_out[off] = rl * rl;
+      } else if constexpr (EPI == E_RELU2_BWD) {
+        C[off] = v * 2.f * fmaxf(aux[off], 0.f);
+      }
+    }
+  }
+}
+
+template <bool AK, bool BKC>
+hipError_t launch_mfma(int epi, const MfmaParams& p, int splits, hipStream_t s) {
+  dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
+  dim3 block(NT);
+  switch (epi) {
+    case E_STORE_F32: gemm_mfma_kernel<AK, BKC, E_STORE_F32><<<grid, block, 0, s>>>(p); break;
+    case E_ACC_F32: gemm_mfma_kernel<AK, BKC, E_ACC_F32><<<grid, block, 0, s>>>(p); break;
+    case E_STORE_BF16: gemm_mfma_kernel<AK, BKC, E_STORE_BF16><<<grid, block, 0, s>>>(p); break;
+    case E_RELU2: gemm_mfma_kernel<AK, BKC, E_RELU2><<<grid, block, 0, s>>>(p); break;
+    case E_RELU2_BWD: gemm_mfma_kernel<AK, BKC, E_RELU2_BWD><<<grid, block, 0, s>>>(p); break;
+    default: gemm_mfma_kernel<AK, BKC, E_PARTIAL><<<grid, block, 0, s>>>(p); break;
+  }
+  return hipGetLastError();
+}
+
+int choose_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = cdiv(M, BM) * cdiv(N, BN);
+  if (tiles >= 512 || K < 4096) return 1;
+  int64_t s = cdiv(640, tiles);
+  const int64_t max_s = K / 1024;
+  if (s > max_s) s = max_s;
+  return s < 1 ? 1 : (int)s;
+}
+
+int split_k_per(int64_t K, int splits) { return (int)(cdiv(cdiv(K, splits), BK) * BK); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int s = choose_splits(M, N, K);
+  if (s <= 1) return 0;
+  return (size_t)s * (size_t)M * (size_t)N * sizeof(float);
+}
+
+int gemm(const GemmDesc& g, hipStream_t stream) {
+  NC_REQUIRE(g.A && g.B && g.C, NC_ERR_INVALID_ARG, "gemm: null operand");
+  NC_REQUIRE(g.M > 0 && g.N > 0 && g.K > 0, NC_ERR_INVALID_ARG, "gemm: M, N, K must be positive");
+  NC_REQUIRE(g.M < (1ll << 31) && g.N < (1ll << 31) && g.K < (1ll << 31), NC_ERR_UNSUPPORTED,
+             "gemm: dimensions must be below 2^31");
+  NC_REQUIRE(g.transA == 0 || g.transA == 1, NC_ERR_INVALID_ARG, "gemm: transA must be 0 or 1");
+  NC_REQUIRE(g.transB == 0 || g.transB == 1, NC_ERR_INVALID_ARG, "gemm: transB must be 0 or 1");
+  NC_REQUIRE(g.dtype == NC_F32 || g.dtype == NC_BF16, NC_ERR_INVALID_ARG, "gemm: bad dtype");
+  NC_REQUIRE(g.epi >= NC_EPI_STORE && g.epi <= NC_EPI_RELU2_BWD, NC_ERR_INVALID_ARG, "gemm: bad epilogue");
+  NC_REQUIRE(g.beta == 0.f || g.beta == 1.f, NC_ERR_INVALID_ARG, "gemm: beta must be 0 or 1");
+  const int64_t a_rows = g.transA ? g.K : g.M, a_cols = g.transA ? g.M : g.K;
+  const int64_t b_rows = g.transB ? g.N : g.K, b_cols = g.transB ? g.K : g.N;
+  (void)a_rows; (void)b_rows;
+  NC_REQUIRE(g.lda >= a_cols && g.ldb >= b_cols && g.ldc >= g.N, NC_ERR_INVALID_ARG,
+             "gemm: leading dimension too small");
+  if (g.epi == NC_EPI_RELU2) NC_REQUIRE(g.aux_out, NC_ERR_INVALID_ARG, "gemm: relu2 needs aux_out");
+  if (g.epi == NC_EPI_RELU2_BWD) NC_REQUIRE(g.aux, NC_ERR_INVALID_ARG, "gemm: relu2_bwd needs aux");
+  if (g.beta == 1.f)
+    NC_REQUIRE(g.cdt == NC_F32 && g.epi == NC_EPI_STORE, NC_ERR_INVALID_ARG,
+               "gemm: beta = 1 needs an fp32 C and the plain store epilogue");
+
+  if (g.dtype == NC_F32) {
+    NC_REQUIRE(g.cdt == NC_F32, NC_ERR_INVALID_ARG, "gemm: fp32 operands need an fp32 C");
+    const float* A = static_cast<const float*>(g.A);
+    const float* B = static_cast<const float*>(g.B);
+    const int64_t sam = g.transA ? 1 : g.lda, sak = g.transA ? g.lda : 1;
+    const int64_t sbk = g.transB ? 1 : g.ldb, sbn = g.transB ? g.ldb : 1;
+    dim3 grid((unsigned)cdiv(g.N, 64), (unsigned)cdiv(g.M, 64));
+    float* C = static_cast<float*>(g.C);
+    const float* aux = static_cast<const float*>(g.aux);
+    float* aux_out = static_cast<float*>(g.aux_out);
+    const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
+    if (g.epi == NC_EPI_RELU2)
+      gemm_f32_kernel<E_RELU2><<<grid, 256, 0, stream>>>(A, sam, sak, B, sbk, sbn, M, N, K, C, g.ldc, aux, aux_out);
+    else if (g.epi == NC_EPI_RELU2_BWD)
+      gemm_f32_kernel<E_RELU2_BWD><<<grid, 256, 0, stream>>>(A, sam, sak, B, sbk, sbn, M, N, K, C, g.ldc, aux, aux_out);
+    else if (g.beta == 1.f)
+      gemm_f32_kernel<E_ACC_F32><<<grid, 256, 0, stream>>>(A, sam, sak, B, sbk, sbn, M, N, K, C, g.ldc, aux, aux_out);
+    else
+      gemm_f32_kernel<E_STORE_F32><<<grid, 256, 0, stream>>>(A, sam, sak, B, sbk, sbn, M, N, K, C, g.ldc, aux, aux_out);
+    return check_launch("gemm_f32_kernel");
+  }
+
+  // bf16 matrix-core path
+  NC_REQUIRE(g.M % 8 == 0 && g.N % 8 == 0 && g.K % 8 == 0, NC_ERR_UNSUPPORTED,
+             "gemm: bf16 path needs M, N, K multiples of 8 (got %lld %lld %lld)", (long long)g.M,
+             (long long)g.N, (long long)g.K);
+  NC_REQUIRE(g.lda % 8 == 0 && g.ldb % 8 == 0, NC_ERR_UNSUPPORTED,
+             "gemm: bf16 path needs lda, ldb multiples of 8");
+  NC_REQUIRE(aligned16(g.A) && aligned16(g.B), NC_ERR_INVALID_ARG, "gemm: A and B must be 16-byte aligned");
+  if (g.epi != NC_EPI_STORE) NC_REQUIRE(g.cdt == NC_BF16, NC_ERR_INVALID_ARG, "gemm: relu2 epilogues write bf16");
+
+  MfmaParams p;
+  p.A = static_cast<const bf16*>(g.A);
+  p.B = static_cast<const bf16*>(g.B);
+  p.lda = g.lda;
+  p.ldb = g.ldb;
+  p.M = (int)g.M;
+  p.N = (int)g.N;
+  p.K = (int)g.K;
+  p.tiles_m = (int)cdiv(g.M, BM);
+  p.tiles_n = (int)cdiv(g.N, BN);
+  p.C = g.C;
+  p.ldc = g.ldc;
+  p.aux = static_cast<const bf16*>(g.aux);
+  p.aux_out = static_cast<bf16*>(g.aux_out);
+
+  int epi;
+  if (g.epi == NC_EPI_RELU2) epi = E_RELU2;
+  else if (g.epi == NC_EPI_RELU2_BWD) epi = E_RELU2_BWD;
+  else if (g.cdt == NC_BF16) epi = E_STORE_BF16;
+  else epi = g.beta == 1.f ? E_ACC_F32 : E_STORE_F32;
+
+  int splits = 1;
+  if (epi == E_STORE_F32 || epi == E_ACC_F32) {
+    splits = choose_splits(g.M, g.N, g.K);
+    if (splits > 1 && (g.ws == nullptr || g.ws_bytes < gemm_workspace_bytes(g.M, g.N, g.K))) splits = 1;
+  }
+  p.k_per_split = splits > 1 ? split_k_per(g.K, splits) : (int)g.K;
+  if (splits > 1) splits = (int)cdiv(g.K, p.k_per_split);
+  float* final_c = static_cast<float*>(g.C);
+  const int final_beta = epi == E_ACC_F32;
+  if (splits > 1) {
+    p.C = g.ws;
+    epi = E_PARTIAL;
+  }
+
+  const bool ak = g.transA == 0, bk = g.transB == 1;
+  hipError_t e;
+  if (ak && bk) e = launch_mfma<true, true>(epi, p, splits, stream);
+  else if (ak && !bk) e = launch_mfma<true, false>(epi, p, splits, stream);
+  else if (!ak && bk) e = launch_mfma<false, true>(epi, p, splits, stream);
+  else e = launch_mfma<false, false>(epi, p, splits, stream);
+  if (e != hipSuccess) return set_error(NC_ERR_HIP, "gemm launch failed: %s", hipGetErrorString(e));
+
+  if (splits > 1) {
+    const int64_t total = g.M * g.N;
+    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(total, 256), 4096);
+    splitk_reduce_kernel<<<blocks, 256, 0, stream>>>(static_cast<const float*>(g.ws), splits, p.M, p.N,
+                                                     final_c, g.ldc, final_beta);
+    return check_launch("splitk_reduce_kernel");
+  }
+  return NC_OK;
+}
+
+}  // namespace nc
+
+extern "C" size_t nc_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return nc::gemm_workspace_bytes(M, N, K);
+}
+
+extern "C" int nc_gemm_bf16(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A,
+                            int64_t lda, const void* B, int64_t ldb, void* C, int cdt, int64_t ldc,
+                            float beta, int epilogue, const void* aux, void* aux_out, int dtype,
+                            void* ws, size_t ws_bytes, void* stream) {
+  nc::GemmDesc g;
+  g.transA = transA;
+  g.transB = transB;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.A = A;
+  g.lda = lda;
+  g.B = B;
+  g.ldb = ldb;
+  g.C = C;
+  g.cdt = cdt;
+  g.ldc = ldc;
+  g.beta = beta;
+  g.epi = epilogue;
+  g.aux = aux;
+  g.aux_out = aux_out;
+  g.dtype = dtype;
+  g.ws = ws;
+  g.ws_bytes = ws_bytes;
+  return nc::gemm(g, static_cast<hipStream_t>(stream));
+}

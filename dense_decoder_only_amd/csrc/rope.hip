@@ -1,0 +1,159 @@
+// Rotary position embedding followed by the per-head RMS norm of queries and
+// of the single key head (release-news page "Karpathy再放大招…", section
+// 技術細節與問答: RoPE with no positional embedding; QK norm).
+//
+// Pairing (i, i + hd/2), rotation by +theta(t, i) = t * base^(-2 i / hd), RoPE
+// before the norm.  The (cos, sin) table is computed in fp64 and rounded to
+// fp32 once.  One wavefront per (token, head); lane i < hd/2 owns the pair
+// (i, i + hd/2), so the rotation and the norm need no data exchange beyond
+// one wave-wide sum.  Works in place on the packed [tokens, (H+2) hd] QKV
+// projection output; these kernels are bound by HBM bandwidth.
+#include "common.h"
+
+namespace nc {
+namespace {
+
+__global__ void rope_table_kernel(float* table, int T, int hd, double base) {
+  const int half = hd / 2;
+  const int64_t total = (int64_t)T * half;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)(e / half), i = (int)(e % half);
+    const double th = (double)t * pow(base, -2.0 * (double)i / (double)hd);
+    table[2 * e] = (float)cos(th);
+    table[2 * e + 1] = (float)sin(th);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qkv, int64_t M, int Tlen, int H,
+                                                              int hd, const float* __restrict__ table, float eps,
+                                                              float* __restrict__ rstd_q,
+                                                              float* __restrict__ rstd_k) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int heads = H + 1;
+  if (item >= M * heads) return;
+  const int64_t tok = item / heads;
+  const int head = (int)(item - tok * heads);
+  const int t = (int)(tok % Tlen);
+  const int half = hd >> 1;
+  T* x = qkv + tok * (int64_t)(H + 2) * hd + (int64_t)head * hd;
+  float ya = 0.f, yb = 0.f;
+  if (lane < half) {
+    const float a = ld(x + lane), b = ld(x + lane + half);
+    const float c = table[2 * ((int64_t)t * half + lane)], s = table[2 * ((int64_t)t * half + lane) + 1];
+    ya = a * c - b * s;
+    yb = a * s + b * c;
+  }
+  const float ss = wave_sum(ya * ya + yb * yb);
+  const float r = 1.f / sqrtf(ss / (float)hd + eps);
+  if (lane < half) {
+    st(x + lane, ya * r);
+    st(x + lane + half, yb * r);
+  }
+  if (lane == 0) {
+    if (head < H) rstd_q[tok * H + head] = r;
+    else rstd_k[tok] = r;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_qknorm_bwd_kernel(const float* __restrict__ dhat,
+                                                              const T* __restrict__ yhat,
+                                                              const float* __restrict__ rstd_q,
+                                                              const float* __restrict__ rstd_k,
+                                                              const float* __restrict__ table, int64_t M, int Tlen,
+                                                              int H, int hd, T* __restrict__ dqkv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int heads = H + 2;
+  if (item >= M * heads) return;
+  const int64_t tok = item / heads;
+  const int head = (int)(item - tok * heads);
+  const int64_t base = tok * (int64_t)heads * hd + (int64_t)head * hd;
+  if (head == H + 1) {  // value head: gradient passes through
+    for (int c = lane; c < hd; c += 64) st(dqkv + base + c, dhat[base + c]);
+    return;
+  }
+  const int t = (int)(tok % Tlen);
+  const int half = hd >> 1;
+  float ga = 0.f, gb = 0.f, ya = 0.f, yb = 0.f;
+  if (lane < half) {
+    ga = dhat[base + lane];
+    gb = dhat[base + lane + half];
+    ya = ld(yhat + base + lane);
+    yb = ld(yhat + base + lane + half);
+  }
+  const float mean = wave_sum(ga * ya + gb * yb) / (float)hd;
+  const float r = head < H ? rstd_q[tok * H + head] : rstd_k[tok];
+  if (lane < half) {
+    const float pa = r * (ga - ya * mean), pb = r * (gb - yb * mean);
+    const float c = table[2 * ((int64_t)t * half + lane)], s = table[2 * ((int64_t)t * half + lane) + 1];
+    st(dqkv + base + lane, pa * c + pb * s);          // rotate back by -theta
+    st(dqkv + base + lane + half, -pa * s + pb * c);
+  }
+}
+
+}  // namespace
+
+int rope_table(float* table, int T, int hd, float base, hipStream_t s) {
+  NC_REQUIRE(table, NC_ERR_INVALID_ARG, "rope_table: null pointer");
+  NC_REQUIRE(T > 0 && hd > 0 && hd % 2 == 0, NC_ERR_INVALID_ARG, "rope_table: bad shape");
+  const int64_t total = (int64_t)T * (hd / 2);
+  const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(total, 256), 1024);
+  rope_table_kernel<<<blocks, 256, 0, s>>>(table, T, hd, (double)base);
+  return check_launch("rope_table_kernel");
+}
+
+int rope_qknorm_fwd(void* qkv, int dtype, int B, int T, int H, int hd, const float* table, float eps,
+                    float* rstd_q, float* rstd_k, hipStream_t s) {
+  NC_REQUIRE(qkv && table && rstd_q && rstd_k, NC_ERR_INVALID_ARG, "rope_qknorm_fwd: null pointer");
+  NC_REQUIRE(B > 0 && T > 0 && H > 0, NC_ERR_INVALID_ARG, "rope_qknorm_fwd: bad shape");
+  NC_REQUIRE(hd == 64 || hd == 128, NC_ERR_UNSUPPORTED, "rope_qknorm_fwd: head_dim must be 64 or 128");
+  NC_REQUIRE(dtype == NC_F32 || dtype == NC_BF16, NC_ERR_INVALID_ARG, "rope_qknorm_fwd: bad dtype");
+  const int64_t M = (int64_t)B * T;
+  const unsigned blocks = (unsigned)cdiv(M * (H + 1), 4);
+  if (dtype == NC_F32)
+    rope_qknorm_fwd_kernel<float><<<blocks, 256, 0, s>>>(static_cast<float*>(qkv), M, T, H, hd, table, eps, rstd_q,
+                                                         rstd_k);
+  else
+    rope_qknorm_fwd_kernel<bf16><<<blocks, 256, 0, s>>>(static_cast<bf16*>(qkv), M, T, H, hd, table, eps, rstd_q,
+                                                        rstd_k);
+  return check_launch("rope_qknorm_fwd_kernel");
+}
+
+int rope_qknorm_bwd(const float* dhat, const void* yhat, const float* rstd_q, const float* rstd_k,
+                    const float* table, int dtype, int B, int T, int H, int hd, void* dqkv, hipStream_t s) {
+  NC_REQUIRE(dhat && yhat && rstd_q && rstd_k && table && dqkv, NC_ERR_INVALID_ARG,
+             "rope_qknorm_bwd: null pointer");
+  NC_REQUIRE(B > 0 && T > 0 && H > 0, NC_ERR_INVALID_ARG, "rope_qknorm_bwd: bad shape");
+  NC_REQUIRE(hd == 64 || hd == 128, NC_ERR_UNSUPPORTED, "rope_qknorm_bwd: head_dim must be 64 or 128");
+  NC_REQUIRE(dtype == NC_F32 || dtype == NC_BF16, NC_ERR_INVALID_ARG, "rope_qknorm_bwd: bad dtype");
+  const int64_t M = (int64_t)B * T;
+  const unsigned blocks = (unsigned)cdiv(M * (H + 2), 4);
+  if (dtype == NC_F32)
+    rope_qknorm_bwd_kernel<float><<<blocks, 256, 0, s>>>(dhat, static_cast<const float*>(yhat), rstd_q, rstd_k,
+                                                         table, M, T, H, hd, static_cast<float*>(dqkv));
+  else
+    rope_qknorm_bwd_kernel<bf16><<<blocks, 256, 0, s>>>(dhat, static_cast<const bf16*>(yhat), rstd_q, rstd_k,
+                                                        table, M, T, H, hd, static_cast<bf16*>(dqkv));
+  return check_launch("rope_qknorm_bwd_kernel");
+}
+
+}  // namespace nc
+
+extern "C" int nc_rope_table(float* table, int T, int hd, float base, void* stream) {
+  return nc::rope_table(table, T, hd, base, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int nc_rope_qknorm_fwd(void* qkv, int dtype, int B, int T, int H, int hd, const float* table, float eps,
+                                  float* rstd_q, float* rstd_k, void* stream) {
+  return nc::rope_qknorm_fwd(qkv, dtype, B, T, H, hd, table, eps, rstd_q, rstd_k, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int nc_rope_qknorm_bwd(const float* dqkv_hat, const void* qkv_hat, const float* rstd_q,
+                                  const float* rstd_k, const float* table, int dtype, int B, int T, int H, int hd,
+                                  void* dqkv, void* stream) {
+  return nc::rope_qknorm_bwd(dqkv_hat, qkv_hat, rstd_q, rstd_k, table, dtype, B, T, H, hd, dqkv,
+                             static_cast<hipStream_t>(stream));
+}

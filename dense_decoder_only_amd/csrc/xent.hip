@@ -1,0 +1,314 @@
+// Untied unembedding, tanh logit softcap and cross entropy, reported as the
+// mean loss and as bits per byte.  Release-news page "Karpathy再放大招…",
+// section 技術細節與問答: untied embedding/unembedding, logit softcap;
+// nano-series page "Karpathy 的 nano 諧系", section nanochat: pretraining loss
+// reported in bits per byte.
+//
+//   z = h U^T, z' = c tanh(z / c), lse_t = log sum_v exp(z'_tv),
+//   loss_t = lse_t - z'_{t, y_t}, loss = mean_t loss_t,
+//   bpb = sum_t loss_t / (ln 2 * sum_t bytes[y_t]).
+//
+// The vocabulary is processed in chunks of Vc columns: a matrix-core GEMM
+// writes one [M, Vc] fp32 logit chunk, a row kernel folds it into per-row
+// partial sums (the full [M, V] fp32 logits are never stored).  Because
+// |z'| < c, exp(z' - c) never overflows, so the softmax needs no running
+// maximum: lse = c + log sum exp(z' - c).  Partial sums are added in chunk
+// order and the loss sums in a fixed tree order, so results are bitwise
+// reproducible.  The backward recomputes each logit chunk, forms
+// dz = dloss (softmax(z') - onehot(y)) (1 - (z'/c)^2) in the GEMM operand
+// dtype, and feeds it to dh += dz U_c and dU_c += dz^T h.
+#include "common.h"
+#include "gemm.h"
+#include "ops.h"
+
+namespace nc {
+namespace {
+
+constexpr double kLn2 = 0.69314718055994530942;
+
+int chunk_cols(int64_t M, int V) {
+  int64_t c = ((int64_t)1 << 28) / std::max<int64_t>(M, 1);  // ~1 GiB of fp32 logits per chunk
+  c = c / 256 * 256;
+  if (c < 256) c = 256;
+  if (c > V) c = V;
+  return (int)c;
+}
+
+struct XentWs {
+  float* zbuf;     // [M, Vc] fp32 logit chunk
+  void* dz;        // [M, Vc] dtype (backward)
+  float* partial;  // [nchunks, M]
+  float* ztgt;     // [M]
+  float* ltok;     // [M]
+  void* gemm_ws;
+  size_t gemm_ws_bytes;
+};
+
+size_t carve(int64_t M, int d, int V, XentWs* w, void* base) {
+  const int Vc = chunk_cols(M, V);
+  const int nch = (int)cdiv(V, Vc);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align_up(bytes, 256);
+    return o;
+  };
+  const size_t o_z = take((size_t)M * Vc * 4);
+  const size_t o_dz = take((size_t)M * Vc * 4);
+  const size_t o_p = take((size_t)nch * M * 4);
+  const size_t o_t = take((size_t)M * 4);
+  const size_t o_l = take((size_t)M * 4);
+  const size_t gwb = gemm_workspace_bytes(Vc, d, M);
+  const size_t o_g = take(gwb);
+  if (w) {
+    char* b = static_cast<char*>(base);
+    w->zbuf = reinterpret_cast<float*>(b + o_z);
+    w->dz = b + o_dz;
+    w->partial = reinterpret_cast<float*>(b + o_p);
+    w->ztgt = reinterpret_cast<float*>(b + o_t);
+    w->ltok = reinterpret_cast<float*>(b + o_l);
+    w->gemm_ws = gwb ? b + o_g : nullptr;
+    w->gemm_ws_bytes = gwb;
+  }
+  return off;
+}
+
+// One wavefront per row of the chunk: partial sum of exp(z' - c) and, when
+// the row's target falls in the chunk, z' at the target.
+__global__ __launch_bounds__(256) void xent_fwd_rows_kernel(const float* __restrict__ z, int64_t M, int Vc, int v0,
+                                                            float c, const int32_t* __restrict__ tgt,
+                                                            float* __restrict__ partial,
+                                                            float* __restrict__ ztgt) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float* zr = z + row * Vc;
+  const int y = tgt[row] - v0;
+  const float inv_c = 1.f / c;
+  float s = 0.f;
+  for (int v = lane * 4; v < Vc; v += 256) {
+    const float4 q = *reinterpret_cast<const float4*>(zr + v);
+    const float a = c * tanhf(q.x * inv_c), b = c * tanhf(q.y * inv_c);
+    const float e = c * tanhf(q.z * inv_c), f = c * tanhf(q.w * inv_c);
+    s += expf(a - c) + expf(b - c) + expf(e - c) + expf(f - c);
+    if (y >= v && y < v + 4) ztgt[row] = y == v ? a : (y == v + 1 ? b : (y == v + 2 ? e : f));
+  }
+  s = wave_sum(s);
+  if (lane == 0) partial[row] = s;
+}
+
+__global__ void xent_finish_kernel(const float* __restrict__ partial, int nch, int64_t M, float c,
+                                   const float* __restrict__ ztgt, float* __restrict__ lse,
+                                   float* __restrict__ ltok_ws, float* __restrict__ loss_tok) {
+  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < M; r += (int64_t)gridDim.x * blockDim.x) {
+    float s = 0.f;
+    for (int k = 0; k < nch; ++k) s += partial[(int64_t)k * M + r];
+    const float L = c + logf(s);
+    lse[r] = L;
+    const float lt = L - ztgt[r];
+    ltok_ws[r] = lt;
+    if (loss_tok) loss_tok[r] = lt;
+  }
+}
+
+// Single block: fixed-order sums of the per-token losses and target bytes.
+__global__ __launch_bounds__(1024) void xent_reduce_kernel(const float* __restrict__ ltok, int64_t M,
+                                                           const int32_t* __restrict__ tgt,
+                                                           const float* __restrict__ token_bytes,
+                                                           float default_bytes, float* loss, float* bpb) {
+  __shared__ double sl[1024];
+  __shared__ double sb[1024];
+  double a = 0.0, b = 0.0;
+  for (int64_t i = threadIdx.x; i < M; i += 1024) {
+    a += (double)ltok[i];
+    b += token_bytes ? (double)token_bytes[tgt[i]] : (double)default_bytes;
+  }
+  sl[threadIdx.x] = a;
+  sb[threadIdx.x] = b;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) {
+      sl[threadIdx.x] += sl[threadIdx.x + o];
+      sb[threadIdx.x] += sb[threadIdx.x + o];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    *loss = (float)(sl[0] / (double)M);
+    *bpb = (float)(sl[0] / (kLn2 * sb[0]));
+  }
+}
+
+// dz[t, v] = dloss (exp(z' - lse_t) - [v0 + v == y_t]) (1 - (z'/c)^2).
+template <typename T>
+__global__ __launch_bounds__(256) void xent_bwd_rows_kernel(const float* __restrict__ z, int64_t M, int Vc, int v0,
+                                                            float c, const int32_t* __restrict__ tgt,
+                                                            const float* __restrict__ lse, float dloss,
+                                                            T* __restrict__ dz) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float* zr = z + row * Vc;
+  T* dr = dz + row * Vc;
+  const int y = tgt[row] - v0;
+  const float L = lse[row];
+  const float inv_c = 1.f / c;
+  for (int v = lane; v < Vc; v += 64) {
+    const float th = tanhf(zr[v] * inv_c);
+    const float p = expf(c * th - L);
+    const float g = dloss * (p - (v == y ? 1.f : 0.f)) * (1.f - th * th);
+    st(dr + v, g);
+  }
+}
+
+int validate(const void* h, const void* U, int dtype, const int32_t* tgt, int64_t M, int d, int V) {
+  NC_REQUIRE(h && U && tgt, NC_ERR_INVALID_ARG, "softcap_xent: null pointer");
+  NC_REQUIRE(M > 0 && d > 0 && V > 0, NC_ERR_INVALID_ARG, "softcap_xent: bad shape");
+  NC_REQUIRE(d % 8 == 0 && V % 8 == 0 && M % 8 == 0, NC_ERR_UNSUPPORTED,
+             "softcap_xent: M, d and V must be multiples of 8");
+  NC_REQUIRE(dtype == NC_F32 || dtype == NC_BF16, NC_ERR_INVALID_ARG, "softcap_xent: bad dtype");
+  return NC_OK;
+}
+
+}  // namespace
+
+size_t xent_workspace_bytes(int64_t M, int d, int V) { return carve(M, d, V, nullptr, nullptr); }
+
+int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* token_bytes, int64_t M, int d,
+             int V, float softcap, float* lse, float* loss_tok, float* loss, float* bpb, void* ws, size_t ws_bytes,
+             hipStream_t s) {
+  NC_TRY(validate(h, U, dtype, tgt, M, d, V));
+  NC_REQUIRE(lse && loss && bpb, NC_ERR_INVALID_ARG, "softcap_xent_fwd: null output");
+  NC_REQUIRE(softcap > 0.f, NC_ERR_INVALID_ARG, "softcap_xent_fwd: softcap must be positive");
+  NC_REQUIRE(ws && ws_bytes >= xent_workspace_bytes(M, d, V), NC_ERR_WORKSPACE,
+             "softcap_xent_fwd: workspace too small");
+  XentWs w;
+  carve(M, d, V, &w, ws);
+  const int Vc = chunk_cols(M, V);
+  const int nch = (int)cdiv(V, Vc);
+  const size_t esz = dtype == NC_BF16 ? 2 : 4;
+  for (int k = 0; k < nch; ++k) {
+    const int v0 = k * Vc;
+    const int n = std::min(Vc, V - v0);
+    GemmDesc g;
+    g.transA = 0;
+    g.transB = 1;
+    g.M = M;
+    g.N = n;
+    g.K = d;
+    g.A = h;
+    g.lda = d;
+    g.B = static_cast<const char*>(U) + (size_t)v0 * d * esz;
+    g.ldb = d;
+    g.C = w.zbuf;
+    g.cdt = NC_F32;
+    g.ldc = n;
+    g.dtype = dtype;
+    NC_TRY(gemm(g, s));
+    xent_fwd_rows_kernel<<<(unsigned)cdiv(M, 4), 256, 0, s>>>(w.zbuf, M, n, v0, softcap, tgt,
+                                                              w.partial + (int64_t)k * M, w.ztgt);
+    NC_TRY(check_launch("xent_fwd_rows_kernel"));
+  }
+  xent_finish_kernel<<<(unsigned)std::min<int64_t>(cdiv(M, 256), 4096), 256, 0, s>>>(w.partial, nch, M, softcap,
+                                                                                       w.ztgt, lse, w.ltok, loss_tok);
+  NC_TRY(check_launch("xent_finish_kernel"));
+  xent_reduce_kernel<<<1, 1024, 0, s>>>(w.ltok, M, tgt, token_bytes, 4.8f, loss, bpb);
+  return check_launch("xent_reduce_kernel");
+}
+
+int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* lse, int64_t M, int d, int V,
+             float softcap, float dloss, float* dh, int dh_acc, float* dU, int dU_acc, void* ws, size_t ws_bytes,
+             hipStream_t s) {
+  NC_TRY(validate(h, U, dtype, tgt, M, d, V));
+  NC_REQUIRE(lse && dh && dU, NC_ERR_INVALID_ARG, "softcap_xent_bwd: null pointer");
+  NC_REQUIRE(softcap > 0.f, NC_ERR_INVALID_ARG, "softcap_xent_bwd: softcap must be positive");
+  NC_REQUIRE(ws && ws_bytes >= xent_workspace_bytes(M, d, V), NC_ERR_WORKSPACE,
+             "softcap_xent_bwd: workspace too small");
+  XentWs w;
+  carve(M, d, V, &w, ws);
+  const int Vc = chunk_cols(M, V);
+  const int nch = (int)cdiv(V, Vc);
+  const size_t esz = dtype == NC_BF16 ? 2 : 4;
+  for (int k = 0; k < nch; ++k) {
+    const int v0 = k * Vc;
+    const int n = std::min(Vc, V - v0);
+    const void* Uc = static_cast<const char*>(U) + (size_t)v0 * d * esz;
+    GemmDesc g;
+    g.transA = 0;
+    g.transB = 1;
+    g.M = M;
+    g.N = n;
+    g.K = d;
+    g.A = h;
+    g.lda = d;
+    g.B = Uc;
+    g.ldb = d;
+    g.C = w.zbuf;
+    g.cdt = NC_F32;
+    g.ldc = n;
+    g.dtype = dtype;
+    NC_TRY(gemm(g, s));
+    if (dtype == NC_BF16)
+      xent_bwd_rows_kernel<bf16><<<(unsigned)cdiv(M, 4), 256, 0, s>>>(w.zbuf, M, n, v0, softcap, tgt, lse, dloss,
+                                                                       static_cast<bf16*>(w.dz));
+    else
+      xent_bwd_rows_kernel<float><<<(unsigned)cdiv(M, 4), 256, 0, s>>>(w.zbuf, M, n, v0, softcap, tgt, lse, dloss,
+                                                                        static_cast<float*>(w.dz));
+    NC_TRY(check_launch("xent_bwd_rows_kernel"));
+    // dh (+)= dz U_c  : [M, n] x [n, d]
+    GemmDesc gh;
+    gh.transA = 0;
+    gh.transB = 0;
+    gh.M = M;
+    gh.N = d;
+    gh.K = n;
+    gh.A = w.dz;
+    gh.lda = n;
+    gh.B = Uc;
+    gh.ldb = d;
+    gh.C = dh;
+    gh.cdt = NC_F32;
+    gh.ldc = d;
+    gh.beta = (k > 0 || dh_acc) ? 1.f : 0.f;
+    gh.dtype = dtype;
+    NC_TRY(gemm(gh, s));
+    // dU_c (+)= dz^T h : [n, M] x [M, d]
+    GemmDesc gu;
+    gu.transA = 1;
+    gu.transB = 0;
+    gu.M = n;
+    gu.N = d;
+    gu.K = M;
+    gu.A = w.dz;
+    gu.lda = n;
+    gu.B = h;
+    gu.ldb = d;
+    gu.C = dU + (size_t)v0 * d;
+    gu.cdt = NC_F32;
+    gu.ldc = d;
+    gu.beta = dU_acc ? 1.f : 0.f;
+    gu.dtype = dtype;
+    gu.ws = w.gemm_ws;
+    gu.ws_bytes = w.gemm_ws_bytes;
+    NC_TRY(gemm(gu, s));
+  }
+  return NC_OK;
+}
+
+}  // namespace nc
+
+extern "C" size_t nc_softcap_xent_workspace_bytes(int64_t M, int d, int V) { return nc::xent_workspace_bytes(M, d, V); }
+
+extern "C" int nc_softcap_xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt,
+                                   const float* token_bytes, int64_t M, int d, int V, float softcap, float* lse,
+                                   float* loss_tok, float* loss, float* bpb, void* ws, size_t ws_bytes, void* stream) {
+  return nc::xent_fwd(h, U, dtype, tgt, token_bytes, M, d, V, softcap, lse, loss_tok, loss, bpb, ws, ws_bytes,
+                      static_cast<hipStream_t>(stream));
+}
+
+extern "C" int nc_softcap_xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* lse,
+                                   int64_t M, int d, int V, float softcap, float dloss, float* dh, int dh_accumulate,
+                                   float* dU, int dU_accumulate, void* ws, size_t ws_bytes, void* stream) {
+  return nc::xent_bwd(h, U, dtype, tgt, lse, M, d, V, softcap, dloss, dh, dh_accumulate, dU, dU_accumulate, ws,
+                      ws_bytes, static_cast<hipStream_t>(stream));
+}

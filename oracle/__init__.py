@@ -32,6 +32,8 @@ from .model import (  # noqa: F401
     cross_entropy,
     embed_bwd,
     relu2,
+    relu2_bwd,
+    softcap_xent_bwd,
     sequence_forward,
     sequence_backward,
     step,

@@ -158,6 +158,23 @@ def cross_entropy(zc: np.ndarray, y: np.ndarray):
     return lse - zc[np.arange(zc.shape[0]), y], lse
 
 
+def relu2_bwd(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Gradient through relu(u)^2: g * 2 max(u, 0) (zero at u = 0)."""
+    return g * 2.0 * np.maximum(u, 0.0)
+
+
+def softcap_xent_bwd(zc: np.ndarray, lse: np.ndarray, y: np.ndarray, c: float, dloss: float) -> np.ndarray:
+    """Gradient of dloss * sum_t loss_t w.r.t. the raw logits z (zc = softcap(z)).
+
+    d loss_t / d zc_tv = softmax(zc_t)_v - [v = y_t]; d zc / d z = 1 - tanh^2 = 1 - (zc/c)^2.
+    """
+    T = zc.shape[0]
+    dzc = np.exp(zc - lse[:, None])
+    dzc[np.arange(T), y] -= 1.0
+    dzc *= dloss
+    return dzc * (1.0 - (zc / c) ** 2)
+
+
 def embed_bwd(ids: np.ndarray, de: np.ndarray, V: int) -> np.ndarray:
     """Scatter-add of embedding-row gradients: dE[v] = sum_{t: ids[t]=v} de[t]."""
     dE = np.zeros((V, de.shape[-1]), dtype=de.dtype)
@@ -236,11 +253,7 @@ def sequence_backward(cfg, p: Dict[str, np.ndarray], cache, dloss: float,
     T = y.shape[0]
 
     # cross entropy and softcap
-    pr = np.exp(zc - lse[:, None])
-    dzc = pr
-    dzc[np.arange(T), y] -= 1.0
-    dzc *= dloss
-    dz = dzc * (1.0 - (zc / c) ** 2)          # d/dz [c tanh(z/c)] = 1 - tanh^2
+    dz = softcap_xent_bwd(zc, lse, y, c, dloss)
     grads["unembed"] += dz.T @ h
     dh = dz @ p["unembed"]
     dx = rms_norm_bwd(dh, h, cache["rf"])
@@ -250,7 +263,7 @@ def sequence_backward(cfg, p: Dict[str, np.ndarray], cache, dloss: float,
         # MLP block: x_out = x_mid + relu(m W1^T)^2 W2^T
         grads["w_proj"][l] += dx.T @ C["a2"]
         da2 = dx @ p["w_proj"][l]
-        du = da2 * 2.0 * np.maximum(C["u"], 0.0)
+        du = relu2_bwd(da2, C["u"])
         grads["w_fc"][l] += du.T @ C["m"]
         dm = du @ p["w_fc"][l]
         dx = dx + rms_norm_bwd(dm, C["m"], C["rm"])

@@ -1,0 +1,82 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/nc.h declares, the binding covers exactly those, and host-side
+validation rejects bad arguments before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nc.h")
+LIB = os.path.join(ROOT, "dense_decoder_only_amd", "libnc.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libnc.so not built")
+
+
+def declared_names():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_names()
+    for n in ("nc_embed_fwd", "nc_embed_bwd", "nc_rmsnorm_fwd", "nc_rmsnorm_bwd", "nc_rope_qknorm_fwd",
+              "nc_rope_qknorm_bwd", "nc_mqa_attn_fwd", "nc_mqa_attn_bwd", "nc_relu2_mlp", "nc_gemm_bf16",
+              "nc_softcap_xent_fwd", "nc_softcap_xent_bwd", "nc_step_fwd_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in declared_names() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_the_header():
+    from dense_decoder_only_amd import nc
+    assert sorted(nc.exported_names()) == declared_names()
+
+
+def test_version_and_host_validation():
+    from dense_decoder_only_amd import nc
+    lib = nc.load()
+    assert b"gfx950" in lib.nc_version()
+    # null operands: rejected on the host, nothing enqueued
+    rc = lib.nc_gemm_bf16(0, 1, 256, 256, 256, None, 256, None, 256, None, nc.NC_F32, 256, 0.0,
+                          nc.NC_EPI_STORE, None, None, nc.NC_BF16, None, 0, None)
+    assert rc == nc.NC_ERR_INVALID_ARG
+    assert "null" in nc.nc_last_error()
+    # unsupported head_dim
+    rc = lib.nc_mqa_attn_fwd(ctypes.c_void_p(16), nc.NC_BF16, 1, 64, 2, 96, 0.1, ctypes.c_void_p(16),
+                             ctypes.c_void_p(16), None)
+    assert rc == nc.NC_ERR_UNSUPPORTED
+    # bad beta
+    rc = lib.nc_gemm_bf16(0, 1, 8, 8, 8, ctypes.c_void_p(16), 8, ctypes.c_void_p(16), 8, ctypes.c_void_p(16),
+                          nc.NC_F32, 8, 0.5, nc.NC_EPI_STORE, None, None, nc.NC_BF16, None, 0, None)
+    assert rc == nc.NC_ERR_INVALID_ARG
+
+
+def test_step_workspace_query_and_config_validation():
+    from dense_decoder_only_amd import nc
+    from synthetic import CONFIGS
+    sizes = {}
+    for name, cfg in CONFIGS.items():
+        c = nc.make_config(cfg)
+        sizes[name] = nc.nc_step_workspace_bytes(c)
+        assert sizes[name] > 0
+    assert sizes["d20"] > sizes["d12"] > sizes["small"] > sizes["tiny"]
+    assert sizes["d26"] < 200 * 2 ** 30  # fits one MI355X with the weights
+    bad = nc.make_config(CONFIGS["tiny"])
+    bad.n_kv_head = 2
+    assert nc.nc_step_workspace_bytes(bad) == 0
+    lib = nc.load()
+    p, g = nc.nc_params(), nc.nc_grads()
+    rc = lib.nc_step_fwd_bwd(ctypes.byref(bad), ctypes.byref(p), ctypes.byref(g), None, None, None, None, 0, None,
+                             None, None, None)
+    assert rc == nc.NC_ERR_INVALID_ARG
+    ok = nc.make_config(CONFIGS["tiny"])
+    rc = lib.nc_step_fwd_bwd(ctypes.byref(ok), ctypes.byref(p), ctypes.byref(g), None, None, None, None, 0, None,
+                             None, None, None)
+    assert rc == nc.NC_ERR_INVALID_ARG

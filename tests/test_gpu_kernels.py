@@ -1,0 +1,392 @@
+"""Per-kernel parity: each libnc entry point against the fp64 oracle (or, for
+the plain contractions, a library matmul) on seeded inputs, at sizes that span
+several tiles plus a ragged tail.  The device consumes bf16-rounded inputs in
+the bf16 cases and the reference consumes the same rounded values in fp64, so
+the comparison bounds the kernels' own arithmetic.
+
+Tolerances: fp32 kernels ~1e-5 relative; bf16 outputs one bf16 rounding
+(2^-8 relative) plus accumulation error; fp32 outputs computed from bf16
+operands 1e-2 max-rel (bf16 intermediates such as P or dz)."""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from gpu_util import DEV, assert_close, cosine, dev_to_f64, max_rel, rounded, to_dev
+from synthetic import zipf_ids
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = torch.float32, torch.bfloat16
+DTYPES = [F32, BF16]
+
+
+def nc():
+    from dense_decoder_only_amd import nc as _nc
+    _nc.load()
+    return _nc
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ RMSNorm --
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("rows,d", [(37, 128), (300, 1280), (9, 1664)])
+def test_rmsnorm_fwd_bwd(dtype, rows, d):
+    n = nc()
+    r = rng(rows * d)
+    x = r.standard_normal((rows, d)) * 3.0
+    xg = to_dev(x, F32)
+    y = torch.empty(rows, d, dtype=dtype, device=DEV)
+    rstd = torch.empty(rows, dtype=F32, device=DEV)
+    n.nc_rmsnorm_fwd(xg, y, rstd, eps=1e-6)
+    sync()
+    ref_y, ref_r = oracle.rms_norm(rounded(x, F32), 1e-6)
+    tol = 2 ** -8 if dtype == BF16 else 2e-6
+    assert_close(dev_to_f64(y), ref_y, tol, 1e-6, "rmsnorm y")
+    assert_close(dev_to_f64(rstd), ref_r[:, 0], 2e-6, 0, "rmsnorm rstd")
+
+    g = r.standard_normal((rows, d))
+    gg = to_dev(g, F32)
+    dx = torch.empty(rows, d, dtype=F32, device=DEV)
+    dxb = torch.empty(rows, d, dtype=BF16, device=DEV)
+    n.nc_rmsnorm_bwd(gg, y, rstd, dx, accumulate=0, dx_bf16=dxb)
+    sync()
+    ref = oracle.rms_norm_bwd(rounded(g, F32), dev_to_f64(y), dev_to_f64(rstd)[:, None])
+    assert_close(dev_to_f64(dx), ref, 1e-5, 1e-6, "rmsnorm dx")
+    assert torch.equal(dxb, dx.to(BF16)), "bf16 copy must be the RNE rounding of dx"
+    dx2 = dx.clone()
+    n.nc_rmsnorm_bwd(gg, y, rstd, dx2, accumulate=1)
+    sync()
+    assert_close(dev_to_f64(dx2), 2 * dev_to_f64(dx), 1e-6, 0, "rmsnorm dx accumulate")
+
+
+# ---------------------------------------------------------------- embedding --
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_embed_fwd_gather_is_bit_exact_and_norm_matches(dtype):
+    n = nc()
+    V, d, N = 1000, 264, 777
+    r = rng(5)
+    table = to_dev(r.standard_normal((V, d)), dtype)
+    ids_np = zipf_ids(r, V, N)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    rows = torch.empty(N, d, dtype=dtype, device=DEV)
+    x = torch.empty(N, d, dtype=F32, device=DEV)
+    rs = torch.empty(N, dtype=F32, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    n.nc_embed_fwd(ids, table, rows_out=rows, x_out=x, rstd=rs, eps=1e-6, flag=flag)
+    sync()
+    ref_rows = table[ids.long()]
+    iv = torch.int16 if dtype == BF16 else torch.int32
+    assert torch.equal(rows.view(iv), ref_rows.view(iv)), "gathered rows must be bit-exact"
+    ref_x, _ = oracle.rms_norm(dev_to_f64(ref_rows), 1e-6)
+    assert_close(dev_to_f64(x), ref_x, 2e-6, 1e-7, "embed norm")
+    assert n.nc_sync_status(flag) == n.NC_OK
+
+
+def test_embed_fwd_flags_out_of_range_ids():
+    n = nc()
+    V, d = 64, 128
+    table = to_dev(rng(1).standard_normal((V, d)), BF16)
+    ids = torch.tensor([0, 5, V, -1, 63, 7, 8, 9], dtype=torch.int32, device=DEV)
+    rows = torch.full((8, d), 7.0, dtype=BF16, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    n.nc_embed_fwd(ids, table, rows_out=rows, flag=flag)
+    assert n.nc_sync_status(flag) == n.NC_ERR_DEVICE_FLAG
+    assert torch.all(rows[2] == 0) and torch.all(rows[3] == 0)
+    assert torch.equal(rows[4], table[63])
+
+
+@pytest.mark.parametrize("n_tok,V,d", [(5000, 1000, 264), (1, 16, 128), (70000, 65536, 128)])
+def test_embed_bwd_matches_scatter_add(n_tok, V, d):
+    n = nc()
+    r = rng(n_tok + V)
+    ids_np = zipf_ids(r, V, n_tok)
+    de = r.standard_normal((n_tok, d))
+    ids = torch.from_numpy(ids_np).to(DEV)
+    deg = to_dev(de, F32)
+    dE = torch.full((V, d), float("nan"), dtype=F32, device=DEV)
+    ws = torch.empty(n.nc_embed_bwd_workspace_bytes(n_tok, V, d), dtype=torch.uint8, device=DEV)
+    n.nc_embed_bwd(ids, deg, dE, 0, ws)
+    sync()
+    ref = oracle.embed_bwd(ids_np, rounded(de, F32), V)
+    got = dev_to_f64(dE)
+    absent = np.setdiff1d(np.arange(V), ids_np)
+    assert np.all(got[absent] == 0.0), "rows of absent ids must be exactly zero"
+    assert_close(got, ref, 1e-5, 1e-6, "embed dE")
+    # deterministic: bitwise identical on a second run
+    dE2 = torch.empty_like(dE)
+    n.nc_embed_bwd(ids, deg, dE2, 0, ws)
+    sync()
+    assert torch.equal(dE, dE2)
+    # accumulate: absent rows untouched bit for bit
+    base = to_dev(r.standard_normal((V, d)), F32)
+    acc = base.clone()
+    n.nc_embed_bwd(ids, deg, acc, 1, ws)
+    sync()
+    assert torch.equal(acc[torch.from_numpy(absent).long().to(DEV)], base[torch.from_numpy(absent).long().to(DEV)])
+    assert_close(dev_to_f64(acc), dev_to_f64(base) + ref, 1e-5, 1e-6, "embed dE accumulate")
+
+
+# -------------------------------------------------------------- RoPE + norm --
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("hd,H", [(64, 2), (128, 3), (128, 10)])
+def test_rope_qknorm_fwd_bwd(dtype, hd, H):
+    n = nc()
+    B, T = 2, 100
+    M, Q = B * T, (H + 2) * hd
+    r = rng(hd * H)
+    table = torch.empty(T * hd, dtype=F32, device=DEV)
+    n.nc_rope_table(table, T, hd, 10000.0)
+    th = oracle.rope_angles(T, hd, 10000.0)
+    tab = dev_to_f64(table).reshape(T, hd // 2, 2)
+    assert_close(tab[..., 0], np.cos(th), 0, 1.2e-7, "cos table")
+    assert_close(tab[..., 1], np.sin(th), 0, 1.2e-7, "sin table")
+
+    qkv_np = r.standard_normal((M, Q)) * 2.0
+    qkv = to_dev(qkv_np, dtype)
+    q_in = dev_to_f64(qkv).reshape(B, T, H + 2, hd)
+    rq = torch.empty(M * H, dtype=F32, device=DEV)
+    rk = torch.empty(M, dtype=F32, device=DEV)
+    out = qkv.clone()
+    n.nc_rope_qknorm_fwd(out, B, T, H, hd, table, 1e-6, rq, rk)
+    sync()
+    got = dev_to_f64(out).reshape(B, T, H + 2, hd)
+    tol = 2 ** -8 if dtype == BF16 else 1e-5
+    for b in range(B):
+        ref, _ = oracle.rms_norm(oracle.rope(q_in[b, :, : H + 1], th), 1e-6)
+        assert_close(got[b, :, : H + 1], ref, tol, 1e-5, "rope_qknorm fwd")
+        np.testing.assert_array_equal(got[b, :, H + 1], q_in[b, :, H + 1])  # value head untouched
+
+    g = r.standard_normal((M, Q))
+    dq = torch.empty(M, Q, dtype=dtype, device=DEV)
+    n.nc_rope_qknorm_bwd(to_dev(g, F32), out, rq, rk, table, B, T, H, hd, dq)
+    sync()
+    gq = dev_to_f64(dq).reshape(B, T, H + 2, hd)
+    g4 = rounded(g, F32).reshape(B, T, H + 2, hd)
+    rq4 = dev_to_f64(rq).reshape(B, T, H, 1)
+    rk4 = dev_to_f64(rk).reshape(B, T, 1, 1)
+    for b in range(B):
+        rr = np.concatenate([rq4[b], rk4[b]], axis=1)
+        ref = oracle.rope_bwd(oracle.rms_norm_bwd(g4[b, :, : H + 1], got[b, :, : H + 1], rr), th)
+        assert_close(gq[b, :, : H + 1], ref, 4 * tol, 1e-4, "rope_qknorm bwd")
+        assert_close(gq[b, :, H + 1], g4[b, :, H + 1], tol, 0, "value grad passthrough")
+
+
+# -------------------------------------------------------------- attention --
+
+def _unit_rms(x):
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("B,T,H,hd", [(2, 130, 3, 64), (1, 257, 10, 128), (2, 64, 2, 128)])
+def test_mqa_attention_fwd_bwd(dtype, B, T, H, hd):
+    n = nc()
+    r = rng(T * H + hd)
+    M, Q = B * T, (H + 2) * hd
+    qkv_np = np.empty((M, Q))
+    qkv_np[:, : (H + 1) * hd] = _unit_rms(r.standard_normal((M, H + 1, hd))).reshape(M, -1)
+    qkv_np[:, (H + 1) * hd:] = r.standard_normal((M, hd))
+    qkv = to_dev(qkv_np, dtype)
+    scale = 1 / math.sqrt(hd)
+    o = torch.empty(M, H * hd, dtype=dtype, device=DEV)
+    lse = torch.empty(M * H, dtype=F32, device=DEV)
+    n.nc_mqa_attn_fwd(qkv, B, T, H, hd, scale, o, lse)
+    sync()
+    q4 = dev_to_f64(qkv).reshape(B, T, H + 2, hd)
+    og = dev_to_f64(o).reshape(B, T, H, hd)
+    lg = dev_to_f64(lse).reshape(B, T, H)
+    do_np = r.standard_normal((M, H * hd))
+    dout = to_dev(do_np, dtype)
+    dq = torch.full((M, Q), float("nan"), dtype=F32, device=DEV)
+    ws = torch.empty(n.nc_mqa_attn_bwd_workspace_bytes(B, T, H), dtype=torch.uint8, device=DEV)
+    n.nc_mqa_attn_bwd(qkv, o, dout, lse, B, T, H, hd, scale, dq, ws)
+    sync()
+    dqg = dev_to_f64(dq).reshape(B, T, H + 2, hd)
+    do4 = dev_to_f64(dout).reshape(B, T, H, hd)
+    tol_o = 2 ** -8 if dtype == BF16 else 1e-5
+    tol_g = 2e-2 if dtype == BF16 else 1e-4
+    for b in range(B):
+        q, k, v = q4[b, :, :H], q4[b, :, H:H + 1], q4[b, :, H + 1:]
+        ref_o, P = oracle.attention(q, k, v, scale)
+        assert_close(og[b], ref_o, tol_o, 1e-3 if dtype == BF16 else 1e-6, "attn o")
+        s = np.einsum("thd,ud->htu", q, k[:, 0]) * scale
+        s = np.where(np.tril(np.ones((T, T), bool))[None], s, -np.inf)
+        assert_close(lg[b], scipy.special.logsumexp(s, axis=2).T, 1e-5, 0, "attn lse")
+        dq_r, dk_r, dv_r = oracle.attention_bwd(do4[b], q, k, v, P, scale)
+        for name, got, ref in (("dq", dqg[b, :, :H], dq_r), ("dk", dqg[b, :, H], dk_r[:, 0]),
+                               ("dv", dqg[b, :, H + 1], dv_r[:, 0])):
+            assert max_rel(got, ref) < tol_g, (name, max_rel(got, ref))
+            assert cosine(got, ref) > 0.9999, (name, cosine(got, ref))
+
+
+# ------------------------------------------------------------------- GEMM --
+
+def _gemm_operands(r, ta, tb, M, N, K, dtype):
+    A = r.standard_normal((K, M) if ta else (M, K))
+    Bm = r.standard_normal((N, K) if tb else (K, N))
+    Ad, Bd = to_dev(A, dtype), to_dev(Bm, dtype)
+    A64, B64 = dev_to_f64(Ad), dev_to_f64(Bd)
+    ref = (A64.T if ta else A64) @ (B64.T if tb else B64)
+    return Ad, Bd, ref
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("ta,tb", [(0, 1), (0, 0), (1, 0), (1, 1)])
+@pytest.mark.parametrize("M,N,K", [(264, 392, 200), (512, 256, 1024), (8, 8, 8)])
+def test_gemm_layouts_and_store(dtype, ta, tb, M, N, K):
+    n = nc()
+    r = rng(M + N + K + 10 * ta + tb)
+    A, Bm, ref = _gemm_operands(r, ta, tb, M, N, K, dtype)
+    lda, ldb = (M if ta else K), (K if tb else N)
+    C = torch.full((M, N), float("nan"), dtype=F32, device=DEV)
+    n.nc_gemm_bf16(ta, tb, M, N, K, A, lda, Bm, ldb, C, N)
+    sync()
+    assert_close(dev_to_f64(C), ref, 1e-4 if dtype == BF16 else 1e-5, 1e-5, "gemm fp32 out")
+    # accumulate (beta = 1)
+    C0 = to_dev(r.standard_normal((M, N)), F32)
+    C1 = C0.clone()
+    n.nc_gemm_bf16(ta, tb, M, N, K, A, lda, Bm, ldb, C1, N, beta=1.0)
+    sync()
+    assert_close(dev_to_f64(C1), dev_to_f64(C0) + ref, 1e-4, 1e-5, "gemm accumulate")
+    if dtype == BF16:
+        Cb = torch.empty((M, N), dtype=BF16, device=DEV)
+        n.nc_gemm_bf16(ta, tb, M, N, K, A, lda, Bm, ldb, Cb, N)
+        sync()
+        assert_close(dev_to_f64(Cb), ref, 2 ** -8, 1e-5, "gemm bf16 out")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gemm_relu2_epilogues(dtype):
+    n = nc()
+    M, N, K = 520, 776, 264
+    r = rng(77)
+    A, Bm, ref = _gemm_operands(r, 0, 1, M, N, K, dtype)
+    u = torch.empty((M, N), dtype=dtype, device=DEV)
+    a2 = torch.empty((M, N), dtype=dtype, device=DEV)
+    n.nc_gemm_bf16(0, 1, M, N, K, A, K, Bm, K, u, N, epilogue=n.NC_EPI_RELU2, aux_out=a2)
+    sync()
+    tol = 2 ** -8 if dtype == BF16 else 1e-5
+    assert_close(dev_to_f64(u), ref, tol, 1e-5, "relu2 u")
+    assert_close(dev_to_f64(a2), oracle.relu2(ref), 2 * tol, 1e-5, "relu2 a2")
+    # backward epilogue: C = acc * 2 relu(aux)
+    aux = to_dev(r.standard_normal((M, N)), dtype)
+    C = torch.empty((M, N), dtype=dtype, device=DEV)
+    n.nc_gemm_bf16(0, 1, M, N, K, A, K, Bm, K, C, N, epilogue=n.NC_EPI_RELU2_BWD, aux=aux)
+    sync()
+    assert_close(dev_to_f64(C), oracle.relu2_bwd(ref, dev_to_f64(aux)), tol, 1e-5, "relu2 bwd")
+
+
+def test_gemm_split_k_is_deterministic():
+    n = nc()
+    M, N, K = 256, 520, 16384
+    r = rng(3)
+    A, Bm, ref = _gemm_operands(r, 1, 0, M, N, K, BF16)
+    ws = torch.empty(max(n.nc_gemm_workspace_bytes(M, N, K), 1), dtype=torch.uint8, device=DEV)
+    assert n.nc_gemm_workspace_bytes(M, N, K) > 0, "this shape should take the split-K path"
+    C1 = torch.empty((M, N), dtype=F32, device=DEV)
+    C2 = torch.empty((M, N), dtype=F32, device=DEV)
+    n.nc_gemm_bf16(1, 0, M, N, K, A, M, Bm, N, C1, N, ws=ws)
+    n.nc_gemm_bf16(1, 0, M, N, K, A, M, Bm, N, C2, N, ws=ws)
+    sync()
+    assert torch.equal(C1, C2)
+    assert_close(dev_to_f64(C1), ref, 1e-4, 1e-5, "split-K gemm")
+    C3 = torch.empty((M, N), dtype=F32, device=DEV)
+    n.nc_gemm_bf16(1, 0, M, N, K, A, M, Bm, N, C3, N)  # no workspace: single pass
+    sync()
+    assert_close(dev_to_f64(C3), ref, 1e-4, 1e-5, "unsplit gemm")
+
+
+# ------------------------------------------------------ relu^2 MLP block --
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_relu2_mlp_fwd_bwd(dtype):
+    n = nc()
+    M, d, F = 264, 256, 1024
+    r = rng(11)
+    m = to_dev(r.standard_normal((M, d)), dtype)
+    w1 = to_dev(r.standard_normal((F, d)) / 16, dtype)
+    w2 = to_dev(r.standard_normal((d, F)) / 32, dtype)
+    x0 = r.standard_normal((M, d))
+    x = to_dev(x0, F32)
+    u = torch.empty(M, F, dtype=dtype, device=DEV)
+    a2 = torch.empty(M, F, dtype=dtype, device=DEV)
+    n.nc_relu2_mlp(m, w1, w2, x, u, a2)
+    sync()
+    m64, w164, w264 = dev_to_f64(m), dev_to_f64(w1), dev_to_f64(w2)
+    u_ref = m64 @ w164.T
+    a2_ref = oracle.relu2(u_ref)
+    tol = 2 ** -8 if dtype == BF16 else 1e-5
+    assert_close(dev_to_f64(u), u_ref, tol, 1e-5, "mlp u")
+    # the device projects its own (rounded) a2
+    x_ref = rounded(x0, F32) + dev_to_f64(a2) @ w264.T
+    assert_close(dev_to_f64(x), x_ref, 1e-4, 1e-5, "mlp residual")
+    g = to_dev(r.standard_normal((M, d)), dtype)
+    dm = torch.empty(M, d, dtype=F32, device=DEV)
+    dw1 = torch.empty(F, d, dtype=F32, device=DEV)
+    dw2 = torch.empty(d, F, dtype=F32, device=DEV)
+    du = torch.empty(M, F, dtype=dtype, device=DEV)
+    n.nc_relu2_mlp_bwd(g, m, u, a2, w1, w2, dm, dw1, dw2, 0, du)
+    sync()
+    g64 = dev_to_f64(g)
+    du_ref = oracle.relu2_bwd(g64 @ w264, dev_to_f64(u))
+    assert_close(dev_to_f64(dw2), g64.T @ dev_to_f64(a2), 1e-4, 1e-5, "mlp dW2")
+    assert_close(dev_to_f64(du), du_ref, tol, 1e-4, "mlp du")
+    du64 = dev_to_f64(du)
+    assert_close(dev_to_f64(dw1), du64.T @ m64, 1e-4, 1e-5, "mlp dW1")
+    assert_close(dev_to_f64(dm), du64 @ w164, 1e-4, 1e-5, "mlp dm")
+
+
+# ------------------------------------------------- softcap cross entropy --
+
+@pytest.mark.parametrize("dtype,M,d,V,ustd", [(F32, 512, 256, 8192, 1.0), (BF16, 512, 256, 8192, 1.0),
+                                              (BF16, 8192, 128, 40960, 1.0), (BF16, 264, 128, 1024, 20.0)])
+def test_softcap_xent_fwd_bwd(dtype, M, d, V, ustd):
+    n = nc()
+    r = rng(M + V)
+    c = 15.0
+    h = to_dev(_unit_rms(r.standard_normal((M, d))), dtype)
+    U = to_dev(r.standard_normal((V, d)) * ustd / math.sqrt(d), dtype)
+    y_np = zipf_ids(r, V, M)
+    y = torch.from_numpy(y_np).to(DEV)
+    tb_np = np.full(V, 4.8, np.float32)
+    tb_np[::7] = 2.0  # a non-constant byte table
+    tb = torch.from_numpy(tb_np).to(DEV)
+    ws = torch.empty(n.nc_softcap_xent_workspace_bytes(M, d, V), dtype=torch.uint8, device=DEV)
+    lse = torch.empty(M, dtype=F32, device=DEV)
+    ltok = torch.empty(M, dtype=F32, device=DEV)
+    loss = torch.empty(1, dtype=F32, device=DEV)
+    bpb = torch.empty(1, dtype=F32, device=DEV)
+    n.nc_softcap_xent_fwd(h, U, y, tb, c, lse, ltok, loss, bpb, ws)
+    sync()
+    h64, U64 = dev_to_f64(h), dev_to_f64(U)
+    zc = oracle.softcap(h64 @ U64.T, c)
+    assert np.all(np.abs(zc) < c + 1e-12)
+    lt_ref, lse_ref = oracle.cross_entropy(zc, y_np)
+    assert_close(dev_to_f64(lse), lse_ref, 2e-6, 0, "xent lse")
+    assert_close(dev_to_f64(ltok), lt_ref, 1e-5, 1e-5, "xent loss_tok")
+    assert float(loss) == pytest.approx(lt_ref.mean(), rel=1e-5)
+    assert float(bpb) == pytest.approx(lt_ref.sum() / (math.log(2) * tb_np[y_np].astype(np.float64).sum()), rel=1e-5)
+
+    dh = torch.empty(M, d, dtype=F32, device=DEV)
+    dU = torch.empty(V, d, dtype=F32, device=DEV)
+    n.nc_softcap_xent_bwd(h, U, y, lse, c, 1.0 / M, dh, 0, dU, 0, ws)
+    sync()
+    dz = oracle.softcap_xent_bwd(zc, lse_ref, y_np, c, 1.0 / M)
+    tol = 1e-2 if dtype == BF16 else 1e-4
+    for name, got, ref in (("dh", dev_to_f64(dh), dz @ U64), ("dU", dev_to_f64(dU), dz.T @ h64)):
+        assert max_rel(got, ref) < tol, (name, max_rel(got, ref))
+        assert cosine(got, ref) > 0.9999, (name, cosine(got, ref))

@@ -39,8 +39,10 @@ MUTATIONS = [
     ("sequence_forward", "x = x + a2 @ p[\"w_proj\"][l].T", "x = a2 @ p[\"w_proj\"][l].T"),
     ("sequence_forward", "h, rf = rms_norm(x, eps)", "h, rf = x, 1.0"),
     ("sequence_forward", "a2 = relu2(u)", "a2 = relu2(-u)"),
-    ("sequence_backward", "dz = dzc * (1.0 - (zc / c) ** 2)", "dz = dzc"),
-    ("sequence_backward", "du = da2 * 2.0 * np.maximum(C[\"u\"], 0.0)", "du = da2 * np.maximum(C[\"u\"], 0.0)"),
+    ("softcap_xent_bwd", "return dzc * (1.0 - (zc / c) ** 2)", "return dzc"),
+    ("softcap_xent_bwd", "dzc[np.arange(T), y] -= 1.0", "dzc[np.arange(T), y] -= 0.0"),
+    ("relu2_bwd", "g * 2.0 * np.maximum(u, 0.0)", "g * np.maximum(u, 0.0)"),
+    ("relu2_bwd", "g * 2.0 * np.maximum(u, 0.0)", "g * 2.0 * np.abs(u)"),
     ("sequence_backward", "dx = dx + rms_norm_bwd(dm, C[\"m\"], C[\"rm\"])", "dx = rms_norm_bwd(dm, C[\"m\"], C[\"rm\"])"),
     ("sequence_backward", "grads[\"w_o\"][l] += dx.T @ C[\"of\"]", "grads[\"w_o\"][l] += C[\"of\"].T @ dx"),
     ("sequence_backward", "dq = rope_bwd(rms_norm_bwd(dqn, C[\"qn\"], C[\"rq\"]), theta)",
