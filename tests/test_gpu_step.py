@@ -70,7 +70,8 @@ def test_step_deterministic_accumulating_and_causal():
     acc = {k: v.clone() for k, v in a["grads"].items()}
     c = run_step(cfg, inp, accumulate=1, grads=acc)
     for k in acc:
-        torch.testing.assert_close(c["grads"][k], 2 * a["grads"][k], rtol=1e-6, atol=0)
+        # (base + p1) + p2 vs base + (p1 + p2): equal up to fp32 rounding
+        torch.testing.assert_close(c["grads"][k], 2 * a["grads"][k], rtol=1e-5, atol=1e-12)
     # future tokens do not change earlier per-token losses, bit for bit
     S = inp["S"].copy()
     t0 = 200
