@@ -9,12 +9,14 @@
 // against the same keys, so the kernels index query rows r = t*H + h of a
 // sequence and map each to its position t = r / H.
 //
-// This file holds the direct (scalar) kernels: one wavefront per query row
-// (forward, dQ) or per key row (dK, dV), keys or query rows processed in
-// chunks of 64 with the probabilities shared through LDS.  They serve the
-// fp32 configuration and any shape the matrix-core kernels do not cover.
+// bf16 with head_dim 128 runs on the matrix-core kernels of attn_mfma.hip.
+// This file holds the direct (scalar) kernels used otherwise (the fp32
+// configuration, head_dim 64): one wavefront per query row (forward, dQ) or
+// per key row (dK, dV), keys or query rows processed in chunks of 64 with the
+// probabilities shared through LDS.
 #include "common.h"
 #include "ops.h"
+#include "attn_mfma.h"
 
 namespace nc {
 namespace {
@@ -229,7 +231,7 @@ int validate(const void* qkv, int dtype, int B, int T, int H, int hd) {
 }  // namespace
 
 size_t mqa_attn_bwd_workspace_bytes(int B, int T, int H) {
-  return align_up((size_t)B * T * H * sizeof(float), 256);
+  return std::max(align_up((size_t)B * T * H * sizeof(float), 256), attn_mfma_bwd_workspace_bytes(B, T, H));
 }
 
 int mqa_attn_fwd(const void* qkv, int dtype, int B, int T, int H, int hd, float scale, void* o, float* lse,
@@ -237,6 +239,7 @@ int mqa_attn_fwd(const void* qkv, int dtype, int B, int T, int H, int hd, float 
   NC_TRY(validate(qkv, dtype, B, T, H, hd));
   NC_REQUIRE(o && lse, NC_ERR_INVALID_ARG, "mqa_attn_fwd: null output");
   if (dtype == NC_F32) return fwd_simple<float>(qkv, B, T, H, hd, scale, o, lse, s);
+  if (hd == 128) return attn_mfma_fwd(qkv, B, T, H, scale, o, lse, s);
   return fwd_simple<bf16>(qkv, B, T, H, hd, scale, o, lse, s);
 }
 
@@ -248,6 +251,7 @@ int mqa_attn_bwd(const void* qkv, const void* o, const void* dout, const float* 
              "mqa_attn_bwd: workspace too small (%zu < %zu)", ws_bytes, mqa_attn_bwd_workspace_bytes(B, T, H));
   float* Dbuf = static_cast<float*>(ws);
   if (dtype == NC_F32) return bwd_simple<float>(qkv, o, dout, lse, B, T, H, hd, scale, dqkv, Dbuf, s);
+  if (hd == 128) return attn_mfma_bwd(qkv, o, dout, lse, B, T, H, scale, dqkv, ws, s);
   return bwd_simple<bf16>(qkv, o, dout, lse, B, T, H, hd, scale, dqkv, Dbuf, s);
 }
 

@@ -192,7 +192,8 @@ def _unit_rms(x):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("B,T,H,hd", [(2, 130, 3, 64), (1, 257, 10, 128), (2, 64, 2, 128)])
+@pytest.mark.parametrize("B,T,H,hd", [(2, 130, 3, 64), (1, 257, 10, 128), (2, 64, 2, 128), (3, 200, 13, 128),
+                                      (1, 1100, 10, 128)])
 def test_mqa_attention_fwd_bwd(dtype, B, T, H, hd):
     n = nc()
     r = rng(T * H + hd)
@@ -225,7 +226,7 @@ def test_mqa_attention_fwd_bwd(dtype, B, T, H, hd):
         assert_close(og[b], ref_o, tol_o, 1e-3 if dtype == BF16 else 1e-6, "attn o")
         s = np.einsum("thd,ud->htu", q, k[:, 0]) * scale
         s = np.where(np.tril(np.ones((T, T), bool))[None], s, -np.inf)
-        assert_close(lg[b], scipy.special.logsumexp(s, axis=2).T, 1e-5, 0, "attn lse")
+        assert_close(lg[b], scipy.special.logsumexp(s, axis=2).T, 1e-5, 1e-6, "attn lse")
         dq_r, dk_r, dv_r = oracle.attention_bwd(do4[b], q, k, v, P, scale)
         for name, got, ref in (("dq", dqg[b, :, :H], dq_r), ("dk", dqg[b, :, H], dk_r[:, 0]),
                                ("dv", dqg[b, :, H + 1], dv_r[:, 0])):
