@@ -6,7 +6,7 @@
 #include <algorithm>
 #include <vector>
 
-#include "../../include/nc.h"
+#include "nc.h"
 
 namespace nc {
 

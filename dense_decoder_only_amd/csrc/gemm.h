@@ -25,5 +25,7 @@ struct GemmDesc {
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int gemm(const GemmDesc& g, hipStream_t stream);
+// dst [C, R] = src [R, C]^T for 2- or 4-byte elements.
+int transpose(const void* src, int64_t R, int64_t C, int elem_bytes, void* dst, hipStream_t s);
 
 }  // namespace nc

@@ -19,7 +19,8 @@
 //     written as eight 16-byte LDS rows.
 //   * Epilogues are fused: bf16 or fp32 store, fp32 accumulate (residual
 //     add / gradient accumulation), relu^2 forward (u and relu(u)^2) and
-//     relu^2 backward (acc * 2 relu(u)).
+//     relu^2 backward (acc * 2 relu(u)); they are staged through LDS so that
+//     global stores are 16-byte and row-contiguous.
 //   * Tall-K problems with few output tiles (the weight gradients, K = B*T)
 //     split K over blockIdx.z into fp32 partials reduced in a fixed order, so
 //     results are bitwise reproducible.
@@ -34,6 +35,13 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int NT = 256;
+
+#ifndef NC_GEMM_SWZ
+#define NC_GEMM_SWZ 1
+#endif
+// LDS chunk swizzle of a [256][64] bf16 tile: 16-byte chunk c of `row` lives
+// at chunk c ^ swz(row).
+__host__ __device__ constexpr int swz(int row) { return NC_GEMM_SWZ ? ((row >> 1) & 7) : (row & 7); }
 
 enum { E_STORE_F32 = 0, E_ACC_F32 = 1, E_STORE_BF16 = 2, E_RELU2 = 3, E_RELU2_BWD = 4, E_PARTIAL = 5 };
 
@@ -94,7 +102,7 @@ __device__ __forceinline__ void store_tile(bf16* __restrict__ S, int tid, const 
     for (int i = 0; i < 8; ++i) {
       const int id = tid + NT * i;
       const int row = id >> 3, kc = id & 7;
-      *reinterpret_cast<uint4*>(S + row * BK + ((kc ^ (row & 7)) << 3)) = v[i];
+      *reinterpret_cast<uint4*>(S + row * BK + ((kc ^ swz(row)) << 3)) = v[i];
     }
   } else {
     // v[kk] holds rows rb*8 + 0..7 at k = kb*8 + kk; write row rb*8 + mm with
@@ -110,8 +118,37 @@ __device__ __forceinline__ void store_tile(bf16* __restrict__ S, int tid, const 
         o[p] = (mm & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
       }
       const int row = rb * 8 + mm;
-      *reinterpret_cast<uint4*>(S + row * BK + ((kb ^ mm) << 3)) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(S + row * BK + ((kb ^ swz(row)) << 3)) = make_uint4(o[0], o[1], o[2], o[3]);
     }
+  }
+}
+
+#ifndef NC_GEMM_DIRECT
+#define NC_GEMM_DIRECT 1  // K-contiguous tiles go global -> LDS without VGPR staging
+#endif
+#ifndef NC_GEMM_XCD
+#define NC_GEMM_XCD 1     // XCD-aware grouped tile order
+#endif
+#ifndef NC_GEMM_GROUP_M
+#define NC_GEMM_GROUP_M 4
+#endif
+
+// Direct global -> LDS staging of a K-contiguous 256 x 64 tile with gfx950's
+// global_load_lds_dwordx4.  Each wave moves 8 groups of 8 rows (1 KB per
+// instruction); lane i of a group lands at byte 16 i of the group, i.e. at
+// row i / 8 of the group, physical chunk i % 8, so it fetches the logical
+// chunk (i % 8) ^ swz(row) that the swizzle puts there.
+__device__ __forceinline__ void stage_direct(const bf16* __restrict__ P, int64_t ld, int r0, int R, int k0, bf16* S,
+                                             int wave, int lane) {
+  const int rsub = lane >> 3;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int grp = wave * 8 + i;
+    const int c = (lane & 7) ^ swz(grp * 8 + rsub);
+    int r = r0 + grp * 8 + rsub;
+    r = r < R ? r : R - 1;
+    __builtin_amdgcn_global_load_lds(P + (int64_t)r * ld + k0 + c * 8,
+                                     (__attribute__((address_space(3))) void*)(S + grp * 8 * BK), 16, 0, 0);
   }
 }
 
@@ -146,8 +183,10 @@ __device__ __forceinline__ void epilogue4(const MfmaParams& p, float4 v, int row
   }
 }
 
-template <bool AK, bool BKC, int EPI>
-__global__ __launch_bounds__(NT) void gemm_mfma_kernel(MfmaParams p) {
+// DIRECT: every k-tile is full (K and the split length are multiples of BK),
+// so K-contiguous operands can use the direct global -> LDS path.
+template <bool AK, bool BKC, int EPI, bool DIRECT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_mfma_kernel(MfmaParams p) {
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * BM * BK];
   // LDS: A buffers at [0, 2) * BM*BK, B buffers at [2, 4) * BM*BK.
   bf16* const As = lds;
@@ -157,14 +196,30 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(MfmaParams p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Consecutive blocks walk down M for a fixed N column of tiles.
-  const int bid = blockIdx.x;
+  // Tile order.  Blocks are dealt round-robin to the 8 XCDs (each with its own
+  // L2); remap so every XCD gets a contiguous run of the grouped order, in
+  // which GROUP_M row tiles sweep the column tiles together, so the A and B
+  // k-slices a run needs are shared in that XCD's L2.
+  int bid = blockIdx.x;
+#if NC_GEMM_XCD
+  {
+    const int nb = p.tiles_m * p.tiles_n;
+    const int per = nb >> 3;
+    if (bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
+  }
+  const int gsize = NC_GEMM_GROUP_M * p.tiles_n;
+  const int first_m = (bid / gsize) * NC_GEMM_GROUP_M;
+  const int gm = min(p.tiles_m - first_m, NC_GEMM_GROUP_M);
+  const int tm = first_m + (bid % gsize) % gm, tn = (bid % gsize) / gm;
+#else
   const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
+#endif
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = blockIdx.z * p.k_per_split;
   int kend = kbeg + p.k_per_split;
   kend = kend < p.K ? kend : p.K;
   const int nk = (kend - kbeg + BK - 1) / BK;
+  constexpr bool kDirA = AK && DIRECT && NC_GEMM_DIRECT, kDirB = BKC && DIRECT && NC_GEMM_DIRECT;
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -175,64 +230,278 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(MfmaParams p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   uint4 ra[8], rb[8];
-  load_tile<AK>(p.A, p.lda, m0, p.M, kbeg, kend, tid, ra);
-  load_tile<BKC>(p.B, p.ldb, n0, p.N, kbeg, kend, tid, rb);
-  store_tile<AK>(As, tid, ra);
-  store_tile<BKC>(Bs, tid, rb);
-  __syncthreads();
-
-  const int frow = lane & 31, fhalf = lane >> 5, fsw = lane & 7;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      load_tile<AK>(p.A, p.lda, m0, p.M, kbeg + (kt + 1) * BK, kend, tid, ra);
-      load_tile<BKC>(p.B, p.ldb, n0, p.N, kbeg + (kt + 1) * BK, kend, tid, rb);
+  {
+    const bool full = DIRECT || kbeg + BK <= kend;
+    if (kDirA && full) {
+      stage_direct(p.A, p.lda, m0, p.M, kbeg, As, wave, lane);
+    } else {
+      load_tile<AK>(p.A, p.lda, m0, p.M, kbeg, kend, tid, ra);
+      store_tile<AK>(As, tid, ra);
     }
+    if (kDirB && full) {
+      stage_direct(p.B, p.ldb, n0, p.N, kbeg, Bs, wave, lane);
+    } else {
+      load_tile<BKC>(p.B, p.ldb, n0, p.N, kbeg, kend, tid, rb);
+      store_tile<BKC>(Bs, tid, rb);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  const int frow = lane & 31, fhalf = lane >> 5, fsw = swz(lane & 31);
+  // Register-path LDS writes per k-tile (direct staging needs none).
+  constexpr int kWrites = (kDirA ? 0 : 8) + (kDirB ? 0 : 8);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1, nxt = cur ^ 1;
+    // The loop body has no branches so that it is one scheduling region: the
+    // last iteration re-stages the first tile (in bounds) into the idle buffer.
+    const int k1 = kt + 1 < nk ? kbeg + (kt + 1) * BK : kbeg;
+    if (kDirA) stage_direct(p.A, p.lda, m0, p.M, k1, As + nxt * (BM * BK), wave, lane);
+    else load_tile<AK>(p.A, p.lda, m0, p.M, k1, kend, tid, ra);
+    if (kDirB) stage_direct(p.B, p.ldb, n0, p.N, k1, Bs + nxt * (BN * BK), wave, lane);
+    else load_tile<BKC>(p.B, p.ldb, n0, p.N, k1, kend, tid, rb);
+
     const bf16* a_s = As + cur * (BM * BK) + (wm * 128 + frow) * BK;
     const bf16* b_s = Bs + cur * (BN * BK) + (wn * 128 + frow) * BK;
+    // Fragments for k-step ks + 1 are read from LDS while the 16 MFMAs of
+    // step ks issue (two register sets), so LDS latency stays hidden.
+    bf16x8_t fa[2][4], fb[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa[0][i] = *reinterpret_cast<const bf16x8_t*>(a_s + i * 32 * BK + ((fhalf ^ fsw) << 3));
+      fb[0][i] = *reinterpret_cast<const bf16x8_t*>(b_s + i * 32 * BK + ((fhalf ^ fsw) << 3));
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 reads of step 0 first
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int ch = ((ks * 2 + fhalf) ^ fsw) << 3;
-      bf16x8_t fa[4], fb[4];
+      const int c = ks & 1;
+      if (ks + 1 < 4) {
+        const int ch = (((ks + 1) * 2 + fhalf) ^ fsw) << 3;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(a_s + i * 32 * BK + ch);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8_t*>(b_s + j * 32 * BK + ch);
+        for (int i = 0; i < 4; ++i) {
+          fa[c ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(a_s + i * 32 * BK + ch);
+          fb[c ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(b_s + i * 32 * BK + ch);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][i], acc[i][j], 0, 0, 0);
+      if (ks + 1 < 4) {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read (next step)
+        }
+      }
     }
-    if (kt + 1 < nk) {
-      store_tile<AK>(As + (cur ^ 1) * (BM * BK), tid, ra);
-      store_tile<BKC>(Bs + (cur ^ 1) * (BN * BK), tid, rb);
+    if (!kDirA) store_tile<AK>(As + nxt * (BM * BK), tid, ra);
+    if (!kDirB) store_tile<BKC>(Bs + nxt * (BN * BK), tid, rb);
+    // last k-step: interleave the staging writes of the next tile
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (g < kWrites) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   // Epilogue, staged through LDS (free after the last barrier) so global
-  // traffic is row-contiguous: per 32-row slab each wave writes its
-  // accumulators into its own [32][SROW] fp32 region and reads them back as
-  // float4 rows.  Lane l of a 32x32 MFMA tile holds column (l & 31) and rows
-  // 8 * (r >> 2) + 4 * (l >> 5) + (r & 3), r = 0..15.
-  constexpr int SROW = 136;  // 128 columns + pad: the two half-waves land on disjoint banks
+  // traffic is row-contiguous.  The MFMAs above take B as their first operand,
+  // so tile (i, j) is computed transposed: lane l holds output row
+  // 32 i + (l & 31) and, in registers 4 q .. 4 q + 3, the four consecutive
+  // columns 32 j + 8 q + 4 (l >> 5) + 0..3 -- one 16-byte LDS write each.
+  // Per 32-row slab every wave writes its [32][SROW] fp32 region, then reads
+  // it back as float4 along rows.
+  constexpr int SROW = 132;  // 128 columns + pad: 16 consecutive rows hit distinct banks
   float* stage = reinterpret_cast<float*>(lds) + wave * (32 * SROW);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        stage[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * SROW + j * 32 + (lane & 31)] = acc[i][j][r];
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(stage + (lane & 31) * SROW + j * 32 + 8 * q + 4 * (lane >> 5)) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
     __syncthreads();
     for (int it = 0; it < 16; ++it) {
       const int idx = it * 64 + lane;
       const int row = idx >> 5, c4 = (idx & 31) * 4;
       const float4 v = *reinterpret_cast<const float4*>(stage + row * SROW + c4);
       const int grow = m0 + wm * 128 + i * 32 + row, gcol = n0 + wn * 128 + c4;
+      if (grow < p.M && gcol < p.N) epilogue4<EPI>(p, v, grow, gcol);
+    }
+    __syncthreads();
+  }
+}
+
+// 8-wave form of stage_direct: each of the 8 waves moves 4 groups of 8 rows.
+__device__ __forceinline__ void stage_direct8(const bf16* __restrict__ P, int64_t ld, int r0, int R, int k0, bf16* S,
+                                              int wave, int lane) {
+  const int rsub = lane >> 3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int grp = wave * 4 + i;
+    const int c = (lane & 7) ^ swz(grp * 8 + rsub);
+    int r = r0 + grp * 8 + rsub;
+    r = r < R ? r : R - 1;
+    __builtin_amdgcn_global_load_lds(P + (int64_t)r * ld + k0 + c * 8,
+                                     (__attribute__((address_space(3))) void*)(S + grp * 8 * BK), 16, 0, 0);
+  }
+}
+
+// 8 waves (2 per SIMD) in a 2 x 4 grid of 128 x 64 wave tiles.
+//   TN = false: both operands K-contiguous and every k-tile full; tiles are
+//               staged with direct global -> LDS loads.
+//   TN = true:  both operands M/N-contiguous (the weight-gradient form); each
+//               half of the block (256 threads) stages one operand through
+//               registers with the 8x8 transpose, any K multiple of 8.
+template <int EPI, bool TN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_mfma8_kernel(MfmaParams p) {
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * BM * BK];
+  // LDS: A buffers at [0, 2) * BM*BK, B buffers at [2, 4) * BM*BK.
+  bf16* const As = lds;
+  bf16* const Bs = lds + 2 * BM * BK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 128 x 64
+
+  // Tile order.  Blocks are dealt round-robin to the 8 XCDs (each with its own
+  // L2); remap so every XCD gets a contiguous run of the grouped order, in
+  // which GROUP_M row tiles sweep the column tiles together, so the A and B
+  // k-slices a run needs are shared in that XCD's L2.
+  int bid = blockIdx.x;
+#if NC_GEMM_XCD
+  {
+    const int nb = p.tiles_m * p.tiles_n;
+    const int per = nb >> 3;
+    if (bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
+  }
+  const int gsize = NC_GEMM_GROUP_M * p.tiles_n;
+  const int first_m = (bid / gsize) * NC_GEMM_GROUP_M;
+  const int gm = min(p.tiles_m - first_m, NC_GEMM_GROUP_M);
+  const int tm = first_m + (bid % gsize) % gm, tn = (bid % gsize) / gm;
+#else
+  const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
+#endif
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = blockIdx.z * p.k_per_split;
+  int kend = kbeg + p.k_per_split;
+  kend = kend < p.K ? kend : p.K;
+  const int nk = (kend - kbeg + BK - 1) / BK;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // TN staging: threads [0, 256) move A, [256, 512) move B.
+  const int op = tid >> 8, tl = tid & 255;
+  const bf16* const sP = op ? p.B : p.A;
+  const int64_t sld = op ? p.ldb : p.lda;
+  const int sr0 = op ? n0 : m0, sR = op ? p.N : p.M;
+  bf16* const sS = op ? Bs : As;
+  uint4 rv[8];
+  if constexpr (TN) {
+    load_tile<false>(sP, sld, sr0, sR, kbeg, kend, tl, rv);
+    store_tile<false>(sS, tl, rv);
+  } else {
+    stage_direct8(p.A, p.lda, m0, p.M, kbeg, As, wave, lane);
+    stage_direct8(p.B, p.ldb, n0, p.N, kbeg, Bs, wave, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int frow = lane & 31, fhalf = lane >> 5, fsw = swz(lane & 31);
+  // Register-path LDS writes per k-tile (direct staging needs none).
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1, nxt = cur ^ 1;
+    // The loop body has no branches so that it is one scheduling region: the
+    // last iteration re-stages the first tile (in bounds) into the idle buffer.
+    const int k1 = kt + 1 < nk ? kbeg + (kt + 1) * BK : kbeg;
+    if constexpr (TN) {
+      load_tile<false>(sP, sld, sr0, sR, k1, kend, tl, rv);
+    } else {
+      stage_direct8(p.A, p.lda, m0, p.M, k1, As + nxt * (BM * BK), wave, lane);
+      stage_direct8(p.B, p.ldb, n0, p.N, k1, Bs + nxt * (BN * BK), wave, lane);
+    }
+
+    const bf16* a_s = As + cur * (BM * BK) + (wm * 128 + frow) * BK;
+    const bf16* b_s = Bs + cur * (BN * BK) + (wn * 64 + frow) * BK;
+    // Fragments for k-step ks + 1 are read from LDS while the 16 MFMAs of
+    // step ks issue (two register sets), so LDS latency stays hidden.
+    bf16x8_t fa[2][4], fb[2][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[0][i] = *reinterpret_cast<const bf16x8_t*>(a_s + i * 32 * BK + ((fhalf ^ fsw) << 3));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[0][j] = *reinterpret_cast<const bf16x8_t*>(b_s + j * 32 * BK + ((fhalf ^ fsw) << 3));
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = ks & 1;
+      if (ks + 1 < 4) {
+        const int ch = (((ks + 1) * 2 + fhalf) ^ fsw) << 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[c ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(a_s + i * 32 * BK + ch);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[c ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(b_s + j * 32 * BK + ch);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][i], acc[i][j], 0, 0, 0);
+      if (ks + 1 < 4) {
+#pragma unroll
+        for (int g = 0; g < 6; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+    }
+    if constexpr (TN) {
+      store_tile<false>(sS + nxt * (BM * BK), tl, rv);
+      // last k-step: interleave the 8 staging writes with its 8 MFMAs
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // Epilogue, staged through LDS (free after the last barrier) so global
+  // traffic is row-contiguous.  The MFMAs above take B as their first operand,
+  // so tile (i, j) is computed transposed: lane l holds output row
+  // 32 i + (l & 31) and, in registers 4 q .. 4 q + 3, the four consecutive
+  // columns 32 j + 8 q + 4 (l >> 5) + 0..3 -- one 16-byte LDS write each.
+  // Per 32-row slab every wave writes its [32][SROW] fp32 region, then reads
+  // it back as float4 along rows.
+  constexpr int SROW = 68;  // 64 columns + pad
+  float* stage = reinterpret_cast<float*>(lds) + wave * (32 * SROW);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(stage + (lane & 31) * SROW + j * 32 + 8 * q + 4 * (lane >> 5)) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    __syncthreads();
+    for (int it = 0; it < 8; ++it) {
+      const int idx = it * 64 + lane;
+      const int row = idx >> 4, c4 = (idx & 15) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(stage + row * SROW + c4);
+      const int grow = m0 + wm * 128 + i * 32 + row, gcol = n0 + wn * 64 + c4;
       if (grow < p.M && gcol < p.N) epilogue4<EPI>(p, v, grow, gcol);
     }
     __syncthreads();
@@ -317,19 +586,47 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
 }
 
-template <bool AK, bool BKC>
+template <bool AK, bool BKC, bool DIRECT>
 hipError_t launch_mfma(int epi, const MfmaParams& p, int splits, hipStream_t s) {
   dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
   dim3 block(NT);
   switch (epi) {
-    case E_STORE_F32: gemm_mfma_kernel<AK, BKC, E_STORE_F32><<<grid, block, 0, s>>>(p); break;
-    case E_ACC_F32: gemm_mfma_kernel<AK, BKC, E_ACC_F32><<<grid, block, 0, s>>>(p); break;
-    case E_STORE_BF16: gemm_mfma_kernel<AK, BKC, E_STORE_BF16><<<grid, block, 0, s>>>(p); break;
-    case E_RELU2: gemm_mfma_kernel<AK, BKC, E_RELU2><<<grid, block, 0, s>>>(p); break;
-    case E_RELU2_BWD: gemm_mfma_kernel<AK, BKC, E_RELU2_BWD><<<grid, block, 0, s>>>(p); break;
-    default: gemm_mfma_kernel<AK, BKC, E_PARTIAL><<<grid, block, 0, s>>>(p); break;
+    case E_STORE_F32: gemm_mfma_kernel<AK, BKC, E_STORE_F32, DIRECT><<<grid, block, 0, s>>>(p); break;
+    case E_ACC_F32: gemm_mfma_kernel<AK, BKC, E_ACC_F32, DIRECT><<<grid, block, 0, s>>>(p); break;
+    case E_STORE_BF16: gemm_mfma_kernel<AK, BKC, E_STORE_BF16, DIRECT><<<grid, block, 0, s>>>(p); break;
+    case E_RELU2: gemm_mfma_kernel<AK, BKC, E_RELU2, DIRECT><<<grid, block, 0, s>>>(p); break;
+    case E_RELU2_BWD: gemm_mfma_kernel<AK, BKC, E_RELU2_BWD, DIRECT><<<grid, block, 0, s>>>(p); break;
+    default: gemm_mfma_kernel<AK, BKC, E_PARTIAL, DIRECT><<<grid, block, 0, s>>>(p); break;
   }
   return hipGetLastError();
+}
+
+#ifndef NC_GEMM_NT8
+#define NC_GEMM_NT8 1
+#endif
+
+template <bool TN>
+hipError_t launch_mfma8(int epi, const MfmaParams& p, int splits, hipStream_t s) {
+  dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
+  dim3 block(512);
+  switch (epi) {
+    case E_STORE_F32: gemm_mfma8_kernel<E_STORE_F32, TN><<<grid, block, 0, s>>>(p); break;
+    case E_ACC_F32: gemm_mfma8_kernel<E_ACC_F32, TN><<<grid, block, 0, s>>>(p); break;
+    case E_STORE_BF16: gemm_mfma8_kernel<E_STORE_BF16, TN><<<grid, block, 0, s>>>(p); break;
+    case E_RELU2: gemm_mfma8_kernel<E_RELU2, TN><<<grid, block, 0, s>>>(p); break;
+    case E_RELU2_BWD: gemm_mfma8_kernel<E_RELU2_BWD, TN><<<grid, block, 0, s>>>(p); break;
+    default: gemm_mfma8_kernel<E_PARTIAL, TN><<<grid, block, 0, s>>>(p); break;
+  }
+  return hipGetLastError();
+}
+
+template <bool AK, bool BKC>
+hipError_t launch_mfma(int epi, const MfmaParams& p, int splits, bool direct, hipStream_t s) {
+  if (NC_GEMM_NT8 && AK && BKC && direct) return launch_mfma8<false>(epi, p, splits, s);
+  if (NC_GEMM_NT8 && !AK && !BKC) return launch_mfma8<true>(epi, p, splits, s);
+  // direct staging only matters for K-contiguous operands
+  if (direct && (AK || BKC)) return launch_mfma<AK, BKC, true>(epi, p, splits, s);
+  return launch_mfma<AK, BKC, false>(epi, p, splits, s);
 }
 
 int choose_splits(int64_t M, int64_t N, int64_t K) {
@@ -441,11 +738,12 @@ int gemm(const GemmDesc& g, hipStream_t stream) {
   }
 
   const bool ak = g.transA == 0, bk = g.transB == 1;
+  const bool direct = g.K % BK == 0 && p.k_per_split % BK == 0;
   hipError_t e;
-  if (ak && bk) e = launch_mfma<true, true>(epi, p, splits, stream);
-  else if (ak && !bk) e = launch_mfma<true, false>(epi, p, splits, stream);
-  else if (!ak && bk) e = launch_mfma<false, true>(epi, p, splits, stream);
-  else e = launch_mfma<false, false>(epi, p, splits, stream);
+  if (ak && bk) e = launch_mfma<true, true>(epi, p, splits, direct, stream);
+  else if (ak && !bk) e = launch_mfma<true, false>(epi, p, splits, direct, stream);
+  else if (!ak && bk) e = launch_mfma<false, true>(epi, p, splits, direct, stream);
+  else e = launch_mfma<false, false>(epi, p, splits, direct, stream);
   if (e != hipSuccess) return set_error(NC_ERR_HIP, "gemm launch failed: %s", hipGetErrorString(e));
 
   if (splits > 1) {
@@ -490,3 +788,44 @@ extern "C" int nc_gemm_bf16(int transA, int transB, int64_t M, int64_t N, int64_
   g.ws_bytes = ws_bytes;
   return nc::gemm(g, static_cast<hipStream_t>(stream));
 }
+
+// ---------------------------------------------------------------------------
+// Transpose of a row-major [R, C] matrix of 2- or 4-byte elements into
+// [C, R] (leading dimension R).  64 x 64 tiles through padded LDS; the
+// backward turns every x W product into the K-contiguous form with it.
+// ---------------------------------------------------------------------------
+namespace nc {
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, int64_t R, int64_t C,
+                                                        T* __restrict__ dst) {
+  __shared__ T tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int rr = ty + 4 * i;
+    if (r0 + rr < R && c0 + tx < C) tile[rr][tx] = src[(r0 + rr) * C + c0 + tx];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int cc = ty + 4 * i;
+    if (c0 + cc < C && r0 + tx < R) dst[(c0 + cc) * R + r0 + tx] = tile[tx][cc];
+  }
+}
+
+}  // namespace
+
+int transpose(const void* src, int64_t R, int64_t C, int elem_bytes, void* dst, hipStream_t s) {
+  NC_REQUIRE(src && dst && R > 0 && C > 0, NC_ERR_INVALID_ARG, "transpose: bad arguments");
+  dim3 grid((unsigned)cdiv(C, 64), (unsigned)cdiv(R, 64));
+  if (elem_bytes == 2)
+    transpose_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), R, C, static_cast<uint16_t*>(dst));
+  else
+    transpose_kernel<uint32_t><<<grid, 256, 0, s>>>(static_cast<const uint32_t*>(src), R, C, static_cast<uint32_t*>(dst));
+  return check_launch("transpose_kernel");
+}
+
+}  // namespace nc

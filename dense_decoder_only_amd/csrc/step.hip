@@ -44,6 +44,7 @@ struct StepWs {
   float* dm;
   void *du, *dout, *dqkv;
   float* dqkv_hat;
+  void* wt;  // one layer's transposed weights (bf16 backward): Wqkv^T, Wo^T, W1^T, W2^T
   void *attn_ws, *gemm_ws, *xent_ws, *emb_ws;
   size_t attn_ws_bytes, gemm_ws_bytes, xent_ws_bytes, emb_ws_bytes;
   Layer* layers;  // host array filled by carve
@@ -83,6 +84,7 @@ size_t carve(const nc_config* c, StepWs* w, void* base) {
   const size_t o_h = take(M * d * e), o_rf = take(M * 4), o_lce = take(M * 4);
   const size_t o_glp = take(M * d * e), o_dm = take(M * d * 4), o_du = take(M * F * e), o_do = take(M * H * hd * e);
   const size_t o_dq = take(M * Q * e), o_dqh = take(M * Q * 4);
+  const size_t o_wt = take((size_t)(Q * d + d * H * hd + 2 * F * d) * e);
   const size_t attn_b = mqa_attn_bwd_workspace_bytes(c->batch, c->seq_len, (int)H);
   size_t gemm_b = 0;
   gemm_b = std::max(gemm_b, gemm_workspace_bytes(F, d, M));
@@ -107,6 +109,7 @@ size_t carve(const nc_config* c, StepWs* w, void* base) {
     w->dout = ptr(o_do);
     w->dqkv = ptr(o_dq);
     w->dqkv_hat = static_cast<float*>(ptr(o_dqh));
+    w->wt = ptr(o_wt);
     w->attn_ws = ptr(o_aws);
     w->attn_ws_bytes = attn_b;
     w->gemm_ws = gemm_b ? ptr(o_gws) : nullptr;
@@ -231,19 +234,33 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
                   gr->unembed, acc, w.xent_ws, w.xent_ws_bytes, s));
   NC_TRY(rmsnorm_bwd(w.dm, NC_F32, w.h, dt, w.rstd_f, M, (int)d, g, 0, glp_out, s));
 
+  // In bf16 the activation gradients dX = dY W use the transposed weights so
+  // that every product runs in the K-contiguous (x W^T) form.
+  const bool tw = dt == NC_BF16;
+  char* wt = static_cast<char*>(w.wt);
+  void* WqkvT = wt;
+  void* WoT = wt + (size_t)Q * d * e;
+  void* W1T = wt + (size_t)(Q * d + d * HD) * e;
+  void* W2T = wt + (size_t)(Q * d + d * HD + F * d) * e;
   for (int l = L - 1; l >= 0; --l) {
     Layer& ly = layers[l];
     const void* Wqkv = wl(p->w_qkv, l, Q * d);
     const void* Wo = wl(p->w_o, l, d * HD);
     const void* W1 = wl(p->w_fc, l, F * d);
     const void* W2 = wl(p->w_proj, l, d * F);
+    if (tw) {
+      NC_TRY(transpose(Wqkv, Q, d, 2, WqkvT, s));
+      NC_TRY(transpose(Wo, d, HD, 2, WoT, s));
+      NC_TRY(transpose(W1, F, d, 2, W1T, s));
+      NC_TRY(transpose(W2, d, F, 2, W2T, s));
+    }
     // MLP: x_out = x_mid + relu(m W1^T)^2 W2^T
     GemmDesc g1 = mk(1, 0, d, F, M, gop, d, ly.a2, F, gr->w_proj + (size_t)l * d * F, NC_F32, F, dt);
     g1.beta = (float)acc;
     g1.ws = w.gemm_ws;
     g1.ws_bytes = w.gemm_ws_bytes;
     NC_TRY(gemm(g1, s));
-    GemmDesc g2 = mk(0, 0, M, F, d, gop, d, W2, F, w.du, dt, F, dt);
+    GemmDesc g2 = tw ? mk(0, 1, M, F, d, gop, d, W2T, d, w.du, dt, F, dt) : mk(0, 0, M, F, d, gop, d, W2, F, w.du, dt, F, dt);
     g2.epi = NC_EPI_RELU2_BWD;
     g2.aux = ly.u;
     NC_TRY(gemm(g2, s));
@@ -252,7 +269,7 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
     g3.ws = w.gemm_ws;
     g3.ws_bytes = w.gemm_ws_bytes;
     NC_TRY(gemm(g3, s));
-    NC_TRY(gemm(mk(0, 0, M, d, F, w.du, F, W1, d, w.dm, NC_F32, d, dt), s));
+    NC_TRY(gemm(tw ? mk(0, 1, M, d, F, w.du, F, W1T, F, w.dm, NC_F32, d, dt) : mk(0, 0, M, d, F, w.du, F, W1, d, w.dm, NC_F32, d, dt), s));
     NC_TRY(rmsnorm_bwd(w.dm, NC_F32, ly.m, dt, ly.rstd_m, M, (int)d, g, 1, glp_out, s));
     // attention: x_mid = x_in + mqa(...) Wo^T
     GemmDesc g4 = mk(1, 0, d, HD, M, gop, d, ly.o, HD, gr->w_o + (size_t)l * d * HD, NC_F32, HD, dt);
@@ -260,7 +277,7 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
     g4.ws = w.gemm_ws;
     g4.ws_bytes = w.gemm_ws_bytes;
     NC_TRY(gemm(g4, s));
-    NC_TRY(gemm(mk(0, 0, M, HD, d, gop, d, Wo, HD, w.dout, dt, HD, dt), s));
+    NC_TRY(gemm(tw ? mk(0, 1, M, HD, d, gop, d, WoT, d, w.dout, dt, HD, dt) : mk(0, 0, M, HD, d, gop, d, Wo, HD, w.dout, dt, HD, dt), s));
     NC_TRY(mqa_attn_bwd(ly.qkv, ly.o, w.dout, ly.lse, dt, B, T, H, hd, scale, w.dqkv_hat, w.attn_ws,
                         w.attn_ws_bytes, s));
     NC_TRY(rope_qknorm_bwd(w.dqkv_hat, ly.qkv, ly.rstd_q, ly.rstd_k, w.table, dt, B, T, H, hd, w.dqkv, s));
@@ -269,7 +286,7 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
     g5.ws = w.gemm_ws;
     g5.ws_bytes = w.gemm_ws_bytes;
     NC_TRY(gemm(g5, s));
-    NC_TRY(gemm(mk(0, 0, M, d, Q, w.dqkv, Q, Wqkv, d, w.dm, NC_F32, d, dt), s));
+    NC_TRY(gemm(tw ? mk(0, 1, M, d, Q, w.dqkv, Q, WqkvT, Q, w.dm, NC_F32, d, dt) : mk(0, 0, M, d, Q, w.dqkv, Q, Wqkv, d, w.dm, NC_F32, d, dt), s));
     NC_TRY(rmsnorm_bwd(w.dm, NC_F32, ly.a, dt, ly.rstd_a, M, (int)d, g, 1, glp_out, s));
   }
   // embedding norm and scatter-add

@@ -42,6 +42,7 @@ struct XentWs {
   float* ltok;     // [M]
   void* gemm_ws;
   size_t gemm_ws_bytes;
+  void* ut;        // U^T [d, V] (bf16 backward)
 };
 
 size_t carve(int64_t M, int d, int V, XentWs* w, void* base) {
@@ -60,6 +61,7 @@ size_t carve(int64_t M, int d, int V, XentWs* w, void* base) {
   const size_t o_l = take((size_t)M * 4);
   const size_t gwb = gemm_workspace_bytes(Vc, d, M);
   const size_t o_g = take(gwb);
+  const size_t o_ut = take((size_t)V * d * 2);
   if (w) {
     char* b = static_cast<char*>(base);
     w->zbuf = reinterpret_cast<float*>(b + o_z);
@@ -69,6 +71,7 @@ size_t carve(int64_t M, int d, int V, XentWs* w, void* base) {
     w->ltok = reinterpret_cast<float*>(b + o_l);
     w->gemm_ws = gwb ? b + o_g : nullptr;
     w->gemm_ws_bytes = gwb;
+    w->ut = b + o_ut;
   }
   return off;
 }
@@ -229,6 +232,7 @@ int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
   const int Vc = chunk_cols(M, V);
   const int nch = (int)cdiv(V, Vc);
   const size_t esz = dtype == NC_BF16 ? 2 : 4;
+  if (dtype == NC_BF16) NC_TRY(transpose(U, V, d, 2, w.ut, s));
   for (int k = 0; k < nch; ++k) {
     const int v0 = k * Vc;
     const int n = std::min(Vc, V - v0);
@@ -255,17 +259,23 @@ int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
       xent_bwd_rows_kernel<float><<<(unsigned)cdiv(M, 4), 256, 0, s>>>(w.zbuf, M, n, v0, softcap, tgt, lse, dloss,
                                                                         static_cast<float*>(w.dz));
     NC_TRY(check_launch("xent_bwd_rows_kernel"));
-    // dh (+)= dz U_c  : [M, n] x [n, d]
+    // dh (+)= dz U_c  : [M, n] x [n, d]; in bf16 through U^T (K-contiguous)
     GemmDesc gh;
     gh.transA = 0;
-    gh.transB = 0;
     gh.M = M;
     gh.N = d;
     gh.K = n;
     gh.A = w.dz;
     gh.lda = n;
-    gh.B = Uc;
-    gh.ldb = d;
+    if (dtype == NC_BF16) {
+      gh.transB = 1;
+      gh.B = static_cast<const bf16*>(w.ut) + v0;
+      gh.ldb = V;
+    } else {
+      gh.transB = 0;
+      gh.B = Uc;
+      gh.ldb = d;
+    }
     gh.C = dh;
     gh.cdt = NC_F32;
     gh.ldc = d;
