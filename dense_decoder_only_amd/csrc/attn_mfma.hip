@@ -5,26 +5,35 @@
 // Folding heads into rows.  With one shared K/V head, the H query heads of a
 // sequence form one [T*H, 128] matrix of query rows r = t*H + h (position
 // t = r / H) against a single [T, 128] key/value pair.  A block therefore
-// stages each K/V tile in LDS once and reuses it for all the heads its rows
-// cover -- the multi-query saving on K/V traffic is structural.
+// stages each K/V tile in LDS once for all the heads its rows cover.
 //
 // Register layouts.  Every product is issued so that the softmax direction
 // (keys) lies along the MFMA rows and the query rows along the lanes: S^T =
 // K Q^T puts one query row per lane column, so row maxima and sums are
 // in-lane (plus one exchange with the partner half-wave), and the
-// probabilities can feed the next product O^T = V^T P^T straight from
+// probabilities feed the next product O^T = V^T P^T straight from
 // registers.  A 32x32 output tile gives lane l the column (l & 31) and rows
 // 8 (r >> 2) + 4 (l >> 5) + (r & 3), r = 0..15; the k-slots of the next
-// product are renumbered to match, which a contraction allows.
+// product are renumbered to match (slot e of half h <-> key
+// 16 jp + 8 (e >> 2) + 4 h + (e & 3)), which a contraction allows.
 //
-// LDS tiles.  Row-major [rows][128] tiles swizzle 16-byte chunks by
-// (row & 7); transposed [128][64] tiles swizzle 8-byte units by (row & 15).
+// LDS.  Every operand tile is stored row-major [64 rows][128] exactly as it
+// sits in HBM and arrives by direct global -> LDS loads (gfx950
+// global_load_lds_dwordx4), double-buffered so the next tile is in flight
+// while the current one is consumed.  Operands needed transposed (V^T, K^T,
+// Q^T, dO^T) are read with ds_read_b64_tr_b16: in a 16-lane group, lane j
+// receives element j % 4 of the 8-byte pieces addressed by lanes j/4,
+// 4 + j/4, 8 + j/4 and 12 + j/4, so pointing lane p at row kb + p/4, columns
+// c0 + 4 (p % 4) hands lane j the four consecutive rows kb..kb+3 of column
+// c0 + j -- exactly four consecutive k-slots of an MFMA A operand.  16-byte
+// chunks are XOR-swizzled by ((r & 3) << 2) | ((r >> 2) & 3) so that both the
+// row reads and the transposed reads spread over the banks.
 //
 // Kernels: forward (online softmax, writes O and the log-sum-exp), dQ (also
 // writes D = rowsum(dO * O)), dK/dV (key blocks of 128 positions, the query
 // range split into chunks so that early key blocks do not serialize, partials
-// summed in a fixed order by a reduce kernel).  Nothing uses atomics; results
-// are bitwise reproducible.
+// summed in a fixed order by a reduce kernel).  No atomics; results are
+// bitwise reproducible.
 #include "common.h"
 #include "attn_mfma.h"
 
@@ -37,50 +46,47 @@ constexpr int KT = 64;    // keys per tile
 constexpr int KB = 128;   // keys per dK/dV block (4 waves x 32)
 constexpr int QT = 64;    // query rows per dK/dV tile
 constexpr int QCH = 5120; // query rows per dK/dV split
+constexpr int TILE = 64 * HD;  // elements of one [64][128] tile
 constexpr float LOG2E = 1.4426950408889634f;
 
-__device__ __forceinline__ int kidx(int row, int chunk) { return row * HD + ((chunk ^ (row & 7)) << 3); }
-__device__ __forceinline__ int tidx(int row, int unit) { return row * 64 + ((unit ^ (row & 15)) << 2); }
+typedef __bf16 bf16x4_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
 
-__device__ __forceinline__ uint32_t wd(const uint4& q, int w) {
-  return w == 0 ? q.x : (w == 1 ? q.y : (w == 2 ? q.z : q.w));
-}
+__device__ __forceinline__ int tswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// element offset of (row, 8-column chunk c) in a swizzled [rows][128] tile
+__device__ __forceinline__ int toff(int row, int c) { return row * HD + ((c ^ tswz(row)) << 3); }
 
-// 8x8 bf16 transpose: v[kk] holds 8 consecutive columns (hd) of row kk;
-// returns in o[mm] the 8 rows (kk = 0..7) of column mm as 4 words.
-__device__ __forceinline__ void transpose8(const uint4 (&v)[8], uint32_t (&o)[8][4]) {
+// Direct global -> LDS staging of a [64][128] tile: 16 instructions of 1 KB
+// (4 rows each), 4 per wave.  rowp(row) gives the global address of a row.
+template <typename RowPtr>
+__device__ __forceinline__ void dma_tile(bf16* S, int wave, int lane, RowPtr rowp) {
+  const int rsub = lane >> 4, cp = lane & 15;
 #pragma unroll
-  for (int mm = 0; mm < 8; ++mm) {
-    const int w = mm >> 1;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t a = wd(v[2 * p], w), b = wd(v[2 * p + 1], w);
-      o[mm][p] = (mm & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int g = wave * 4 + i;
+    const int row = g * 4 + rsub;
+    const int c = cp ^ tswz(row);
+    __builtin_amdgcn_global_load_lds(rowp(row) + c * 8, (__attribute__((address_space(3))) void*)(S + g * 4 * HD),
+                                     16, 0, 0);
   }
 }
 
-// Write a transposed 8x8 block: LDS rows hd0 + mm, columns col0 .. col0 + 7.
-__device__ __forceinline__ void store_t8(bf16* T, int hd0, int col0, const uint32_t (&o)[8][4]) {
-  const int u0 = col0 >> 2;
-#pragma unroll
-  for (int mm = 0; mm < 8; ++mm) {
-    const int row = hd0 + mm;
-    *reinterpret_cast<uint2*>(T + tidx(row, u0)) = make_uint2(o[mm][0], o[mm][1]);
-    *reinterpret_cast<uint2*>(T + tidx(row, u0 + 1)) = make_uint2(o[mm][2], o[mm][3]);
-  }
+// MFMA operand: 8 consecutive columns (chunk c) of `row`.
+__device__ __forceinline__ bf16x8_t frag_row(const bf16* S, int row, int c) {
+  return *reinterpret_cast<const bf16x8_t*>(S + toff(row, c));
 }
 
-__device__ __forceinline__ bf16x8_t frag_k(const bf16* S, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8_t*>(S + kidx(row, chunk));
-}
-
-// A-operand from a transposed tile: 8 values at columns c0 .. c0+3 and
-// c0+8 .. c0+11 of `row` (c0 = 4 * unit index).
-__device__ __forceinline__ bf16x8_t frag_t(const bf16* T, int row, int unit) {
-  const uint2 a = *reinterpret_cast<const uint2*>(T + tidx(row, unit));
-  const uint2 b = *reinterpret_cast<const uint2*>(T + tidx(row, unit + 2));
-  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+// MFMA A operand of X^T from a row-major tile X: output rows are the columns
+// col0 .. col0 + 31 of X, k-slots are rows rbase + 8 (e >> 2) + 4 h + (e & 3).
+__device__ __forceinline__ bf16x8_t frag_tr(const bf16* S, int rbase, int col0, int lane) {
+  const int g = lane >> 4, p = lane & 15, h = lane >> 5;
+  const int col = col0 + 16 * (g & 1) + 4 * (p & 3);
+  const int r1 = rbase + 4 * h + (p >> 2);
+  const bf16* a1 = S + toff(r1, col >> 3) + (col & 7);
+  const bf16* a2 = S + toff(r1 + 8, col >> 3) + (col & 7);
+  const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)a1);
+  const bf16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)a2);
+  const uint2 u = __builtin_bit_cast(uint2, x), v = __builtin_bit_cast(uint2, y);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(u.x, u.y, v.x, v.y));
 }
 
 // Registers r = 8 jp .. 8 jp + 7 of a score tile, rounded to bf16, as the
@@ -102,11 +108,15 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+__device__ __forceinline__ uint32_t wd(const uint4& q, int w) {
+  return w == 0 ? q.x : (w == 1 ? q.y : (w == 2 ? q.z : q.w));
+}
+
 // ------------------------------------------------------------------ forward --
 // grid (B, ceil(R / QB)); heavy (late) row blocks first.
 __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnMfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[KT * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[HD * KT];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2 * TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2 * TILE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
   const int H = a.H, T = a.T;
   const int R = T * H;
@@ -130,60 +140,57 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnMfmaArgs a) {
   const int tmin = r0 / H;
   const int tmax = min(T - 1, (min(r0 + QB, R) - 1) / H);
   const int ntiles = tmax / KT + 1;
+  auto stage = [&](int j, int buf) {
+    const int kv0 = j * KT;
+    dma_tile(Ks + buf * TILE, w, lane,
+             [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + H * HD; });
+    dma_tile(Vs + buf * TILE, w, lane,
+             [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + (H + 1) * HD; });
+  };
 
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
 
+  stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
     const int kv0 = j * KT;
-    __syncthreads();  // previous tile fully consumed
-    if (tid < 128) {  // V^T: one 8x8 block per thread
-      const int kvb = tid & 7, hdb = tid >> 3;
-      uint4 v[8];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int u = min(kv0 + kvb * 8 + kk, T - 1);
-        v[kk] = *reinterpret_cast<const uint4*>(base + (int64_t)u * a.S + (H + 1) * HD + hdb * 8);
-      }
-      uint32_t t8[8][4];
-      transpose8(v, t8);
-      store_t8(Vt, hdb * 8, kvb * 8, t8);
-    } else {  // K row-major: 1024 chunks over 128 threads
-      const int t2 = tid - 128;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int id = t2 + 128 * i;
-        const int row = id >> 4, c = id & 15;
-        const int u = min(kv0 + row, T - 1);
-        *reinterpret_cast<uint4*>(Ks + kidx(row, c)) =
-            *reinterpret_cast<const uint4*>(base + (int64_t)u * a.S + H * HD + c * 8);
-      }
-    }
-    __syncthreads();
+    if (j + 1 < ntiles) stage(j + 1, cur ^ 1);
+    const bf16* K = Ks + cur * TILE;
+    const bf16* V = Vs + cur * TILE;
 
     f32x16 s[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       s[st] = zero16();
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s[st] = mfma(frag_k(Ks, st * 32 + lc, 2 * ks + h), qreg[ks], s[st]);
+      for (int ks = 0; ks < 8; ++ks) s[st] = mfma(frag_row(K, st * 32 + lc, 2 * ks + h), qreg[ks], s[st]);
     }
-    const bool need_mask = kv0 + KT - 1 > tmin;
     float mt = -INFINITY;
+    if (kv0 + KT - 1 > tmin) {  // the tile crosses some row's diagonal
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[st][r] * a.scale_log2;
-        if (need_mask) {
+        for (int r = 0; r < 16; ++r) {
           const int kv = kv0 + st * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (kv > tq) x = -INFINITY;
+          const float x = kv > tq ? -INFINITY : s[st][r] * a.scale_log2;
+          s[st][r] = x;
+          mt = fmaxf(mt, x);
         }
-        s[st][r] = x;
-        mt = fmaxf(mt, x);
-      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = s[st][r] * a.scale_log2;
+          s[st][r] = x;
+          mt = fmaxf(mt, x);
+        }
+    }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
     const float alpha = exp2f(m_run - m_new);
@@ -209,8 +216,10 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnMfmaArgs a) {
       for (int jp = 0; jp < 2; ++jp) {
         const bf16x8_t pb = pack_p(s[st], jp);
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) o[ht] = mfma(frag_t(Vt, ht * 32 + lc, 8 * st + 4 * jp + h), pb, o[ht]);
+        for (int ht = 0; ht < 4; ++ht) o[ht] = mfma(frag_tr(V, st * 32 + 16 * jp, ht * 32, lane), pb, o[ht]);
       }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
   if (valid) {
@@ -232,9 +241,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnMfmaArgs a) {
 // ----------------------------------------------------------------------- dQ --
 // Also writes D = rowsum(dO * O) for the key-side kernel.
 __global__ __launch_bounds__(256) void attn_dq_kernel(AttnMfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[KT * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[KT * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[HD * KT];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2 * TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2 * TILE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
   const int H = a.H, T = a.T;
   const int R = T * H;
@@ -276,36 +284,26 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnMfmaArgs a) {
   const int tmin = r0 / H;
   const int tmax = min(T - 1, (min(r0 + QB, R) - 1) / H);
   const int ntiles = tmax / KT + 1;
+  auto stage = [&](int j, int buf) {
+    const int kv0 = j * KT;
+    dma_tile(Ks + buf * TILE, w, lane,
+             [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + H * HD; });
+    dma_tile(Vs + buf * TILE, w, lane,
+             [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + (H + 1) * HD; });
+  };
   f32x16 dq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dq[i] = zero16();
 
+  stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
     const int kv0 = j * KT;
-    __syncthreads();
-    // K and V row-major: 2 x 1024 chunks, 8 per thread.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id >> 4, c = id & 15;
-      const int u = min(kv0 + row, T - 1);
-      const bf16* rp = base + (int64_t)u * a.S + H * HD + c * 8;
-      *reinterpret_cast<uint4*>(Ks + kidx(row, c)) = *reinterpret_cast<const uint4*>(rp);
-      *reinterpret_cast<uint4*>(Vs + kidx(row, c)) = *reinterpret_cast<const uint4*>(rp + HD);
-    }
-    if (tid < 128) {  // K^T
-      const int kvb = tid & 7, hdb = tid >> 3;
-      uint4 v[8];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int u = min(kv0 + kvb * 8 + kk, T - 1);
-        v[kk] = *reinterpret_cast<const uint4*>(base + (int64_t)u * a.S + H * HD + hdb * 8);
-      }
-      uint32_t t8[8][4];
-      transpose8(v, t8);
-      store_t8(Kt, hdb * 8, kvb * 8, t8);
-    }
-    __syncthreads();
+    if (j + 1 < ntiles) stage(j + 1, cur ^ 1);
+    const bf16* K = Ks + cur * TILE;
+    const bf16* V = Vs + cur * TILE;
 
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -314,8 +312,8 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnMfmaArgs a) {
       dp[st] = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        s[st] = mfma(frag_k(Ks, st * 32 + lc, 2 * ks + h), qreg[ks], s[st]);
-        dp[st] = mfma(frag_k(Vs, st * 32 + lc, 2 * ks + h), dreg[ks], dp[st]);
+        s[st] = mfma(frag_row(K, st * 32 + lc, 2 * ks + h), qreg[ks], s[st]);
+        dp[st] = mfma(frag_row(V, st * 32 + lc, 2 * ks + h), dreg[ks], dp[st]);
       }
     }
     const bool need_mask = kv0 + KT - 1 > tmin;
@@ -336,8 +334,10 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnMfmaArgs a) {
       for (int jp = 0; jp < 2; ++jp) {
         const bf16x8_t pb = pack_p(s[st], jp);
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) dq[ht] = mfma(frag_t(Kt, ht * 32 + lc, 8 * st + 4 * jp + h), pb, dq[ht]);
+        for (int ht = 0; ht < 4; ++ht) dq[ht] = mfma(frag_tr(K, st * 32 + 16 * jp, ht * 32, lane), pb, dq[ht]);
       }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
   if (valid) {
@@ -362,12 +362,10 @@ __device__ __forceinline__ int nsplit_of(int kb, int H, int R) { return (R - qbe
 // query rows [qbeg + s*QCH, min(R, qbeg + (s+1)*QCH)).  Writes partial dK^T,
 // dV^T sums (unscaled) to part[(b * nkb + kb) * SMAX + s].
 __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 Qs[QT * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Ds[QT * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[HD * QT];
-  __shared__ __attribute__((aligned(16))) bf16 Dt[HD * QT];
-  __shared__ float lse_s[QT], D_s[QT];
-  __shared__ int tpos_s[QT];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[2 * TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Ds[2 * TILE];
+  __shared__ float lse_s[2][QT], D_s[2][QT];
+  __shared__ int tpos_s[2][QT];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
   const int H = a.H, T = a.T;
   const int R = T * H;
@@ -376,6 +374,7 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
   const int b = blockIdx.x;
   if (sp >= nsplit_of(kb, H, R)) return;
   const bf16* base = a.qkv + (int64_t)b * T * a.S;
+  const bf16* dbase = a.dout + (int64_t)b * R * HD;
   const int u0 = kb * KB;
   const int myu = u0 + w * 32 + lc;  // this lane's key position (column)
   const int uu = min(myu, T - 1);
@@ -390,6 +389,40 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
   }
   const int qs0 = qbeg_of(kb, H) + sp * QCH;
   const int qs1 = min(R, qs0 + QCH);
+  const int nq = (qs1 - qs0 + QT - 1) / QT;
+  auto stage = [&](int i, int buf) {
+    const int q0 = qs0 + i * QT;
+    dma_tile(Qs + buf * TILE, w, lane, [&](int row) {
+      const int r = min(q0 + row, R - 1);
+      const int t = r / H;
+      return base + (int64_t)t * a.S + (r - t * H) * HD;
+    });
+    dma_tile(Ds + buf * TILE, w, lane, [&](int row) { return dbase + (int64_t)min(q0 + row, R - 1) * HD; });
+  };
+  // per-row statistics of a query tile, loaded by threads 0..63 into registers
+  float n_lse = 0.f, n_D = 0.f;
+  int n_t = -1;
+  auto fetch_stats = [&](int i) {
+    const int r = qs0 + i * QT + tid;
+    if (tid < QT) {
+      if (r < R) {
+        n_lse = a.lse[(int64_t)b * R + r] * LOG2E;
+        n_D = a.Dbuf[(int64_t)b * R + r];
+        n_t = r / H;
+      } else {
+        n_lse = INFINITY;  // p = 0 for rows past the end
+        n_D = 0.f;
+        n_t = -1;
+      }
+    }
+  };
+  auto put_stats = [&](int buf) {
+    if (tid < QT) {
+      lse_s[buf][tid] = n_lse;
+      D_s[buf][tid] = n_D;
+      tpos_s[buf][tid] = n_t;
+    }
+  };
   f32x16 dk[4], dv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -397,51 +430,19 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
     dv[i] = zero16();
   }
 
-  for (int q0 = qs0; q0 < qs1; q0 += QT) {
-    __syncthreads();
-    // Q and dO row-major: 2 x 1024 chunks.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id >> 4, c = id & 15;
-      const int r = min(q0 + row, R - 1);
-      const int t = r / H, hh = r - t * H;
-      *reinterpret_cast<uint4*>(Qs + kidx(row, c)) =
-          *reinterpret_cast<const uint4*>(base + (int64_t)t * a.S + hh * HD + c * 8);
-      *reinterpret_cast<uint4*>(Ds + kidx(row, c)) =
-          *reinterpret_cast<const uint4*>(a.dout + ((int64_t)b * R + r) * HD + c * 8);
+  stage(0, 0);
+  fetch_stats(0);
+  put_stats(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int i = 0; i < nq; ++i) {
+    const int cur = i & 1;
+    if (i + 1 < nq) {
+      stage(i + 1, cur ^ 1);
+      fetch_stats(i + 1);
     }
-    {  // Q^T (threads 0..127) and dO^T (threads 128..255), one 8x8 block each
-      const int t2 = tid & 127;
-      const int qb = t2 & 7, hdb = t2 >> 3;
-      uint4 v[8];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int r = min(q0 + qb * 8 + kk, R - 1);
-        if (tid < 128) {
-          const int t = r / H, hh = r - t * H;
-          v[kk] = *reinterpret_cast<const uint4*>(base + (int64_t)t * a.S + hh * HD + hdb * 8);
-        } else {
-          v[kk] = *reinterpret_cast<const uint4*>(a.dout + ((int64_t)b * R + r) * HD + hdb * 8);
-        }
-      }
-      uint32_t t8[8][4];
-      transpose8(v, t8);
-      store_t8(tid < 128 ? Qt : Dt, hdb * 8, qb * 8, t8);
-    }
-    if (tid < QT) {
-      const int r = q0 + tid;
-      if (r < R) {
-        lse_s[tid] = a.lse[(int64_t)b * R + r] * LOG2E;
-        D_s[tid] = a.Dbuf[(int64_t)b * R + r];
-        tpos_s[tid] = r / H;
-      } else {
-        lse_s[tid] = INFINITY;  // p = 0 for rows past the end
-        D_s[tid] = 0.f;
-        tpos_s[tid] = -1;
-      }
-    }
-    __syncthreads();
+    const bf16* Q = Qs + cur * TILE;
+    const bf16* G = Ds + cur * TILE;
 
     // S = Q K^T and dP = dO V^T: rows q (two 32-row halves), column = key.
     f32x16 s[2], dp[2];
@@ -451,8 +452,8 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
       dp[qt] = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        s[qt] = mfma(frag_k(Qs, qt * 32 + lc, 2 * ks + h), kreg[ks], s[qt]);
-        dp[qt] = mfma(frag_k(Ds, qt * 32 + lc, 2 * ks + h), vreg[ks], dp[qt]);
+        s[qt] = mfma(frag_row(Q, qt * 32 + lc, 2 * ks + h), kreg[ks], s[qt]);
+        dp[qt] = mfma(frag_row(G, qt * 32 + lc, 2 * ks + h), vreg[ks], dp[qt]);
       }
     }
 #pragma unroll
@@ -460,10 +461,10 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = qt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        float p = exp2f(s[qt][r] * a.scale_log2 - lse_s[qi]);
-        if (myu > tpos_s[qi]) p = 0.f;
+        float p = exp2f(s[qt][r] * a.scale_log2 - lse_s[cur][qi]);
+        if (myu > tpos_s[cur][qi]) p = 0.f;
         s[qt][r] = p;
-        dp[qt][r] = p * (dp[qt][r] - D_s[qi]);
+        dp[qt][r] = p * (dp[qt][r] - D_s[cur][qi]);
       }
     // dV^T += dO^T P ; dK^T += Q^T dS
 #pragma unroll
@@ -474,10 +475,13 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
         const bf16x8_t db = pack_p(dp[qt], jp);
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
-          dv[ht] = mfma(frag_t(Dt, ht * 32 + lc, 8 * qt + 4 * jp + h), pb, dv[ht]);
-          dk[ht] = mfma(frag_t(Qt, ht * 32 + lc, 8 * qt + 4 * jp + h), db, dk[ht]);
+          dv[ht] = mfma(frag_tr(G, qt * 32 + 16 * jp, ht * 32, lane), pb, dv[ht]);
+          dk[ht] = mfma(frag_tr(Q, qt * 32 + 16 * jp, ht * 32, lane), db, dk[ht]);
         }
       }
+    if (i + 1 < nq) put_stats(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
   // partial [slot][2][KB keys][HD]: lane holds hd = ht*32 + 8 q4 + 4 h + e for key (w*32 + lc)
