@@ -605,6 +605,176 @@ hipError_t launch_mfma(int epi, const MfmaParams& p, int splits, hipStream_t s) 
 #define NC_GEMM_NT8 1
 #endif
 
+// ---------------------------------------------------------------------------
+// Weight-gradient form (both operands M/N-contiguous, K = tokens) with direct
+// staging: tiles are moved exactly as stored, [64 k-rows][256 columns], by
+// global_load_lds, and MFMA operands are read transposed from LDS with
+// ds_read_b64_tr_b16 (in a 16-lane group lane j receives element j % 4 of the
+// 8-byte pieces addressed by lanes j/4, 4 + j/4, 8 + j/4, 12 + j/4; pointing
+// lane p at k-row kb + p/4, column c0 + 4 (p % 4) gives lane j the four
+// k-rows kb..kb+3 of column c0 + j).  Both operands use the same k-slot order
+// (slot e of half h <-> k = 16 ks + 8 (e >> 2) + 4 h + (e & 3)).  16-byte
+// chunks are swizzled by c ^ 4 (row & 3), which spreads a 32-lane transposed
+// read over all 64 banks.  8 waves in a 2 x 4 grid of 128 x 64.
+// Requires every k-tile to be full.
+// ---------------------------------------------------------------------------
+constexpr int TROW = 256;  // columns per staged k-row
+__device__ __forceinline__ int tn_off(int row, int c) { return row * TROW + ((c ^ (4 * (row & 3))) << 3); }
+
+__device__ __forceinline__ void stage_tn(const bf16* __restrict__ P, int64_t ld, int c0, int C, int k0, bf16* S,
+                                         int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = wave * 4 + i;  // 2 k-rows per 1 KB instruction
+    const int row = g * 2 + (lane >> 5);
+    const int c = (lane & 31) ^ (4 * (row & 3));
+    int col = c0 + c * 8;
+    col = col < C ? col : C - 8;
+    __builtin_amdgcn_global_load_lds(P + (int64_t)(k0 + row) * ld + col,
+                                     (__attribute__((address_space(3))) void*)(S + g * 2 * TROW), 16, 0, 0);
+  }
+}
+
+typedef __bf16 bf16x4_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
+
+// operand fragment: MFMA rows = columns col0 .. col0 + 31, k-slots from k-rows
+// 16 ks + 8 (e >> 2) + 4 h + (e & 3)
+__device__ __forceinline__ bf16x8_t frag_tn(const bf16* S, int ks, int col0, int lane) {
+  const int g = lane >> 4, p = lane & 15, h = lane >> 5;
+  const int col = col0 + 16 * (g & 1) + 4 * (p & 3);
+  const int r1 = 16 * ks + 4 * h + (p >> 2);
+  const bf16* a1 = S + tn_off(r1, col >> 3) + (col & 7);
+  const bf16* a2 = S + tn_off(r1 + 8, col >> 3) + (col & 7);
+  const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)a1);
+  const bf16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)a2);
+  const uint2 u = __builtin_bit_cast(uint2, x), v = __builtin_bit_cast(uint2, y);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(u.x, u.y, v.x, v.y));
+}
+
+template <int EPI>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_tn_direct_kernel(MfmaParams p) {
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * BM * BK];
+  bf16* const As = lds;
+  bf16* const Bs = lds + 2 * BM * BK;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  int bid = blockIdx.x;
+#if NC_GEMM_XCD
+  {
+    const int nb = p.tiles_m * p.tiles_n;
+    const int per = nb >> 3;
+    if (bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
+  }
+  const int gsize = NC_GEMM_GROUP_M * p.tiles_n;
+  const int first_m = (bid / gsize) * NC_GEMM_GROUP_M;
+  const int gm = min(p.tiles_m - first_m, NC_GEMM_GROUP_M);
+  const int tm = first_m + (bid % gsize) % gm, tn = (bid % gsize) / gm;
+#else
+  const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
+#endif
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = blockIdx.z * p.k_per_split;
+  int kend = kbeg + p.k_per_split;
+  kend = kend < p.K ? kend : p.K;
+  const int nk = (kend - kbeg) / BK;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  stage_tn(p.A, p.lda, m0, p.M, kbeg, As, wave, lane);
+  stage_tn(p.B, p.ldb, n0, p.N, kbeg, Bs, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1, nxt = cur ^ 1;
+    const int k1 = kt + 1 < nk ? kbeg + (kt + 1) * BK : kbeg;
+    stage_tn(p.A, p.lda, m0, p.M, k1, As + nxt * (BM * BK), wave, lane);
+    stage_tn(p.B, p.ldb, n0, p.N, k1, Bs + nxt * (BN * BK), wave, lane);
+    const bf16* a_s = As + cur * (BM * BK);
+    const bf16* b_s = Bs + cur * (BN * BK);
+    bf16x8_t fa[2][4], fb[2][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[0][i] = frag_tn(a_s, 0, wm * 128 + i * 32, lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[0][j] = frag_tn(b_s, 0, wn * 64 + j * 32, lane);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = ks & 1;
+      if (ks + 1 < 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[c ^ 1][i] = frag_tn(a_s, ks + 1, wm * 128 + i * 32, lane);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[c ^ 1][j] = frag_tn(b_s, ks + 1, wn * 64 + j * 32, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][i], acc[i][j], 0, 0, 0);
+      if (ks + 1 < 4) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // epilogue: same LDS staging as the 8-wave kernel (wave tile 128 x 64)
+  constexpr int SROW = 68;
+  float* stage = reinterpret_cast<float*>(lds) + wave * (32 * SROW);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(stage + (lane & 31) * SROW + j * 32 + 8 * q + 4 * (lane >> 5)) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    __syncthreads();
+    for (int it = 0; it < 8; ++it) {
+      const int idx = it * 64 + lane;
+      const int row = idx >> 4, c4 = (idx & 15) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(stage + row * SROW + c4);
+      const int grow = m0 + wm * 128 + i * 32 + row, gcol = n0 + wn * 64 + c4;
+      if (grow < p.M && gcol < p.N) epilogue4<EPI>(p, v, grow, gcol);
+    }
+    __syncthreads();
+  }
+}
+
+template <int EPI>
+hipError_t launch_tn_direct_epi(const MfmaParams& p, int splits, hipStream_t s) {
+  gemm_tn_direct_kernel<EPI><<<dim3(p.tiles_m * p.tiles_n, 1, splits), 512, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_tn_direct(int epi, const MfmaParams& p, int splits, hipStream_t s) {
+  switch (epi) {
+    case E_STORE_F32: return launch_tn_direct_epi<E_STORE_F32>(p, splits, s);
+    case E_ACC_F32: return launch_tn_direct_epi<E_ACC_F32>(p, splits, s);
+    case E_STORE_BF16: return launch_tn_direct_epi<E_STORE_BF16>(p, splits, s);
+    case E_RELU2: return launch_tn_direct_epi<E_RELU2>(p, splits, s);
+    case E_RELU2_BWD: return launch_tn_direct_epi<E_RELU2_BWD>(p, splits, s);
+    default: return launch_tn_direct_epi<E_PARTIAL>(p, splits, s);
+  }
+}
+
+#ifndef NC_GEMM_TN_DIRECT
+#define NC_GEMM_TN_DIRECT 1
+#endif
+
 template <bool TN>
 hipError_t launch_mfma8(int epi, const MfmaParams& p, int splits, hipStream_t s) {
   dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
@@ -623,8 +793,8 @@ hipError_t launch_mfma8(int epi, const MfmaParams& p, int splits, hipStream_t s)
 template <bool AK, bool BKC>
 hipError_t launch_mfma(int epi, const MfmaParams& p, int splits, bool direct, hipStream_t s) {
   if (NC_GEMM_NT8 && AK && BKC && direct) return launch_mfma8<false>(epi, p, splits, s);
+  if (NC_GEMM_TN_DIRECT && !AK && !BKC && direct) return launch_tn_direct(epi, p, splits, s);
   if (NC_GEMM_NT8 && !AK && !BKC) return launch_mfma8<true>(epi, p, splits, s);
-  // direct staging only matters for K-contiguous operands
   if (direct && (AK || BKC)) return launch_mfma<AK, BKC, true>(epi, p, splits, s);
   return launch_mfma<AK, BKC, false>(epi, p, splits, s);
 }
