@@ -16,7 +16,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -53,39 +52,55 @@ def build_device_inputs(cfg, torch, nc):
     return inp, ccfg, params, grads, ids, tgt, tb, ws
 
 
-def time_dominant_kernel(cfg, torch, nc, reps=20):
-    """The forward MLP up-projection GEMM with its fused relu^2 epilogue
-    (M = B*T, N = d_ff, K = d_model) -- the largest single launch of the step
-    -- timed with HIP events on the stream it is launched on."""
-    M, d, F = cfg.tokens, cfg.d_model, cfg.d_ff
-    dev = "cuda"
-    g = torch.Generator(device=dev).manual_seed(0)
-    m = torch.randn(M, d, device=dev, generator=g).to(torch.bfloat16)
-    w = (torch.randn(F, d, device=dev, generator=g) / math.sqrt(d)).to(torch.bfloat16)
-    u = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
-    a2 = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
-    s = torch.cuda.current_stream()
-    for _ in range(3):
-        nc.nc_gemm_bf16(0, 1, M, F, d, m, d, w, d, u, F, epilogue=nc.NC_EPI_RELU2, aux_out=a2, stream=s)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(reps):
-        nc.nc_gemm_bf16(0, 1, M, F, d, m, d, w, d, u, F, epilogue=nc.NC_EPI_RELU2, aux_out=a2, stream=s)
-    e1.record(s)
-    e1.synchronize()
-    avg_s = e0.elapsed_time(e1) / 1e3 / reps
-    flops = 2.0 * M * F * d
-    achieved = flops / avg_s / 1e12
+FAMILIES = {
+    # name: (probe family, kernel symbol in profiles, what it computes)
+    "wgrad": ("NC_PROBE_GEMM_WGRAD", "gemm_tn_direct_kernel",
+              "weight-gradient GEMMs dW = dY^T X (K = tokens, split-K partial products)"),
+    "nt": ("NC_PROBE_GEMM_NT", "gemm_mfma8_kernel",
+           "K-contiguous GEMMs (forward projections and activation gradients)"),
+    "attn_fwd": ("NC_PROBE_ATTN_FWD", "attn_fwd_kernel", "causal MQA attention forward"),
+    "attn_dq": ("NC_PROBE_ATTN_DQ", "attn_dq_kernel", "attention backward, dQ"),
+    "attn_dkv": ("NC_PROBE_ATTN_DKV", "attn_dkv_kernel", "attention backward, dK and dV"),
+}
+DOMINANT = "wgrad"   # largest share of kernel time in the committed kernel-trace summary
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/<kernel>_traffic.md), or None if there is none or the kernel's
+    source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    src = fields.get("source")
+    if not src or "traffic_bytes_per_launch" not in fields:
+        return None
+    digest = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+    if digest != fields.get("source_sha256"):
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
+def roofline(name, ms, launches, flops):
+    fam = FAMILIES[name]
+    achieved = flops / (ms / 1e3) / 1e12
     return {
-        "kernel": "gemm_mfma_kernel<NT, relu2> (MLP up-projection)",
-        "shape": {"M": M, "N": F, "K": d},
-        "avg_launch_us": avg_s * 1e6,
+        "kernel": f"{fam[1]}: {fam[2]}",
+        "avg_launch_us": 1e3 * ms / max(launches, 1),
+        "launches": launches,
+        "flops_per_launch": flops / max(launches, 1),
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": None,
+        "traffic": stored_traffic(fam[1]),
     }
 
 
@@ -99,7 +114,7 @@ def cpu_baseline(cfg, inp, budget_tokens=None):
         cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    n = budget_tokens or (256 if cfg.d_model >= 768 else cfg.seq_len)
+    n = budget_tokens or cfg.seq_len
     p = oracle.to_f64_params(inp["weights"])
     ids = inp["ids"][:1, :n]
     tg = inp["targets"][:1, :n]
@@ -124,6 +139,9 @@ def main():
     ap.add_argument("--config", default="d20", choices=["tiny", "small", "d12", "d20", "d26"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None)
+    ap.add_argument("--roofline-kernel", default=DOMINANT, choices=sorted(FAMILIES))
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with one 1 GiB device-to-device copy (counter calibration runs)")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", a.gpus))
     if a.gpus != 1 or world != 1:
@@ -152,6 +170,8 @@ def main():
     if nc.nc_sync_status(ws) != nc.NC_OK:
         raise RuntimeError("device flag raised during warmup")
     torch.cuda.synchronize()
+    fam = FAMILIES[a.roofline_kernel]
+    nc.nc_probe_start(getattr(nc, fam[0]), 512 * a.steps)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(s)
@@ -161,6 +181,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_s = e0.elapsed_time(e1) / 1e3
+    roof = roofline(a.roofline_kernel, *nc.nc_probe_stop())
     elapsed = max(wall, gpu_s)
     tokens = cfg.tokens * a.steps
     value = tokens / elapsed
@@ -169,8 +190,14 @@ def main():
     log(f"[bench] {a.steps} steps in {elapsed:.3f} s: {value:.0f} tok/s, {tflops:.1f} TFLOP/s "
         f"({100 * tflops / PEAK_BF16_TFLOPS:.2f}% of bf16 peak), loss {float(loss):.4f} bpb {float(bpb):.4f}")
 
-    roof = time_dominant_kernel(cfg, torch, nc)
-    log(f"[bench] dominant kernel: {roof['achieved']} TFLOP/s ({roof['avg_launch_us']:.0f} us/launch)")
+    log(f"[bench] {roof['kernel']}: {roof['launches']} launches, {roof['avg_launch_us']:.1f} us/launch, "
+        f"{roof['achieved']} TFLOP/s")
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 1 GiB device to device (calibration)")
     base = None
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
@@ -200,7 +227,7 @@ def main():
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
-        "roofline_kernel": roof["kernel"],
+        "roofline_kernel": {k: roof[k] for k in ("kernel", "launches", "avg_launch_us", "flops_per_launch")},
         "cpu_baseline": base,
     }
     print(json.dumps(out), flush=True)

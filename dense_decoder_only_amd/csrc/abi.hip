@@ -4,6 +4,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace nc {
 
 namespace {
@@ -24,7 +27,95 @@ int check_launch(const char* what) {
   return NC_OK;
 }
 
+namespace {
+struct Probe {
+  std::mutex mu;
+  std::atomic<int> family{NC_PROBE_OFF};
+  std::vector<hipEvent_t> ev;  // 2 per launch
+  int used = 0;                // pairs recorded
+  int open = -1;               // pair whose end is pending
+  int64_t dropped = 0;
+  double flops = 0;
+} g_probe;
+
+void probe_release() {
+  for (hipEvent_t e : g_probe.ev) (void)hipEventDestroy(e);
+  g_probe.ev.clear();
+  g_probe.used = 0;
+  g_probe.open = -1;
+  g_probe.dropped = 0;
+  g_probe.flops = 0;
+}
+}  // namespace
+
+void probe_begin(int family, hipStream_t s) {
+  if (g_probe.family.load(std::memory_order_relaxed) != family || family == NC_PROBE_OFF) return;
+  std::lock_guard<std::mutex> lk(g_probe.mu);
+  if (g_probe.family.load() != family) return;
+  if (2 * (g_probe.used + 1) > (int)g_probe.ev.size()) {
+    ++g_probe.dropped;
+    return;
+  }
+  g_probe.open = g_probe.used;
+  (void)hipEventRecord(g_probe.ev[2 * g_probe.used], s);
+}
+
+void probe_end(int family, hipStream_t s, double flops) {
+  if (g_probe.family.load(std::memory_order_relaxed) != family || family == NC_PROBE_OFF) return;
+  std::lock_guard<std::mutex> lk(g_probe.mu);
+  if (g_probe.family.load() != family || g_probe.open != g_probe.used) return;
+  (void)hipEventRecord(g_probe.ev[2 * g_probe.used + 1], s);
+  g_probe.flops += flops;
+  ++g_probe.used;
+  g_probe.open = -1;
+}
+
 }  // namespace nc
+
+extern "C" int nc_probe_start(int family, int max_launches) {
+  NC_REQUIRE(family >= NC_PROBE_OFF && family <= NC_PROBE_ATTN_DKV, NC_ERR_INVALID_ARG, "probe: unknown family %d",
+             family);
+  NC_REQUIRE(max_launches >= 0 && max_launches <= (1 << 20), NC_ERR_INVALID_ARG, "probe: max_launches %d",
+             max_launches);
+  std::lock_guard<std::mutex> lk(nc::g_probe.mu);
+  nc::g_probe.family.store(NC_PROBE_OFF);
+  nc::probe_release();
+  if (family == NC_PROBE_OFF) return NC_OK;
+  nc::g_probe.ev.resize(2 * (size_t)max_launches);
+  for (size_t i = 0; i < nc::g_probe.ev.size(); ++i) {
+    const hipError_t e = hipEventCreate(&nc::g_probe.ev[i]);
+    if (e != hipSuccess) {
+      nc::g_probe.ev.resize(i);
+      nc::probe_release();
+      return nc::set_error(NC_ERR_HIP, "probe: hipEventCreate: %s", hipGetErrorString(e));
+    }
+  }
+  nc::g_probe.family.store(family);
+  return NC_OK;
+}
+
+extern "C" int nc_probe_stop(double* total_ms, int64_t* launches, double* flops) {
+  NC_REQUIRE(total_ms && launches && flops, NC_ERR_INVALID_ARG, "probe: null output pointer");
+  std::lock_guard<std::mutex> lk(nc::g_probe.mu);
+  nc::g_probe.family.store(NC_PROBE_OFF);
+  double ms = 0;
+  int rc = NC_OK;
+  for (int i = 0; i < nc::g_probe.used && rc == NC_OK; ++i) {
+    float t = 0;
+    hipError_t e = hipEventSynchronize(nc::g_probe.ev[2 * i + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, nc::g_probe.ev[2 * i], nc::g_probe.ev[2 * i + 1]);
+    if (e != hipSuccess) rc = nc::set_error(NC_ERR_HIP, "probe: event %d: %s", i, hipGetErrorString(e));
+    ms += t;
+  }
+  *total_ms = ms;
+  *launches = nc::g_probe.used;
+  *flops = nc::g_probe.flops;
+  if (rc == NC_OK && nc::g_probe.dropped)
+    rc = nc::set_error(NC_ERR_WORKSPACE, "probe: %lld launches beyond max_launches were not timed",
+                       (long long)nc::g_probe.dropped);
+  nc::probe_release();
+  return rc;
+}
 
 extern "C" const char* nc_last_error(void) { return nc::g_err; }
 

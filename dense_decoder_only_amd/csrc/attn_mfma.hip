@@ -545,7 +545,10 @@ int attn_mfma_fwd(const void* qkv, int B, int T, int H, float scale, void* o, fl
   a.scale = scale;
   a.scale_log2 = scale * LOG2E;
   const int nrb = (T * H + QB - 1) / QB;
+  const double fl = 2.0 * B * H * (double)HD * T * T;
+  probe_begin(NC_PROBE_ATTN_FWD, s);
   attn_fwd_kernel<<<dim3(B, nrb), 256, 0, s>>>(a);
+  probe_end(NC_PROBE_ATTN_FWD, s, fl);
   return check_launch("attn_fwd_kernel");
 }
 
@@ -568,9 +571,14 @@ int attn_mfma_bwd(const void* qkv, const void* o, const void* dout, const float*
   a.nkb = (T + KB - 1) / KB;
   a.smax = attn_mfma_smax(T, H);
   const int nrb = (T * H + QB - 1) / QB;
+  const double fl = 2.0 * B * H * (double)HD * T * T;
+  probe_begin(NC_PROBE_ATTN_DQ, s);
   attn_dq_kernel<<<dim3(B, nrb), 256, 0, s>>>(a);
+  probe_end(NC_PROBE_ATTN_DQ, s, fl);
   NC_TRY(check_launch("attn_dq_kernel"));
+  probe_begin(NC_PROBE_ATTN_DKV, s);
   attn_dkv_kernel<<<dim3(B, a.nkb * a.smax), 256, 0, s>>>(a);
+  probe_end(NC_PROBE_ATTN_DKV, s, fl);
   NC_TRY(check_launch("attn_dkv_kernel"));
   attn_dkv_reduce_kernel<<<dim3(a.nkb, B), 256, 0, s>>>(a);
   return check_launch("attn_dkv_reduce_kernel");

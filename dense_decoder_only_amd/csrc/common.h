@@ -63,6 +63,9 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ---------------------------------------------------------------------------
 int set_error(int code, const char* fmt, ...);
 int check_launch(const char* what);
+// Kernel timer hooks (nc_probe_*): cheap no-ops unless `family` is armed.
+void probe_begin(int family, hipStream_t s);
+void probe_end(int family, hipStream_t s, double flops);
 
 }  // namespace nc
 

@@ -792,8 +792,19 @@ hipError_t launch_mfma8(int epi, const MfmaParams& p, int splits, hipStream_t s)
 
 template <bool AK, bool BKC>
 hipError_t launch_mfma(int epi, const MfmaParams& p, int splits, bool direct, hipStream_t s) {
-  if (NC_GEMM_NT8 && AK && BKC && direct) return launch_mfma8<false>(epi, p, splits, s);
-  if (NC_GEMM_TN_DIRECT && !AK && !BKC && direct) return launch_tn_direct(epi, p, splits, s);
+  const double flops = 2.0 * p.M * p.N * p.K;
+  if (NC_GEMM_NT8 && AK && BKC && direct) {
+    probe_begin(NC_PROBE_GEMM_NT, s);
+    const hipError_t e = launch_mfma8<false>(epi, p, splits, s);
+    probe_end(NC_PROBE_GEMM_NT, s, flops);
+    return e;
+  }
+  if (NC_GEMM_TN_DIRECT && !AK && !BKC && direct) {
+    probe_begin(NC_PROBE_GEMM_WGRAD, s);
+    const hipError_t e = launch_tn_direct(epi, p, splits, s);
+    probe_end(NC_PROBE_GEMM_WGRAD, s, flops);
+    return e;
+  }
   if (NC_GEMM_NT8 && !AK && !BKC) return launch_mfma8<true>(epi, p, splits, s);
   if (direct && (AK || BKC)) return launch_mfma<AK, BKC, true>(epi, p, splits, s);
   return launch_mfma<AK, BKC, false>(epi, p, splits, s);

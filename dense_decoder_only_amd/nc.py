@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libnc.so")
 NC_OK, NC_ERR_INVALID_ARG, NC_ERR_UNSUPPORTED, NC_ERR_WORKSPACE, NC_ERR_HIP, NC_ERR_DEVICE_FLAG = range(6)
 NC_F32, NC_BF16 = 0, 1
 NC_EPI_STORE, NC_EPI_RELU2, NC_EPI_RELU2_BWD = 0, 1, 2
+(NC_PROBE_OFF, NC_PROBE_GEMM_WGRAD, NC_PROBE_GEMM_NT, NC_PROBE_ATTN_FWD, NC_PROBE_ATTN_DQ,
+ NC_PROBE_ATTN_DKV) = range(6)
 
 c_int, c_i64, c_f, c_sz, c_p = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -50,6 +52,9 @@ _SIGS = {
     "nc_last_error": (ctypes.c_char_p, []),
     "nc_version": (ctypes.c_char_p, []),
     "nc_sync_status": (c_int, [c_p, c_p]),
+    "nc_probe_start": (c_int, [c_int, c_int]),
+    "nc_probe_stop": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64),
+                              ctypes.POINTER(ctypes.c_double)]),
     "nc_step_workspace_bytes": (c_sz, [ctypes.POINTER(nc_config)]),
     "nc_step_fwd_bwd": (c_int, [ctypes.POINTER(nc_config), ctypes.POINTER(nc_params), ctypes.POINTER(nc_grads),
                                 c_p, c_p, c_p, c_p, c_sz, c_p, c_p, c_p, c_p]),
@@ -147,6 +152,17 @@ def nc_last_error() -> str:
 def nc_sync_status(flag, stream=None) -> int:
     """Returns the status code (NC_OK or NC_ERR_DEVICE_FLAG) instead of raising on the flag."""
     return load().nc_sync_status(_p(flag), _stream(stream))
+
+
+def nc_probe_start(family: int, max_launches: int) -> None:
+    _check(load().nc_probe_start(int(family), int(max_launches)))
+
+
+def nc_probe_stop() -> tuple:
+    """Returns (total_ms, launches, flops) of the bracketed launches."""
+    ms, n, fl = ctypes.c_double(), c_i64(), ctypes.c_double()
+    _check(load().nc_probe_stop(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(fl)))
+    return ms.value, n.value, fl.value
 
 
 def nc_step_workspace_bytes(cfg: nc_config) -> int:

@@ -30,7 +30,8 @@
  *     is enqueued and nc_last_error() returns a message (thread-local).
  *     Nothing aborts, prints or throws across this ABI.
  *   - Calls are thread-safe; the library has no mutable global state other
- *     than the thread-local error message.
+ *     than the thread-local error message and the kernel timer (nc_probe_*),
+ *     which a mutex guards.
  *   - Out-of-range token ids are caught on the device: the row is treated as
  *     zeros and a device flag (an int32 given by the caller) is set to 1;
  *     nc_sync_status reads it.
@@ -112,6 +113,37 @@ const char* nc_version(void);
  * Returns NC_ERR_DEVICE_FLAG if it is nonzero, NC_OK otherwise.  The step's
  * flag is the first int32 of its workspace. */
 int nc_sync_status(const int32_t* flag, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Kernel timer, for measurement only.  While armed, every launch of the
+ * chosen kernel family -- from any entry point, on any stream -- is bracketed
+ * by a pair of HIP events recorded on the stream it is launched on, and the
+ * library adds up the algorithmic FLOPs of those launches:
+ *   GEMM families: 2 M N K per launch (a split-K launch counts its whole K);
+ *   attention (causal, per launch over B sequences of T tokens, H heads of
+ *   width hd, counting half of the T x T score square): forward
+ *   2 B H hd T^2 (two products), dQ 2 B H hd T^2 (dP and dQ), dK/dV
+ *   2 B H hd T^2 (dV and dK); recomputed scores are not counted.
+ * The events add a few microseconds per bracketed launch.
+ *   nc_probe_start: arms the timer for `family` with room for `max_launches`
+ *     launches (events are created here).  Re-arming discards what was
+ *     recorded.  Launches beyond the room are not bracketed and are reported
+ *     by nc_probe_stop as an error.
+ *   nc_probe_stop: waits for the recorded events, writes (host pointers) the
+ *     summed elapsed time between each pair, the number of launches and the
+ *     summed FLOPs, then disarms and releases the events.
+ * ------------------------------------------------------------------------- */
+typedef enum {
+  NC_PROBE_OFF = 0,
+  NC_PROBE_GEMM_WGRAD = 1, /* weight-gradient GEMMs: both operands with K as rows (TN) */
+  NC_PROBE_GEMM_NT = 2,    /* K-contiguous GEMMs (forward projections, dX)           */
+  NC_PROBE_ATTN_FWD = 3,   /* causal MQA attention forward                           */
+  NC_PROBE_ATTN_DQ = 4,    /* attention backward, dQ kernel                          */
+  NC_PROBE_ATTN_DKV = 5    /* attention backward, dK/dV kernel                       */
+} nc_probe_family;
+
+int nc_probe_start(int family, int max_launches);
+int nc_probe_stop(double* total_ms, int64_t* launches, double* flops);
 
 /* ---------------------------------------------------------------------------
  * Whole step: forward and backward of the mean next-token loss [NEWS], with
