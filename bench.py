@@ -53,24 +53,28 @@ def build_device_inputs(cfg, torch, nc):
 
 
 FAMILIES = {
-    # name: (probe family, kernel symbol in profiles, what it computes)
-    "wgrad": ("NC_PROBE_GEMM_WGRAD", "gemm_tn_direct_kernel",
-              "weight-gradient GEMMs dW = dY^T X (K = tokens, split-K partial products)"),
-    "nt": ("NC_PROBE_GEMM_NT", "gemm_mfma8_kernel",
-           "K-contiguous GEMMs (forward projections and activation gradients)"),
-    "attn_fwd": ("NC_PROBE_ATTN_FWD", "attn_fwd_kernel", "causal MQA attention forward"),
-    "attn_dq": ("NC_PROBE_ATTN_DQ", "attn_dq_kernel", "attention backward, dQ"),
-    "attn_dkv": ("NC_PROBE_ATTN_DKV", "attn_dkv_kernel", "attention backward, dK and dV"),
+    # name: (probe family, kernel symbol in the profiles, what it computes,
+    #        committed counter summary giving its HBM bytes per launch)
+    "wgrad": ("NC_PROBE_GEMM_WGRAD", "gemm_pipe_kernel<E, true>",
+              "weight-gradient GEMMs dW = dY^T X (K = tokens, split-K partial products)",
+              "gemm_pipe_kernel_tn_d20_traffic.md"),
+    "nt": ("NC_PROBE_GEMM_NT", "gemm_pipe_kernel<E, false>",
+           "K-contiguous GEMMs (forward projections and activation gradients)", None),
+    "attn_fwd": ("NC_PROBE_ATTN_FWD", "attn_fwd_kernel", "causal MQA attention forward", None),
+    "attn_dq": ("NC_PROBE_ATTN_DQ", "attn_dq_kernel", "attention backward, dQ", None),
+    "attn_dkv": ("NC_PROBE_ATTN_DKV", "attn_dkv_kernel", "attention backward, dK and dV", None),
 }
 DOMINANT = "wgrad"   # largest share of kernel time in the committed kernel-trace summary
 
 
-def stored_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (profiles/<kernel>_traffic.md), or None if there is none or the kernel's
-    source has changed since the counters were taken."""
+def stored_traffic(summary):
+    """HBM bytes per launch from a committed counter summary under profiles/,
+    or None if there is none or the kernel's source has changed since the
+    counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.md")
+    if summary is None:
+        return None
+    path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -100,7 +104,7 @@ def roofline(name, ms, launches, flops):
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": stored_traffic(fam[1]),
+        "traffic": stored_traffic(fam[3]),
     }
 
 

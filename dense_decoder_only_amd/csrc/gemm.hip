@@ -353,11 +353,13 @@ __device__ __forceinline__ void stage_direct8(const bf16* __restrict__ P, int64_
 }
 
 // 8 waves (2 per SIMD) in a 2 x 4 grid of 128 x 64 wave tiles.
-//   TN = false: both operands K-contiguous and every k-tile full; tiles are
-//               staged with direct global -> LDS loads.
 //   TN = true:  both operands M/N-contiguous (the weight-gradient form); each
 //               half of the block (256 threads) stages one operand through
-//               registers with the 8x8 transpose, any K multiple of 8.
+//               registers with the 8x8 transpose, any K multiple of 8.  Only
+//               launched when a k-tile is ragged (full tiles take the
+//               pipelined kernel below).
+//   TN = false: K-contiguous operands staged by DMA (superseded by the
+//               pipelined kernel; kept for the shared code path).
 template <int EPI, bool TN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_mfma8_kernel(MfmaParams p) {
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * BM * BK];
@@ -601,9 +603,6 @@ hipError_t launch_mfma(int epi, const MfmaParams& p, int splits, hipStream_t s) 
   return hipGetLastError();
 }
 
-#ifndef NC_GEMM_NT8
-#define NC_GEMM_NT8 1
-#endif
 
 // ---------------------------------------------------------------------------
 // Weight-gradient form (both operands M/N-contiguous, K = tokens) with direct
@@ -615,8 +614,8 @@ hipError_t launch_mfma(int epi, const MfmaParams& p, int splits, hipStream_t s) 
 // k-rows kb..kb+3 of column c0 + j).  Both operands use the same k-slot order
 // (slot e of half h <-> k = 16 ks + 8 (e >> 2) + 4 h + (e & 3)).  16-byte
 // chunks are swizzled by c ^ 4 (row & 3), which spreads a 32-lane transposed
-// read over all 64 banks.  8 waves in a 2 x 4 grid of 128 x 64.
-// Requires every k-tile to be full.
+// read over all 64 banks.  Used by the pipelined kernel below; every k-tile
+// must be full.
 // ---------------------------------------------------------------------------
 constexpr int TROW = 256;  // columns per staged k-row
 __device__ __forceinline__ int tn_off(int row, int c) { return row * TROW + ((c ^ (4 * (row & 3))) << 3); }
@@ -651,8 +650,69 @@ __device__ __forceinline__ bf16x8_t frag_tn(const bf16* S, int ks, int col0, int
   return __builtin_bit_cast(bf16x8_t, make_uint4(u.x, u.y, v.x, v.y));
 }
 
-template <int EPI>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_tn_direct_kernel(MfmaParams p) {
+// ---------------------------------------------------------------------------
+// Pipelined 8-wave kernel for both direct-staged forms (TN = false: operands
+// K-contiguous, staged with stage_direct8 and read as row fragments;
+// TN = true: operands with K as rows, staged with stage_tn and read with
+// ds_read_b64_tr_b16).  Same 2 x 4 grid of 128 x 64 wave tiles as above, but
+// the k loop is rotated so the MFMA pipe never waits on a barrier-fresh tile:
+// the block barrier sits inside the last k-step, after its first MFMAs, and
+// right after it the waves issue the DMA of tile kt + 2 (into the buffer just
+// released) and the first fragment reads of tile kt + 1, while the rest of
+// the last k-step's MFMAs run.  Every k-tile must be full.
+// ---------------------------------------------------------------------------
+#ifndef NC_GEMM_PIPE_PRE
+#define NC_GEMM_PIPE_PRE 2  // MFMAs of the last k-step issued before the barrier
+#endif
+
+template <bool TN>
+__device__ __forceinline__ void pipe_stage(const MfmaParams& p, int m0, int n0, int k0, bf16* a_buf, bf16* b_buf,
+                                           int wave, int lane) {
+  if constexpr (TN) {
+    stage_tn(p.A, p.lda, m0, p.M, k0, a_buf, wave, lane);
+    stage_tn(p.B, p.ldb, n0, p.N, k0, b_buf, wave, lane);
+  } else {
+    stage_direct8(p.A, p.lda, m0, p.M, k0, a_buf, wave, lane);
+    stage_direct8(p.B, p.ldb, n0, p.N, k0, b_buf, wave, lane);
+  }
+}
+
+template <bool TN>
+__device__ __forceinline__ void pipe_frags(const bf16* a_buf, const bf16* b_buf, int ks, int wm, int wn, int lane,
+                                           bf16x8_t (&fa)[4], bf16x8_t (&fb)[2]) {
+  if constexpr (TN) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = frag_tn(a_buf, ks, wm * 128 + i * 32, lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[j] = frag_tn(b_buf, ks, wn * 64 + j * 32, lane);
+  } else {
+    const int frow = lane & 31, fhalf = lane >> 5;
+    const int ch = ((ks * 2 + fhalf) ^ swz(frow)) << 3;
+    const bf16* a_s = a_buf + (wm * 128 + frow) * BK + ch;
+    const bf16* b_s = b_buf + (wn * 64 + frow) * BK + ch;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(a_s + i * 32 * BK);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(b_s + j * 32 * BK);
+  }
+}
+
+// Scheduling pattern: NG groups of one MFMA followed by a share of NRD DS reads.
+template <int G, int NG, int NRD>
+__device__ __forceinline__ void sched_mfma_ds() {
+  if constexpr (G < NG) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NRD / NG + (G < NRD % NG ? 1 : 0), 0);
+    sched_mfma_ds<G + 1, NG, NRD>();
+  }
+}
+
+// DS reads per fragment set: 6 row reads, or 12 transposed half reads.
+template <bool TN>
+constexpr int pipe_nreads() { return TN ? 12 : 6; }
+
+template <int EPI, bool TN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pipe_kernel(MfmaParams p) {
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * BM * BK];
   bf16* const As = lds;
   bf16* const Bs = lds + 2 * BM * BK;
@@ -678,6 +738,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int kend = kbeg + p.k_per_split;
   kend = kend < p.K ? kend : p.K;
   const int nk = (kend - kbeg) / BK;
+  const int klast = kbeg + (nk - 1) * BK;
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -687,51 +748,64 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  stage_tn(p.A, p.lda, m0, p.M, kbeg, As, wave, lane);
-  stage_tn(p.B, p.ldb, n0, p.N, kbeg, Bs, wave, lane);
+  pipe_stage<TN>(p, m0, n0, kbeg, As, Bs, wave, lane);
+  pipe_stage<TN>(p, m0, n0, nk > 1 ? kbeg + BK : kbeg, As + BM * BK, Bs + BN * BK, wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  constexpr int NR = pipe_nreads<TN>();
+  bf16x8_t fa[2][4], fb[2][2];
+  pipe_frags<TN>(As, Bs, 0, wm, wn, lane, fa[0], fb[0]);
+
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1, nxt = cur ^ 1;
-    const int k1 = kt + 1 < nk ? kbeg + (kt + 1) * BK : kbeg;
-    stage_tn(p.A, p.lda, m0, p.M, k1, As + nxt * (BM * BK), wave, lane);
-    stage_tn(p.B, p.ldb, n0, p.N, k1, Bs + nxt * (BN * BK), wave, lane);
-    const bf16* a_s = As + cur * (BM * BK);
-    const bf16* b_s = Bs + cur * (BN * BK);
-    bf16x8_t fa[2][4], fb[2][2];
+    const int cur = kt & 1;
+    const bf16* a_c = As + cur * (BM * BK);
+    const bf16* b_c = Bs + cur * (BN * BK);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = frag_tn(a_s, 0, wm * 128 + i * 32, lane);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) fb[0][j] = frag_tn(b_s, 0, wn * 64 + j * 32, lane);
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 3; ++ks) {
       const int c = ks & 1;
-      if (ks + 1 < 4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fa[c ^ 1][i] = frag_tn(a_s, ks + 1, wm * 128 + i * 32, lane);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) fb[c ^ 1][j] = frag_tn(b_s, ks + 1, wn * 64 + j * 32, lane);
-      }
+      pipe_frags<TN>(a_c, b_c, ks + 1, wm, wn, lane, fa[c ^ 1], fb[c ^ 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][i], acc[i][j], 0, 0, 0);
-      if (ks + 1 < 4) {
+      // all of the next k-step's reads go out under the first MFMAs
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-        }
+      for (int g = 0; g < 3; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NR / 3, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
     }
+    // last k-step (fragments in set 1): PRE MFMAs, barrier, then the DMA of
+    // tile kt + 2 into the released buffer and tile kt + 1's first fragments
+    // under the remaining MFMAs.
+#pragma unroll
+    for (int q = 0; q < NC_GEMM_PIPE_PRE; ++q)
+      acc[q >> 1][q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][q & 1], fa[1][q >> 1], acc[q >> 1][q & 1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // tile kt + 1 has landed (this wave's DMA) and this wave's reads of tile
+    // kt are done; the barrier extends both to the whole block
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    const int k2 = kt + 2 < nk ? kbeg + (kt + 2) * BK : klast;
+    pipe_stage<TN>(p, m0, n0, k2, As + cur * (BM * BK), Bs + cur * (BN * BK), wave, lane);
+    pipe_frags<TN>(As + (cur ^ 1) * (BM * BK), Bs + (cur ^ 1) * (BN * BK), 0, wm, wn, lane, fa[0], fb[0]);
+#pragma unroll
+    for (int q = NC_GEMM_PIPE_PRE; q < 8; ++q)
+      acc[q >> 1][q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][q & 1], fa[1][q >> 1], acc[q >> 1][q & 1], 0, 0, 0);
+    constexpr int POST = 8 - NC_GEMM_PIPE_PRE;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x010, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x010, 4, 0);
+    sched_mfma_ds<0, POST - 2, NR>();
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
-  // epilogue: same LDS staging as the 8-wave kernel (wave tile 128 x 64)
   constexpr int SROW = 68;
   float* stage = reinterpret_cast<float*>(lds) + wave * (32 * SROW);
 #pragma unroll
@@ -754,26 +828,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-template <int EPI>
-hipError_t launch_tn_direct_epi(const MfmaParams& p, int splits, hipStream_t s) {
-  gemm_tn_direct_kernel<EPI><<<dim3(p.tiles_m * p.tiles_n, 1, splits), 512, 0, s>>>(p);
+template <bool TN>
+hipError_t launch_pipe(int epi, const MfmaParams& p, int splits, hipStream_t s) {
+  dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
+  switch (epi) {
+    case E_STORE_F32: gemm_pipe_kernel<E_STORE_F32, TN><<<grid, 512, 0, s>>>(p); break;
+    case E_ACC_F32: gemm_pipe_kernel<E_ACC_F32, TN><<<grid, 512, 0, s>>>(p); break;
+    case E_STORE_BF16: gemm_pipe_kernel<E_STORE_BF16, TN><<<grid, 512, 0, s>>>(p); break;
+    case E_RELU2: gemm_pipe_kernel<E_RELU2, TN><<<grid, 512, 0, s>>>(p); break;
+    case E_RELU2_BWD: gemm_pipe_kernel<E_RELU2_BWD, TN><<<grid, 512, 0, s>>>(p); break;
+    default: gemm_pipe_kernel<E_PARTIAL, TN><<<grid, 512, 0, s>>>(p); break;
+  }
   return hipGetLastError();
 }
-
-hipError_t launch_tn_direct(int epi, const MfmaParams& p, int splits, hipStream_t s) {
-  switch (epi) {
-    case E_STORE_F32: return launch_tn_direct_epi<E_STORE_F32>(p, splits, s);
-    case E_ACC_F32: return launch_tn_direct_epi<E_ACC_F32>(p, splits, s);
-    case E_STORE_BF16: return launch_tn_direct_epi<E_STORE_BF16>(p, splits, s);
-    case E_RELU2: return launch_tn_direct_epi<E_RELU2>(p, splits, s);
-    case E_RELU2_BWD: return launch_tn_direct_epi<E_RELU2_BWD>(p, splits, s);
-    default: return launch_tn_direct_epi<E_PARTIAL>(p, splits, s);
-  }
-}
-
-#ifndef NC_GEMM_TN_DIRECT
-#define NC_GEMM_TN_DIRECT 1
-#endif
 
 template <bool TN>
 hipError_t launch_mfma8(int epi, const MfmaParams& p, int splits, hipStream_t s) {
@@ -793,19 +860,24 @@ hipError_t launch_mfma8(int epi, const MfmaParams& p, int splits, hipStream_t s)
 template <bool AK, bool BKC>
 hipError_t launch_mfma(int epi, const MfmaParams& p, int splits, bool direct, hipStream_t s) {
   const double flops = 2.0 * p.M * p.N * p.K;
-  if (NC_GEMM_NT8 && AK && BKC && direct) {
+  if (AK && BKC && direct) {
     probe_begin(NC_PROBE_GEMM_NT, s);
-    const hipError_t e = launch_mfma8<false>(epi, p, splits, s);
+    const hipError_t e = launch_pipe<false>(epi, p, splits, s);
     probe_end(NC_PROBE_GEMM_NT, s, flops);
     return e;
   }
-  if (NC_GEMM_TN_DIRECT && !AK && !BKC && direct) {
+  if (!AK && !BKC && direct) {
     probe_begin(NC_PROBE_GEMM_WGRAD, s);
-    const hipError_t e = launch_tn_direct(epi, p, splits, s);
+    const hipError_t e = launch_pipe<true>(epi, p, splits, s);
     probe_end(NC_PROBE_GEMM_WGRAD, s, flops);
     return e;
   }
-  if (NC_GEMM_NT8 && !AK && !BKC) return launch_mfma8<true>(epi, p, splits, s);
+  if (!AK && !BKC) {  // weight-gradient form with a ragged k-tile
+    probe_begin(NC_PROBE_GEMM_WGRAD, s);
+    const hipError_t e = launch_mfma8<true>(epi, p, splits, s);
+    probe_end(NC_PROBE_GEMM_WGRAD, s, flops);
+    return e;
+  }
   if (direct && (AK || BKC)) return launch_mfma<AK, BKC, true>(epi, p, splits, s);
   return launch_mfma<AK, BKC, false>(epi, p, splits, s);
 }
