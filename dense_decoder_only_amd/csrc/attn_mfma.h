@@ -18,6 +18,7 @@ struct AttnMfmaArgs {
   int64_t S;           // qkv row stride in elements
   float scale, scale_log2;
   int nkb, smax;
+  uint32_t hmagic;     // ceil(2^32 / H): r / H == umulhi(r, hmagic) for r < 2^32 / H^2
 };
 
 size_t attn_mfma_bwd_workspace_bytes(int B, int T, int H);

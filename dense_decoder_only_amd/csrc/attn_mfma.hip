@@ -47,6 +47,7 @@ constexpr int KB = 128;   // keys per dK/dV block (4 waves x 32)
 constexpr int QT = 64;    // query rows per dK/dV tile
 constexpr int QCH = 5120; // query rows per dK/dV split
 constexpr int TILE = 64 * HD;  // elements of one [64][128] tile
+constexpr int QTILE = QT * HD; // elements of one dK/dV query tile
 constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __bf16 bf16x4_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
@@ -55,14 +56,15 @@ __device__ __forceinline__ int tswz(int r) { return ((r & 3) << 2) | ((r >> 2) &
 // element offset of (row, 8-column chunk c) in a swizzled [rows][128] tile
 __device__ __forceinline__ int toff(int row, int c) { return row * HD + ((c ^ tswz(row)) << 3); }
 
-// Direct global -> LDS staging of a [64][128] tile: 16 instructions of 1 KB
-// (4 rows each), 4 per wave.  rowp(row) gives the global address of a row.
-template <typename RowPtr>
+// Direct global -> LDS staging of a [ROWS][128] tile: ROWS / 4 instructions
+// of 1 KB (4 rows each), ROWS / 16 per wave.  rowp(row) gives the global
+// address of a row.
+template <int ROWS = 64, typename RowPtr>
 __device__ __forceinline__ void dma_tile(bf16* S, int wave, int lane, RowPtr rowp) {
   const int rsub = lane >> 4, cp = lane & 15;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int g = wave * 4 + i;
+  for (int i = 0; i < ROWS / 16; ++i) {
+    const int g = wave * (ROWS / 16) + i;
     const int row = g * 4 + rsub;
     const int c = cp ^ tswz(row);
     __builtin_amdgcn_global_load_lds(rowp(row) + c * 8, (__attribute__((address_space(3))) void*)(S + g * 4 * HD),
@@ -97,6 +99,12 @@ __device__ __forceinline__ bf16x8_t pack_p(const f32x16& p, int jp) {
                                                  pack_bf16x2(p[b + 4], p[b + 5]), pack_bf16x2(p[b + 6], p[b + 7])));
 }
 
+// 2^x by the hardware v_exp_f32 (results below 2^-126 flush to zero, which
+// is immaterial for probabilities that are summed with ones of order 1).
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int div_h(int r, uint32_t hmagic) { return (int)__umulhi((uint32_t)r, hmagic); }
+
 __device__ __forceinline__ f32x16 mfma(bf16x8_t a, bf16x8_t b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -114,7 +122,7 @@ __device__ __forceinline__ uint32_t wd(const uint4& q, int w) {
 
 // ------------------------------------------------------------------ forward --
 // grid (B, ceil(R / QB)); heavy (late) row blocks first.
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnMfmaArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnMfmaArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Ks[2 * TILE];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2 * TILE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
@@ -192,24 +200,32 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnMfmaArgs a) {
         }
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
+    // Lazy rescaling: the reference maximum only moves when the tile maximum
+    // exceeds it by more than 8 (log2 units), so probabilities stay <= 2^8
+    // and the rescale of the running sums is skipped (wave-uniformly) on most
+    // tiles.  The result does not depend on the reference.
+    const bool bump = mt > m_run + 8.f;
+    if (__builtin_amdgcn_ballot_w64(bump)) {
+      const float m_new = bump ? mt : m_run;
+      const float alpha = fexp2(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[ht][r] *= alpha;
+    }
     float ls = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(s[st][r] - m_new);
+        const float p = fexp2(s[st][r] - m_run);
         s[st][r] = p;
         ls += p;
       }
     ls += __shfl_xor(ls, 32, 64);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[ht][r] *= alpha;
+    l_run += ls;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -240,7 +256,10 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnMfmaArgs a) {
 
 // ----------------------------------------------------------------------- dQ --
 // Also writes D = rowsum(dO * O) for the key-side kernel.
-__global__ __launch_bounds__(256) void attn_dq_kernel(AttnMfmaArgs a) {
+#ifndef NC_ATTN_DQ_WAVES
+#define NC_ATTN_DQ_WAVES 2  // waves per SIMD the dQ kernel is compiled for
+#endif
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC_ATTN_DQ_WAVES, NC_ATTN_DQ_WAVES))) void attn_dq_kernel(AttnMfmaArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Ks[2 * TILE];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2 * TILE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
@@ -316,18 +335,24 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnMfmaArgs a) {
         dp[st] = mfma(frag_row(V, st * 32 + lc, 2 * ks + h), dreg[ks], dp[st]);
       }
     }
-    const bool need_mask = kv0 + KT - 1 > tmin;
+    if (kv0 + KT - 1 > tmin) {  // the tile crosses some row's diagonal
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = exp2f(s[st][r] * a.scale_log2 - lse2);
-        if (need_mask) {
+        for (int r = 0; r < 16; ++r) {
           const int kv = kv0 + st * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (kv > tq) p = 0.f;
+          const float p = kv > tq ? 0.f : fexp2(s[st][r] * a.scale_log2 - lse2);
+          s[st][r] = p * (dp[st][r] - D);
         }
-        s[st][r] = p * (dp[st][r] - D);
-      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fexp2(s[st][r] * a.scale_log2 - lse2);
+          s[st][r] = p * (dp[st][r] - D);
+        }
+    }
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -361,9 +386,12 @@ __device__ __forceinline__ int nsplit_of(int kb, int H, int R) { return (R - qbe
 // grid (B, nkb * SMAX): block (kb, s) handles key rows kb*128 .. +127 against
 // query rows [qbeg + s*QCH, min(R, qbeg + (s+1)*QCH)).  Writes partial dK^T,
 // dV^T sums (unscaled) to part[(b * nkb + kb) * SMAX + s].
+// One wave per SIMD: K and V of the wave's 32 keys live in registers
+// (64 VGPRs) beside the dK/dV accumulators (128); forcing two waves per SIMD
+// spills them (measured slower).
 __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 Qs[2 * TILE];
-  __shared__ __attribute__((aligned(16))) bf16 Ds[2 * TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[2 * QTILE];
+  __shared__ __attribute__((aligned(16))) bf16 Ds[2 * QTILE];
   __shared__ float lse_s[2][QT], D_s[2][QT];
   __shared__ int tpos_s[2][QT];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
@@ -387,17 +415,18 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
       vreg[ks] = *reinterpret_cast<const bf16x8_t*>(kp + HD + ks * 16);
     }
   }
+
   const int qs0 = qbeg_of(kb, H) + sp * QCH;
   const int qs1 = min(R, qs0 + QCH);
   const int nq = (qs1 - qs0 + QT - 1) / QT;
   auto stage = [&](int i, int buf) {
     const int q0 = qs0 + i * QT;
-    dma_tile(Qs + buf * TILE, w, lane, [&](int row) {
+    dma_tile<QT>(Qs + buf * QTILE, w, lane, [&](int row) {
       const int r = min(q0 + row, R - 1);
-      const int t = r / H;
+      const int t = div_h(r, a.hmagic);
       return base + (int64_t)t * a.S + (r - t * H) * HD;
     });
-    dma_tile(Ds + buf * TILE, w, lane, [&](int row) { return dbase + (int64_t)min(q0 + row, R - 1) * HD; });
+    dma_tile<QT>(Ds + buf * QTILE, w, lane, [&](int row) { return dbase + (int64_t)min(q0 + row, R - 1) * HD; });
   };
   // per-row statistics of a query tile, loaded by threads 0..63 into registers
   float n_lse = 0.f, n_D = 0.f;
@@ -408,7 +437,7 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
       if (r < R) {
         n_lse = a.lse[(int64_t)b * R + r] * LOG2E;
         n_D = a.Dbuf[(int64_t)b * R + r];
-        n_t = r / H;
+        n_t = div_h(r, a.hmagic);
       } else {
         n_lse = INFINITY;  // p = 0 for rows past the end
         n_D = 0.f;
@@ -441,13 +470,14 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
       stage(i + 1, cur ^ 1);
       fetch_stats(i + 1);
     }
-    const bf16* Q = Qs + cur * TILE;
-    const bf16* G = Ds + cur * TILE;
+    const bf16* Q = Qs + cur * QTILE;
+    const bf16* G = Ds + cur * QTILE;
 
-    // S = Q K^T and dP = dO V^T: rows q (two 32-row halves), column = key.
-    f32x16 s[2], dp[2];
+    // S = Q K^T and dP = dO V^T: rows q (one 32-row tile), column = key.
+    constexpr int NQT = QT / 32;
+    f32x16 s[NQT], dp[NQT];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < NQT; ++qt) {
       s[qt] = zero16();
       dp[qt] = zero16();
 #pragma unroll
@@ -456,19 +486,32 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
         dp[qt] = mfma(frag_row(G, qt * 32 + lc, 2 * ks + h), vreg[ks], dp[qt]);
       }
     }
+    // Keys of this block after the earliest query position of the tile need
+    // the causal mask; other tiles skip it (a uniform branch).
+    if (u0 + KB - 1 > div_h(qs0 + i * QT, a.hmagic)) {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = qt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        float p = exp2f(s[qt][r] * a.scale_log2 - lse_s[cur][qi]);
-        if (myu > tpos_s[cur][qi]) p = 0.f;
-        s[qt][r] = p;
-        dp[qt][r] = p * (dp[qt][r] - D_s[cur][qi]);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const float p = myu > tpos_s[cur][qi] ? 0.f : fexp2(s[qt][r] * a.scale_log2 - lse_s[cur][qi]);
+          s[qt][r] = p;
+          dp[qt][r] = p * (dp[qt][r] - D_s[cur][qi]);
+        }
+    } else {
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const float p = fexp2(s[qt][r] * a.scale_log2 - lse_s[cur][qi]);
+          s[qt][r] = p;
+          dp[qt][r] = p * (dp[qt][r] - D_s[cur][qi]);
+        }
+    }
     // dV^T += dO^T P ; dK^T += Q^T dS
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
       for (int jp = 0; jp < 2; ++jp) {
         const bf16x8_t pb = pack_p(s[qt], jp);
@@ -534,6 +577,7 @@ size_t attn_mfma_bwd_workspace_bytes(int B, int T, int H) {
 }
 
 int attn_mfma_fwd(const void* qkv, int B, int T, int H, float scale, void* o, float* lse, hipStream_t s) {
+  NC_REQUIRE((uint64_t)T * H * H < ((uint64_t)1 << 32), NC_ERR_UNSUPPORTED, "attention: T * H^2 must be < 2^32");
   AttnMfmaArgs a{};
   a.qkv = static_cast<const bf16*>(qkv);
   a.o_out = static_cast<bf16*>(o);
@@ -544,6 +588,7 @@ int attn_mfma_fwd(const void* qkv, int B, int T, int H, float scale, void* o, fl
   a.S = (int64_t)(H + 2) * HD;
   a.scale = scale;
   a.scale_log2 = scale * LOG2E;
+  a.hmagic = (uint32_t)((((uint64_t)1 << 32) + H - 1) / H);
   const int nrb = (T * H + QB - 1) / QB;
   const double fl = 2.0 * B * H * (double)HD * T * T;
   probe_begin(NC_PROBE_ATTN_FWD, s);
@@ -554,6 +599,7 @@ int attn_mfma_fwd(const void* qkv, int B, int T, int H, float scale, void* o, fl
 
 int attn_mfma_bwd(const void* qkv, const void* o, const void* dout, const float* lse, int B, int T, int H, float scale,
                   float* dqkv, void* ws, hipStream_t s) {
+  NC_REQUIRE((uint64_t)T * H * H < ((uint64_t)1 << 32), NC_ERR_UNSUPPORTED, "attention: T * H^2 must be < 2^32");
   AttnMfmaArgs a{};
   a.qkv = static_cast<const bf16*>(qkv);
   a.o = static_cast<const bf16*>(o);
@@ -570,6 +616,7 @@ int attn_mfma_bwd(const void* qkv, const void* o, const void* dout, const float*
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)B * T * H * sizeof(float), 256));
   a.nkb = (T + KB - 1) / KB;
   a.smax = attn_mfma_smax(T, H);
+  a.hmagic = (uint32_t)((((uint64_t)1 << 32) + H - 1) / H);
   const int nrb = (T * H + QB - 1) / QB;
   const double fl = 2.0 * B * H * (double)HD * T * T;
   probe_begin(NC_PROBE_ATTN_DQ, s);
