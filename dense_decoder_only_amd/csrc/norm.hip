@@ -5,9 +5,9 @@
 //
 // One 64-lane wavefront per row, four rows per 256-thread block; each lane
 // moves 4 elements per access (16 bytes fp32 / 8 bytes bf16), so a row of
-// d = 1280 is read in 5 coalesced passes.  The row is read twice (sum of
-// squares, then scale); the second read hits L2.  These kernels are bound by
-// HBM bandwidth.
+// d = 1280 is read in 5 coalesced passes.  Rows up to 2048 wide stay in
+// registers between the reduction and the scaling pass; wider rows are read
+// twice.  These kernels are bound by HBM bandwidth.
 #include "common.h"
 
 namespace nc {
@@ -25,6 +25,79 @@ __device__ __forceinline__ void store4(bf16* p, float4 v) {
 }
 __device__ __forceinline__ float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
 __device__ __forceinline__ float4 scale4(float4 a, float s) { return make_float4(a.x * s, a.y * s, a.z * s, a.w * s); }
+
+// Rows of up to 64 * 4 * CV elements are held in registers between the two
+// passes (CV float4 per lane), so each element is read from HBM once.
+constexpr int CV = 8;
+
+template <typename TX, typename TY>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_reg_kernel(const TX* __restrict__ x, int64_t rows, int d,
+                                                              float eps, TY* __restrict__ y,
+                                                              float* __restrict__ rstd) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const TX* xr = x + row * d;
+  float4 v[CV];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < CV; ++k) {
+    const int c = lane * 4 + k * 256;
+    if (c < d) {
+      v[k] = load4(xr + c);
+      ss += dot4(v[k], v[k]);
+    }
+  }
+  ss = wave_sum(ss);
+  const float r = 1.f / sqrtf(ss / (float)d + eps);
+  TY* yr = y + row * d;
+#pragma unroll
+  for (int k = 0; k < CV; ++k) {
+    const int c = lane * 4 + k * 256;
+    if (c < d) store4(yr + c, scale4(v[k], r));
+  }
+  if (lane == 0 && rstd) rstd[row] = r;
+}
+
+template <typename TG, typename TY>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(const TG* __restrict__ g, const TY* __restrict__ y,
+                                                              const float* __restrict__ rstd, int64_t rows, int d,
+                                                              float* __restrict__ dx, int accumulate,
+                                                              bf16* __restrict__ dx_bf16) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const TG* gr = g + row * d;
+  const TY* yr = y + row * d;
+  float4 gv[CV], yv[CV];
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < CV; ++k) {
+    const int c = lane * 4 + k * 256;
+    if (c < d) {
+      gv[k] = load4(gr + c);
+      yv[k] = load4(yr + c);
+      s += dot4(gv[k], yv[k]);
+    }
+  }
+  const float mean = wave_sum(s) / (float)d;
+  const float r = rstd[row];
+  float* dr = dx + row * d;
+#pragma unroll
+  for (int k = 0; k < CV; ++k) {
+    const int c = lane * 4 + k * 256;
+    if (c < d) {
+      float4 o = make_float4(r * (gv[k].x - yv[k].x * mean), r * (gv[k].y - yv[k].y * mean),
+                             r * (gv[k].z - yv[k].z * mean), r * (gv[k].w - yv[k].w * mean));
+      if (accumulate) {
+        const float4 p = load4(dr + c);
+        o = make_float4(o.x + p.x, o.y + p.y, o.z + p.z, o.w + p.w);
+      }
+      store4(dr + c, o);
+      if (dx_bf16) store4(dx_bf16 + row * d + c, o);
+    }
+  }
+}
 
 template <typename TX, typename TY>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const TX* __restrict__ x, int64_t rows, int d,
@@ -117,6 +190,11 @@ template <typename TG, typename TY>
 int launch_bwd(const void* g, const void* y, const float* rstd, int64_t rows, int d, float* dx, int acc,
                bf16* dxb, hipStream_t s) {
   const unsigned blocks = (unsigned)cdiv(rows, 4);
+  if (d <= 256 * CV) {
+    rmsnorm_bwd_reg_kernel<TG, TY><<<blocks, 256, 0, s>>>(static_cast<const TG*>(g), static_cast<const TY*>(y), rstd,
+                                                           rows, d, dx, acc, dxb);
+    return check_launch("rmsnorm_bwd_reg_kernel");
+  }
   rmsnorm_bwd_kernel<TG, TY><<<blocks, 256, 0, s>>>(static_cast<const TG*>(g), static_cast<const TY*>(y), rstd,
                                                      rows, d, dx, acc, dxb);
   return check_launch("rmsnorm_bwd_kernel");
@@ -125,6 +203,11 @@ int launch_bwd(const void* g, const void* y, const float* rstd, int64_t rows, in
 template <typename TX, typename TY>
 int launch_fwd(const void* x, int64_t rows, int d, float eps, void* y, float* rstd, hipStream_t s) {
   const unsigned blocks = (unsigned)cdiv(rows, 4);
+  if (d <= 256 * CV) {
+    rmsnorm_fwd_reg_kernel<TX, TY><<<blocks, 256, 0, s>>>(static_cast<const TX*>(x), rows, d, eps,
+                                                           static_cast<TY*>(y), rstd);
+    return check_launch("rmsnorm_fwd_reg_kernel");
+  }
   rmsnorm_fwd_kernel<TX, TY><<<blocks, 256, 0, s>>>(static_cast<const TX*>(x), rows, d, eps, static_cast<TY*>(y),
                                                      rstd);
   return check_launch("rmsnorm_fwd_kernel");
