@@ -21,6 +21,22 @@ struct GemmDesc {
   int dtype = NC_BF16;
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  // Softcap cross-entropy epilogues on the logit product z = h U^T (bf16,
+  // K-contiguous operands, K a multiple of 64).  Columns are vocabulary ids
+  // xv0 + n.
+  //   xent = 1: C is not written; per row and 64-column group g (vocabulary
+  //             columns 64 g .. 64 g + 63) xpart[g * M + row] = sum of
+  //             exp(z' - c), z' = c tanh(z / c); xztgt[row] = z' at the
+  //             row's target when the target is one of these columns.
+  //   xent = 2: C (bf16) = xdl (exp(z' - xlse[row]) - [col == target])
+  //             (1 - (z'/c)^2).
+  int xent = 0;
+  float xc = 0.f, xdl = 0.f;
+  const int32_t* xtgt = nullptr;
+  const float* xlse = nullptr;
+  float* xpart = nullptr;
+  float* xztgt = nullptr;
+  int xv0 = 0;
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);

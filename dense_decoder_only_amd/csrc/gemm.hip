@@ -43,7 +43,8 @@ constexpr int NT = 256;
 // at chunk c ^ swz(row).
 __host__ __device__ constexpr int swz(int row) { return NC_GEMM_SWZ ? ((row >> 1) & 7) : (row & 7); }
 
-enum { E_STORE_F32 = 0, E_ACC_F32 = 1, E_STORE_BF16 = 2, E_RELU2 = 3, E_RELU2_BWD = 4, E_PARTIAL = 5 };
+enum { E_STORE_F32 = 0, E_ACC_F32 = 1, E_STORE_BF16 = 2, E_RELU2 = 3, E_RELU2_BWD = 4, E_PARTIAL = 5,
+       E_XENT_FWD = 6, E_XENT_BWD = 7 };
 
 struct MfmaParams {
   const bf16* A;
@@ -56,7 +57,64 @@ struct MfmaParams {
   int64_t ldc;
   const bf16* aux;
   bf16* aux_out;
+  // softcap cross-entropy epilogues (see GemmDesc)
+  float xc, xinv_c, xdl;
+  const int32_t* xtgt;
+  const float* xlse;
+  float* xpart;
+  float* xztgt;
+  int xv0;
 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// c tanh(z / c) from one hardware exp2 and reciprocal:
+// tanh|x| = (1 - e^{-2|x|}) / (1 + e^{-2|x|}).
+__device__ __forceinline__ float softcap_of(float z, float c, float inv_c) {
+  const float x = z * inv_c;
+  const float t = __builtin_amdgcn_exp2f(-2.f * kLog2e * fabsf(x));
+  return copysignf(c * (1.f - t) * __builtin_amdgcn_rcpf(1.f + t), x);
+}
+
+// Logit-gradient epilogue on four consecutive columns of one row.
+__device__ __forceinline__ void xent_bwd4(const MfmaParams& p, float4 v, int row, int col) {
+  const float L = p.xlse[row] * kLog2e;
+  const int y = p.xtgt[row] - p.xv0;
+  const float zz[4] = {v.x, v.y, v.z, v.w};
+  float g[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float zc = softcap_of(zz[e], p.xc, p.xinv_c);
+    const float th = zc * p.xinv_c;
+    const float pr = __builtin_amdgcn_exp2f(zc * kLog2e - L);
+    g[e] = p.xdl * (pr - (col + e == y ? 1.f : 0.f)) * (1.f - th * th);
+  }
+  *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + (int64_t)row * p.ldc + col) =
+      make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
+}
+
+// Forward cross-entropy epilogue: a 16-lane group holds one row's 64 columns
+// (4 per lane); every lane of the group must call this (it shuffles).
+__device__ __forceinline__ void xent_fwd4(const MfmaParams& p, float4 v, int row, int col, int gcol64) {
+  const bool ok = row < p.M;
+  const int y = ok ? p.xtgt[row] - p.xv0 : -1;
+  const float zz[4] = {v.x, v.y, v.z, v.w};
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (col + e < p.N) {
+      const float zc = softcap_of(zz[e], p.xc, p.xinv_c);
+      s += __builtin_amdgcn_exp2f((zc - p.xc) * kLog2e);
+      if (ok && col + e == y) p.xztgt[row] = zc;
+    }
+  }
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  s += __shfl_xor(s, 4, 64);
+  s += __shfl_xor(s, 8, 64);
+  if (ok && (threadIdx.x & 15) == 0 && gcol64 < p.N)
+    p.xpart[(int64_t)((p.xv0 + gcol64) >> 6) * p.M + row] = s;
+}
 
 // Global -> registers: one 256 x 64 tile of an operand.
 template <bool KC>
@@ -177,6 +235,8 @@ __device__ __forceinline__ void epilogue4(const MfmaParams& p, float4 v, int row
     *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + off) =
         make_uint2(pack_bf16x2(v.x * 2.f * fmaxf(u0, 0.f), v.y * 2.f * fmaxf(u1, 0.f)),
                    pack_bf16x2(v.z * 2.f * fmaxf(u2, 0.f), v.w * 2.f * fmaxf(u3, 0.f)));
+  } else if constexpr (EPI == E_XENT_BWD) {
+    xent_bwd4(p, v, row, col);
   } else {  // E_PARTIAL: [split][M][N] fp32
     *reinterpret_cast<float4*>(static_cast<float*>(p.C) + (int64_t)blockIdx.z * p.M * p.N +
                                (int64_t)row * p.N + col) = v;
@@ -822,7 +882,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int row = idx >> 4, c4 = (idx & 15) * 4;
       const float4 v = *reinterpret_cast<const float4*>(stage + row * SROW + c4);
       const int grow = m0 + wm * 128 + i * 32 + row, gcol = n0 + wn * 64 + c4;
-      if (grow < p.M && gcol < p.N) epilogue4<EPI>(p, v, grow, gcol);
+      if constexpr (EPI == E_XENT_FWD) xent_fwd4(p, v, grow, gcol, n0 + wn * 64);
+      else if (grow < p.M && gcol < p.N) epilogue4<EPI>(p, v, grow, gcol);
     }
     __syncthreads();
   }
@@ -837,6 +898,8 @@ hipError_t launch_pipe(int epi, const MfmaParams& p, int splits, hipStream_t s) 
     case E_STORE_BF16: gemm_pipe_kernel<E_STORE_BF16, TN><<<grid, 512, 0, s>>>(p); break;
     case E_RELU2: gemm_pipe_kernel<E_RELU2, TN><<<grid, 512, 0, s>>>(p); break;
     case E_RELU2_BWD: gemm_pipe_kernel<E_RELU2_BWD, TN><<<grid, 512, 0, s>>>(p); break;
+    case E_XENT_FWD: gemm_pipe_kernel<E_XENT_FWD, false><<<grid, 512, 0, s>>>(p); break;
+    case E_XENT_BWD: gemm_pipe_kernel<E_XENT_BWD, false><<<grid, 512, 0, s>>>(p); break;
     default: gemm_pipe_kernel<E_PARTIAL, TN><<<grid, 512, 0, s>>>(p); break;
   }
   return hipGetLastError();
@@ -903,7 +966,52 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return (size_t)s * (size_t)M * (size_t)N * sizeof(float);
 }
 
+// Logit product with a softcap cross-entropy epilogue (internal; the
+// pipelined kernel's K-contiguous form only).
+int gemm_xent(const GemmDesc& g, hipStream_t stream) {
+  NC_REQUIRE(g.xent == 1 || g.xent == 2, NC_ERR_INVALID_ARG, "gemm: bad cross-entropy mode");
+  NC_REQUIRE(g.A && g.B && g.xtgt, NC_ERR_INVALID_ARG, "gemm: null operand");
+  NC_REQUIRE(g.dtype == NC_BF16 && g.transA == 0 && g.transB == 1, NC_ERR_UNSUPPORTED,
+             "gemm: the cross-entropy epilogues need bf16 K-contiguous operands");
+  NC_REQUIRE(g.M > 0 && g.N > 0 && g.K > 0 && g.M < (1ll << 31) && g.N < (1ll << 31), NC_ERR_INVALID_ARG,
+             "gemm: bad shape");
+  NC_REQUIRE(g.K % BK == 0 && g.N % 8 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.lda >= g.K && g.ldb >= g.K,
+             NC_ERR_UNSUPPORTED, "gemm: the cross-entropy epilogues need K a multiple of 64");
+  NC_REQUIRE(aligned16(g.A) && aligned16(g.B), NC_ERR_INVALID_ARG, "gemm: A and B must be 16-byte aligned");
+  NC_REQUIRE(g.xv0 % 64 == 0, NC_ERR_INVALID_ARG, "gemm: vocabulary offset must be a multiple of 64");
+  if (g.xent == 1) NC_REQUIRE(g.xpart && g.xztgt, NC_ERR_INVALID_ARG, "gemm: null cross-entropy output");
+  else NC_REQUIRE(g.C && g.xlse && g.cdt == NC_BF16 && g.ldc >= g.N, NC_ERR_INVALID_ARG, "gemm: bad dz output");
+  MfmaParams p{};
+  p.A = static_cast<const bf16*>(g.A);
+  p.B = static_cast<const bf16*>(g.B);
+  p.lda = g.lda;
+  p.ldb = g.ldb;
+  p.M = (int)g.M;
+  p.N = (int)g.N;
+  p.K = (int)g.K;
+  p.k_per_split = (int)g.K;
+  p.tiles_m = (int)cdiv(g.M, BM);
+  p.tiles_n = (int)cdiv(g.N, BN);
+  p.C = g.C;
+  p.ldc = g.ldc;
+  p.xc = g.xc;
+  p.xinv_c = 1.f / g.xc;
+  p.xdl = g.xdl;
+  p.xtgt = g.xtgt;
+  p.xlse = g.xlse;
+  p.xpart = g.xpart;
+  p.xztgt = g.xztgt;
+  p.xv0 = g.xv0;
+  const double flops = 2.0 * p.M * p.N * p.K;
+  probe_begin(NC_PROBE_GEMM_NT, stream);
+  const hipError_t e = launch_pipe<false>(g.xent == 1 ? E_XENT_FWD : E_XENT_BWD, p, 1, stream);
+  probe_end(NC_PROBE_GEMM_NT, stream, flops);
+  if (e != hipSuccess) return set_error(NC_ERR_HIP, "gemm launch failed: %s", hipGetErrorString(e));
+  return NC_OK;
+}
+
 int gemm(const GemmDesc& g, hipStream_t stream) {
+  if (g.xent) return gemm_xent(g, stream);
   NC_REQUIRE(g.A && g.B && g.C, NC_ERR_INVALID_ARG, "gemm: null operand");
   NC_REQUIRE(g.M > 0 && g.N > 0 && g.K > 0, NC_ERR_INVALID_ARG, "gemm: M, N, K must be positive");
   NC_REQUIRE(g.M < (1ll << 31) && g.N < (1ll << 31) && g.K < (1ll << 31), NC_ERR_UNSUPPORTED,

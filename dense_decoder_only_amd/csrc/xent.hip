@@ -8,15 +8,21 @@
 //   loss_t = lse_t - z'_{t, y_t}, loss = mean_t loss_t,
 //   bpb = sum_t loss_t / (ln 2 * sum_t bytes[y_t]).
 //
-// The vocabulary is processed in chunks of Vc columns: a matrix-core GEMM
-// writes one [M, Vc] fp32 logit chunk, a row kernel folds it into per-row
-// partial sums (the full [M, V] fp32 logits are never stored).  Because
-// |z'| < c, exp(z' - c) never overflows, so the softmax needs no running
-// maximum: lse = c + log sum exp(z' - c).  Partial sums are added in chunk
-// order and the loss sums in a fixed tree order, so results are bitwise
-// reproducible.  The backward recomputes each logit chunk, forms
-// dz = dloss (softmax(z') - onehot(y)) (1 - (z'/c)^2) in the GEMM operand
-// dtype, and feeds it to dh += dz U_c and dU_c += dz^T h.
+// Because |z'| < c, exp(z' - c) never overflows, so the softmax needs no
+// running maximum: lse = c + log sum exp(z' - c).  The fp32 logits are never
+// stored.
+//
+// bf16 (d a multiple of 64): the logit GEMM's epilogue applies the softcap
+// and folds each row's 64-column groups into partial sums of exp(z' - c)
+// (and picks z' at the target), so the forward writes only [V/64, M]
+// partials.  The backward recomputes the logits with an epilogue that writes
+// dz = dloss (softmax(z') - onehot(y)) (1 - (z'/c)^2) in bf16 directly, then
+// dh (+)= dz U and dU (+)= dz^T h.  The vocabulary is one chunk unless the
+// bf16 dz would exceed 8 GiB.
+// fp32 (and other shapes): a GEMM writes one [M, Vc] fp32 logit chunk and a
+// row kernel folds it (forward) or forms dz from it (backward).
+// Partial sums are added in a fixed order and the loss sums in a fixed tree
+// order, so results are bitwise reproducible.
 #include "common.h"
 #include "gemm.h"
 #include "ops.h"
@@ -34,10 +40,21 @@ int chunk_cols(int64_t M, int V) {
   return (int)c;
 }
 
+// Fused path: bf16 dz chunk of at most 8 GiB.
+int fused_cols(int64_t M, int V) {
+  int64_t c = ((int64_t)1 << 32) / std::max<int64_t>(M, 1);
+  c = c / 256 * 256;
+  if (c < 256) c = 256;
+  if (c > V) c = V;
+  return (int)c;
+}
+
+bool use_fused(int dtype, int d) { return dtype == NC_BF16 && d % 64 == 0; }
+
 struct XentWs {
-  float* zbuf;     // [M, Vc] fp32 logit chunk
+  float* zbuf;     // [M, Vc] fp32 logit chunk (chunked path)
   void* dz;        // [M, Vc] dtype (backward)
-  float* partial;  // [nchunks, M]
+  float* partial;  // [nparts, M]
   float* ztgt;     // [M]
   float* ltok;     // [M]
   void* gemm_ws;
@@ -45,18 +62,18 @@ struct XentWs {
   void* ut;        // U^T [d, V] (bf16 backward)
 };
 
-size_t carve(int64_t M, int d, int V, XentWs* w, void* base) {
-  const int Vc = chunk_cols(M, V);
-  const int nch = (int)cdiv(V, Vc);
+size_t carve(int64_t M, int d, int V, bool fused, XentWs* w, void* base) {
+  const int Vc = fused ? fused_cols(M, V) : chunk_cols(M, V);
+  const int nparts = fused ? (int)cdiv(V, 64) : (int)cdiv(V, Vc);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
     off += align_up(bytes, 256);
     return o;
   };
-  const size_t o_z = take((size_t)M * Vc * 4);
-  const size_t o_dz = take((size_t)M * Vc * 4);
-  const size_t o_p = take((size_t)nch * M * 4);
+  const size_t o_z = take(fused ? 0 : (size_t)M * Vc * 4);
+  const size_t o_dz = take((size_t)M * Vc * (fused ? 2 : 4));
+  const size_t o_p = take((size_t)nparts * M * 4);
   const size_t o_t = take((size_t)M * 4);
   const size_t o_l = take((size_t)M * 4);
   const size_t gwb = gemm_workspace_bytes(Vc, d, M);
@@ -175,7 +192,9 @@ int validate(const void* h, const void* U, int dtype, const int32_t* tgt, int64_
 
 }  // namespace
 
-size_t xent_workspace_bytes(int64_t M, int d, int V) { return carve(M, d, V, nullptr, nullptr); }
+size_t xent_workspace_bytes(int64_t M, int d, int V) {
+  return std::max(carve(M, d, V, false, nullptr, nullptr), carve(M, d, V, true, nullptr, nullptr));
+}
 
 int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* token_bytes, int64_t M, int d,
              int V, float softcap, float* lse, float* loss_tok, float* loss, float* bpb, void* ws, size_t ws_bytes,
@@ -185,9 +204,10 @@ int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
   NC_REQUIRE(softcap > 0.f, NC_ERR_INVALID_ARG, "softcap_xent_fwd: softcap must be positive");
   NC_REQUIRE(ws && ws_bytes >= xent_workspace_bytes(M, d, V), NC_ERR_WORKSPACE,
              "softcap_xent_fwd: workspace too small");
+  const bool fused = use_fused(dtype, d);
   XentWs w;
-  carve(M, d, V, &w, ws);
-  const int Vc = chunk_cols(M, V);
+  carve(M, d, V, fused, &w, ws);
+  const int Vc = fused ? fused_cols(M, V) : chunk_cols(M, V);
   const int nch = (int)cdiv(V, Vc);
   const size_t esz = dtype == NC_BF16 ? 2 : 4;
   for (int k = 0; k < nch; ++k) {
@@ -203,16 +223,27 @@ int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
     g.lda = d;
     g.B = static_cast<const char*>(U) + (size_t)v0 * d * esz;
     g.ldb = d;
+    g.dtype = dtype;
+    if (fused) {
+      g.xent = 1;
+      g.xc = softcap;
+      g.xtgt = tgt;
+      g.xpart = w.partial;
+      g.xztgt = w.ztgt;
+      g.xv0 = v0;
+      NC_TRY(gemm(g, s));
+      continue;
+    }
     g.C = w.zbuf;
     g.cdt = NC_F32;
     g.ldc = n;
-    g.dtype = dtype;
     NC_TRY(gemm(g, s));
     xent_fwd_rows_kernel<<<(unsigned)cdiv(M, 4), 256, 0, s>>>(w.zbuf, M, n, v0, softcap, tgt,
                                                               w.partial + (int64_t)k * M, w.ztgt);
     NC_TRY(check_launch("xent_fwd_rows_kernel"));
   }
-  xent_finish_kernel<<<(unsigned)std::min<int64_t>(cdiv(M, 256), 4096), 256, 0, s>>>(w.partial, nch, M, softcap,
+  const int nparts = fused ? (int)cdiv(V, 64) : nch;
+  xent_finish_kernel<<<(unsigned)std::min<int64_t>(cdiv(M, 256), 4096), 256, 0, s>>>(w.partial, nparts, M, softcap,
                                                                                        w.ztgt, lse, w.ltok, loss_tok);
   NC_TRY(check_launch("xent_finish_kernel"));
   xent_reduce_kernel<<<1, 1024, 0, s>>>(w.ltok, M, tgt, token_bytes, 4.8f, loss, bpb);
@@ -227,9 +258,10 @@ int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
   NC_REQUIRE(softcap > 0.f, NC_ERR_INVALID_ARG, "softcap_xent_bwd: softcap must be positive");
   NC_REQUIRE(ws && ws_bytes >= xent_workspace_bytes(M, d, V), NC_ERR_WORKSPACE,
              "softcap_xent_bwd: workspace too small");
+  const bool fused = use_fused(dtype, d);
   XentWs w;
-  carve(M, d, V, &w, ws);
-  const int Vc = chunk_cols(M, V);
+  carve(M, d, V, fused, &w, ws);
+  const int Vc = fused ? fused_cols(M, V) : chunk_cols(M, V);
   const int nch = (int)cdiv(V, Vc);
   const size_t esz = dtype == NC_BF16 ? 2 : 4;
   if (dtype == NC_BF16) NC_TRY(transpose(U, V, d, 2, w.ut, s));
@@ -247,18 +279,31 @@ int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
     g.lda = d;
     g.B = Uc;
     g.ldb = d;
-    g.C = w.zbuf;
-    g.cdt = NC_F32;
-    g.ldc = n;
     g.dtype = dtype;
-    NC_TRY(gemm(g, s));
-    if (dtype == NC_BF16)
-      xent_bwd_rows_kernel<bf16><<<(unsigned)cdiv(M, 4), 256, 0, s>>>(w.zbuf, M, n, v0, softcap, tgt, lse, dloss,
-                                                                       static_cast<bf16*>(w.dz));
-    else
-      xent_bwd_rows_kernel<float><<<(unsigned)cdiv(M, 4), 256, 0, s>>>(w.zbuf, M, n, v0, softcap, tgt, lse, dloss,
-                                                                        static_cast<float*>(w.dz));
-    NC_TRY(check_launch("xent_bwd_rows_kernel"));
+    if (fused) {
+      g.xent = 2;
+      g.xc = softcap;
+      g.xdl = dloss;
+      g.xtgt = tgt;
+      g.xlse = lse;
+      g.xv0 = v0;
+      g.C = w.dz;
+      g.cdt = NC_BF16;
+      g.ldc = n;
+      NC_TRY(gemm(g, s));
+    } else {
+      g.C = w.zbuf;
+      g.cdt = NC_F32;
+      g.ldc = n;
+      NC_TRY(gemm(g, s));
+      if (dtype == NC_BF16)
+        xent_bwd_rows_kernel<bf16><<<(unsigned)cdiv(M, 4), 256, 0, s>>>(w.zbuf, M, n, v0, softcap, tgt, lse, dloss,
+                                                                         static_cast<bf16*>(w.dz));
+      else
+        xent_bwd_rows_kernel<float><<<(unsigned)cdiv(M, 4), 256, 0, s>>>(w.zbuf, M, n, v0, softcap, tgt, lse, dloss,
+                                                                          static_cast<float*>(w.dz));
+      NC_TRY(check_launch("xent_bwd_rows_kernel"));
+    }
     // dh (+)= dz U_c  : [M, n] x [n, d]; in bf16 through U^T (K-contiguous)
     GemmDesc gh;
     gh.transA = 0;

@@ -353,8 +353,11 @@ def test_relu2_mlp_fwd_bwd(dtype):
 
 # ------------------------------------------------- softcap cross entropy --
 
+# bf16 with d a multiple of 64 takes the fused epilogue path; d = 200 the
+# chunked fp32-logit path.
 @pytest.mark.parametrize("dtype,M,d,V,ustd", [(F32, 512, 256, 8192, 1.0), (BF16, 512, 256, 8192, 1.0),
-                                              (BF16, 8192, 128, 40960, 1.0), (BF16, 264, 128, 1024, 20.0)])
+                                              (BF16, 8192, 128, 40960, 1.0), (BF16, 264, 128, 1024, 20.0),
+                                              (BF16, 512, 200, 4096, 1.0)])
 def test_softcap_xent_fwd_bwd(dtype, M, d, V, ustd):
     n = nc()
     r = rng(M + V)
@@ -391,3 +394,47 @@ def test_softcap_xent_fwd_bwd(dtype, M, d, V, ustd):
     for name, got, ref in (("dh", dev_to_f64(dh), dz @ U64), ("dU", dev_to_f64(dU), dz.T @ h64)):
         assert max_rel(got, ref) < tol, (name, max_rel(got, ref))
         assert cosine(got, ref) > 0.9999, (name, cosine(got, ref))
+
+
+def test_softcap_xent_two_vocab_chunks():
+    """bf16 fused path with the vocabulary split in two chunks (M V > 2^32:
+    the second chunk starts at vocabulary id 65536); checked on sampled rows
+    and vocabulary columns against the oracle in fp64."""
+    n = nc()
+    M, d, V, c = 65536, 64, 65536 + 256, 15.0
+    r = rng(77)
+    h_np = _unit_rms(r.standard_normal((M, d)))
+    U_np = r.standard_normal((V, d)) / math.sqrt(d)
+    h, U = to_dev(h_np, BF16), to_dev(U_np, BF16)
+    y_np = zipf_ids(r, V, M)
+    y_np[:64] = V - 1 - np.arange(64)  # targets in the second chunk
+    y = torch.from_numpy(y_np).to(DEV)
+    ws = torch.empty(n.nc_softcap_xent_workspace_bytes(M, d, V), dtype=torch.uint8, device=DEV)
+    lse = torch.empty(M, dtype=F32, device=DEV)
+    ltok = torch.empty(M, dtype=F32, device=DEV)
+    loss = torch.empty(1, dtype=F32, device=DEV)
+    bpb = torch.empty(1, dtype=F32, device=DEV)
+    n.nc_softcap_xent_fwd(h, U, y, None, c, lse, ltok, loss, bpb, ws)
+    dh = torch.empty(M, d, dtype=F32, device=DEV)
+    dU = torch.empty(V, d, dtype=F32, device=DEV)
+    n.nc_softcap_xent_bwd(h, U, y, lse, c, 1.0 / M, dh, 0, dU, 0, ws)
+    sync()
+    h64, U64 = dev_to_f64(h), dev_to_f64(U)
+    rows = np.concatenate([np.arange(8), r.choice(M, 24, replace=False)])
+    zc_rows = oracle.softcap(h64[rows] @ U64.T, c)
+    lt_ref, lse_ref = oracle.cross_entropy(zc_rows, y_np[rows])
+    assert_close(dev_to_f64(lse)[rows], lse_ref, 2e-6, 0, "xent lse (sampled rows)")
+    assert_close(dev_to_f64(ltok)[rows], lt_ref, 1e-5, 1e-5, "xent loss_tok (sampled rows)")
+    dz_rows = oracle.softcap_xent_bwd(zc_rows, lse_ref, y_np[rows], c, 1.0 / M)
+    got = dev_to_f64(dh)[rows]
+    ref = dz_rows @ U64
+    assert max_rel(got, ref) < 1e-2 and cosine(got, ref) > 0.9999, ("dh", max_rel(got, ref))
+    # dU over both chunks: dh = dz U and dU = dz^T h share one dz, so
+    # sum_v U[v] . dU[v] = sum_t h[t] . dh[t] for any dz (dh itself is pinned
+    # on the sampled rows above, targets in the second chunk included).
+    dU64, dh64 = dev_to_f64(dU), dev_to_f64(dh)
+    lhs = float(np.sum(U64 * dU64))
+    rhs = float(np.sum(h64 * dh64))
+    assert abs(lhs - rhs) <= 1e-4 * max(abs(rhs), 1e-30), (lhs, rhs)
+    per_chunk = [float(np.sum(U64[a:b] * dU64[a:b])) for a, b in ((0, 65536), (65536, V))]
+    assert all(np.isfinite(per_chunk)) and abs(per_chunk[1]) > 0.0
