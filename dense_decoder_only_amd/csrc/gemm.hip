@@ -44,7 +44,7 @@ constexpr int NT = 256;
 __host__ __device__ constexpr int swz(int row) { return NC_GEMM_SWZ ? ((row >> 1) & 7) : (row & 7); }
 
 enum { E_STORE_F32 = 0, E_ACC_F32 = 1, E_STORE_BF16 = 2, E_RELU2 = 3, E_RELU2_BWD = 4, E_PARTIAL = 5,
-       E_XENT_FWD = 6, E_XENT_BWD = 7 };
+       E_XENT_FWD = 6, E_XENT_BWD = 7, E_RELU2_SQ = 8, E_RELU2_BWD_SQ = 9 };
 
 struct MfmaParams {
   const bf16* A;
@@ -235,6 +235,19 @@ __device__ __forceinline__ void epilogue4(const MfmaParams& p, float4 v, int row
     *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + off) =
         make_uint2(pack_bf16x2(v.x * 2.f * fmaxf(u0, 0.f), v.y * 2.f * fmaxf(u1, 0.f)),
                    pack_bf16x2(v.z * 2.f * fmaxf(u2, 0.f), v.w * 2.f * fmaxf(u3, 0.f)));
+  } else if constexpr (EPI == E_RELU2_SQ) {
+    const float a = fmaxf(v.x, 0.f), b = fmaxf(v.y, 0.f), c = fmaxf(v.z, 0.f), d = fmaxf(v.w, 0.f);
+    *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + off) =
+        make_uint2(pack_bf16x2(a * a, b * b), pack_bf16x2(c * c, d * d));
+  } else if constexpr (EPI == E_RELU2_BWD_SQ) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p.aux + off);
+    // hardware square root (about 1 ulp): relu(u) from the stored relu(u)^2
+    const float r0 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.x & 0xffffu)));
+    const float r1 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.x >> 16)));
+    const float r2 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.y & 0xffffu)));
+    const float r3 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.y >> 16)));
+    *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + off) =
+        make_uint2(pack_bf16x2(v.x * 2.f * r0, v.y * 2.f * r1), pack_bf16x2(v.z * 2.f * r2, v.w * 2.f * r3));
   } else if constexpr (EPI == E_XENT_BWD) {
     xent_bwd4(p, v, row, col);
   } else {  // E_PARTIAL: [split][M][N] fp32
@@ -643,6 +656,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
         aux_out[off] = rl * rl;
       } else if constexpr (EPI == E_RELU2_BWD) {
         C[off] = v * 2.f * fmaxf(aux[off], 0.f);
+      } else if constexpr (EPI == E_RELU2_SQ) {
+        const float rl = fmaxf(v, 0.f);
+        C[off] = rl * rl;
+      } else if constexpr (EPI == E_RELU2_BWD_SQ) {
+        C[off] = v * 2.f * sqrtf(aux[off]);
       }
     }
   }
@@ -658,6 +676,8 @@ hipError_t launch_mfma(int epi, const MfmaParams& p, int splits, hipStream_t s) 
     case E_STORE_BF16: gemm_mfma_kernel<AK, BKC, E_STORE_BF16, DIRECT><<<grid, block, 0, s>>>(p); break;
     case E_RELU2: gemm_mfma_kernel<AK, BKC, E_RELU2, DIRECT><<<grid, block, 0, s>>>(p); break;
     case E_RELU2_BWD: gemm_mfma_kernel<AK, BKC, E_RELU2_BWD, DIRECT><<<grid, block, 0, s>>>(p); break;
+    case E_RELU2_SQ: gemm_mfma_kernel<AK, BKC, E_RELU2_SQ, DIRECT><<<grid, block, 0, s>>>(p); break;
+    case E_RELU2_BWD_SQ: gemm_mfma_kernel<AK, BKC, E_RELU2_BWD_SQ, DIRECT><<<grid, block, 0, s>>>(p); break;
     default: gemm_mfma_kernel<AK, BKC, E_PARTIAL, DIRECT><<<grid, block, 0, s>>>(p); break;
   }
   return hipGetLastError();
@@ -898,6 +918,8 @@ hipError_t launch_pipe(int epi, const MfmaParams& p, int splits, hipStream_t s) 
     case E_STORE_BF16: gemm_pipe_kernel<E_STORE_BF16, TN><<<grid, 512, 0, s>>>(p); break;
     case E_RELU2: gemm_pipe_kernel<E_RELU2, TN><<<grid, 512, 0, s>>>(p); break;
     case E_RELU2_BWD: gemm_pipe_kernel<E_RELU2_BWD, TN><<<grid, 512, 0, s>>>(p); break;
+    case E_RELU2_SQ: gemm_pipe_kernel<E_RELU2_SQ, TN><<<grid, 512, 0, s>>>(p); break;
+    case E_RELU2_BWD_SQ: gemm_pipe_kernel<E_RELU2_BWD_SQ, TN><<<grid, 512, 0, s>>>(p); break;
     case E_XENT_FWD: gemm_pipe_kernel<E_XENT_FWD, false><<<grid, 512, 0, s>>>(p); break;
     case E_XENT_BWD: gemm_pipe_kernel<E_XENT_BWD, false><<<grid, 512, 0, s>>>(p); break;
     default: gemm_pipe_kernel<E_PARTIAL, TN><<<grid, 512, 0, s>>>(p); break;
@@ -915,6 +937,8 @@ hipError_t launch_mfma8(int epi, const MfmaParams& p, int splits, hipStream_t s)
     case E_STORE_BF16: gemm_mfma8_kernel<E_STORE_BF16, TN><<<grid, block, 0, s>>>(p); break;
     case E_RELU2: gemm_mfma8_kernel<E_RELU2, TN><<<grid, block, 0, s>>>(p); break;
     case E_RELU2_BWD: gemm_mfma8_kernel<E_RELU2_BWD, TN><<<grid, block, 0, s>>>(p); break;
+    case E_RELU2_SQ: gemm_mfma8_kernel<E_RELU2_SQ, TN><<<grid, block, 0, s>>>(p); break;
+    case E_RELU2_BWD_SQ: gemm_mfma8_kernel<E_RELU2_BWD_SQ, TN><<<grid, block, 0, s>>>(p); break;
     default: gemm_mfma8_kernel<E_PARTIAL, TN><<<grid, block, 0, s>>>(p); break;
   }
   return hipGetLastError();
@@ -1019,7 +1043,7 @@ int gemm(const GemmDesc& g, hipStream_t stream) {
   NC_REQUIRE(g.transA == 0 || g.transA == 1, NC_ERR_INVALID_ARG, "gemm: transA must be 0 or 1");
   NC_REQUIRE(g.transB == 0 || g.transB == 1, NC_ERR_INVALID_ARG, "gemm: transB must be 0 or 1");
   NC_REQUIRE(g.dtype == NC_F32 || g.dtype == NC_BF16, NC_ERR_INVALID_ARG, "gemm: bad dtype");
-  NC_REQUIRE(g.epi >= NC_EPI_STORE && g.epi <= NC_EPI_RELU2_BWD, NC_ERR_INVALID_ARG, "gemm: bad epilogue");
+  NC_REQUIRE(g.epi >= NC_EPI_STORE && g.epi <= NC_EPI_RELU2_BWD_SQ, NC_ERR_INVALID_ARG, "gemm: bad epilogue");
   NC_REQUIRE(g.beta == 0.f || g.beta == 1.f, NC_ERR_INVALID_ARG, "gemm: beta must be 0 or 1");
   const int64_t a_rows = g.transA ? g.K : g.M, a_cols = g.transA ? g.M : g.K;
   const int64_t b_rows = g.transB ? g.N : g.K, b_cols = g.transB ? g.K : g.N;
@@ -1027,7 +1051,8 @@ int gemm(const GemmDesc& g, hipStream_t stream) {
   NC_REQUIRE(g.lda >= a_cols && g.ldb >= b_cols && g.ldc >= g.N, NC_ERR_INVALID_ARG,
              "gemm: leading dimension too small");
   if (g.epi == NC_EPI_RELU2) NC_REQUIRE(g.aux_out, NC_ERR_INVALID_ARG, "gemm: relu2 needs aux_out");
-  if (g.epi == NC_EPI_RELU2_BWD) NC_REQUIRE(g.aux, NC_ERR_INVALID_ARG, "gemm: relu2_bwd needs aux");
+  if (g.epi == NC_EPI_RELU2_BWD || g.epi == NC_EPI_RELU2_BWD_SQ)
+    NC_REQUIRE(g.aux, NC_ERR_INVALID_ARG, "gemm: relu2_bwd needs aux");
   if (g.beta == 1.f)
     NC_REQUIRE(g.cdt == NC_F32 && g.epi == NC_EPI_STORE, NC_ERR_INVALID_ARG,
                "gemm: beta = 1 needs an fp32 C and the plain store epilogue");
@@ -1047,6 +1072,11 @@ int gemm(const GemmDesc& g, hipStream_t stream) {
       gemm_f32_kernel<E_RELU2><<<grid, 256, 0, stream>>>(A, sam, sak, B, sbk, sbn, M, N, K, C, g.ldc, aux, aux_out);
     else if (g.epi == NC_EPI_RELU2_BWD)
       gemm_f32_kernel<E_RELU2_BWD><<<grid, 256, 0, stream>>>(A, sam, sak, B, sbk, sbn, M, N, K, C, g.ldc, aux, aux_out);
+    else if (g.epi == NC_EPI_RELU2_SQ)
+      gemm_f32_kernel<E_RELU2_SQ><<<grid, 256, 0, stream>>>(A, sam, sak, B, sbk, sbn, M, N, K, C, g.ldc, aux, aux_out);
+    else if (g.epi == NC_EPI_RELU2_BWD_SQ)
+      gemm_f32_kernel<E_RELU2_BWD_SQ><<<grid, 256, 0, stream>>>(A, sam, sak, B, sbk, sbn, M, N, K, C, g.ldc, aux,
+                                                              aux_out);
     else if (g.beta == 1.f)
       gemm_f32_kernel<E_ACC_F32><<<grid, 256, 0, stream>>>(A, sam, sak, B, sbk, sbn, M, N, K, C, g.ldc, aux, aux_out);
     else
@@ -1081,6 +1111,8 @@ int gemm(const GemmDesc& g, hipStream_t stream) {
   int epi;
   if (g.epi == NC_EPI_RELU2) epi = E_RELU2;
   else if (g.epi == NC_EPI_RELU2_BWD) epi = E_RELU2_BWD;
+  else if (g.epi == NC_EPI_RELU2_SQ) epi = E_RELU2_SQ;
+  else if (g.epi == NC_EPI_RELU2_BWD_SQ) epi = E_RELU2_BWD_SQ;
   else if (g.cdt == NC_BF16) epi = E_STORE_BF16;
   else epi = g.beta == 1.f ? E_ACC_F32 : E_STORE_F32;
 

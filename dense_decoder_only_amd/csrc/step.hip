@@ -30,7 +30,7 @@ __global__ void check_ids_kernel(const int32_t* __restrict__ ids, int64_t n, int
 }
 
 struct Layer {
-  void *a, *qkv, *o, *m, *u, *a2;
+  void *a, *qkv, *o, *m, *a2;  // a2 = relu(u)^2; u itself is not kept
   float *rstd_a, *rstd_q, *rstd_k, *lse, *rstd_m;
 };
 
@@ -122,7 +122,7 @@ size_t carve(const nc_config* c, StepWs* w, void* base) {
   for (int64_t l = 0; l < L; ++l) {
     const size_t o_a = take(M * d * e), o_ra = take(M * 4), o_qkv = take(M * Q * e), o_rq = take(M * H * 4),
                  o_rk = take(M * 4), o_o = take(M * H * hd * e), o_lse = take(M * H * 4), o_m = take(M * d * e),
-                 o_rm = take(M * 4), o_u = take(M * F * e), o_a2 = take(M * F * e);
+                 o_rm = take(M * 4), o_a2 = take(M * F * e);
     if (w) {
       Layer& ly = w->layers[l];
       ly.a = ptr(o_a);
@@ -134,7 +134,6 @@ size_t carve(const nc_config* c, StepWs* w, void* base) {
       ly.lse = static_cast<float*>(ptr(o_lse));
       ly.m = ptr(o_m);
       ly.rstd_m = static_cast<float*>(ptr(o_rm));
-      ly.u = ptr(o_u);
       ly.a2 = ptr(o_a2);
     }
   }
@@ -214,9 +213,8 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
     go.beta = 1.f;
     NC_TRY(gemm(go, s));
     NC_TRY(rmsnorm_fwd(w.x, NC_F32, M, (int)d, c->eps, ly.m, dt, ly.rstd_m, s));
-    GemmDesc gf = mk(0, 1, M, F, d, ly.m, d, wl(p->w_fc, l, F * d), d, ly.u, dt, F, dt);
-    gf.epi = NC_EPI_RELU2;
-    gf.aux_out = ly.a2;
+    GemmDesc gf = mk(0, 1, M, F, d, ly.m, d, wl(p->w_fc, l, F * d), d, ly.a2, dt, F, dt);
+    gf.epi = NC_EPI_RELU2_SQ;  // only relu(u)^2 is stored; the backward takes relu(u) = sqrt of it
     NC_TRY(gemm(gf, s));
     GemmDesc gp = mk(0, 1, M, d, F, ly.a2, F, wl(p->w_proj, l, d * F), F, w.x, NC_F32, d, dt);
     gp.beta = 1.f;
@@ -261,8 +259,8 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
     g1.ws_bytes = w.gemm_ws_bytes;
     NC_TRY(gemm(g1, s));
     GemmDesc g2 = tw ? mk(0, 1, M, F, d, gop, d, W2T, d, w.du, dt, F, dt) : mk(0, 0, M, F, d, gop, d, W2, F, w.du, dt, F, dt);
-    g2.epi = NC_EPI_RELU2_BWD;
-    g2.aux = ly.u;
+    g2.epi = NC_EPI_RELU2_BWD_SQ;
+    g2.aux = ly.a2;
     NC_TRY(gemm(g2, s));
     GemmDesc g3 = mk(1, 0, F, d, M, w.du, F, ly.m, d, gr->w_fc + (size_t)l * F * d, NC_F32, d, dt);
     g3.beta = (float)acc;

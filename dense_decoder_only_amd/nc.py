@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libnc.so")
 
 NC_OK, NC_ERR_INVALID_ARG, NC_ERR_UNSUPPORTED, NC_ERR_WORKSPACE, NC_ERR_HIP, NC_ERR_DEVICE_FLAG = range(6)
 NC_F32, NC_BF16 = 0, 1
-NC_EPI_STORE, NC_EPI_RELU2, NC_EPI_RELU2_BWD = 0, 1, 2
+NC_EPI_STORE, NC_EPI_RELU2, NC_EPI_RELU2_BWD, NC_EPI_RELU2_SQ, NC_EPI_RELU2_BWD_SQ = 0, 1, 2, 3, 4
 (NC_PROBE_OFF, NC_PROBE_GEMM_WGRAD, NC_PROBE_GEMM_NT, NC_PROBE_ATTN_FWD, NC_PROBE_ATTN_DQ,
  NC_PROBE_ATTN_DKV) = range(6)
 

@@ -257,11 +257,21 @@ int nc_mqa_attn_bwd(const void* qkv, const void* o, const void* dout, const floa
  *   NC_EPI_STORE     C (cdt) = acc, or C += acc when beta = 1 (cdt = NC_F32).
  *   NC_EPI_RELU2     C (bf16) = acc; aux_out (bf16) = relu(acc)^2 [NEWS: relu^2].
  *   NC_EPI_RELU2_BWD C (bf16) = acc * 2 relu(aux).
+ *   NC_EPI_RELU2_SQ  C (bf16) = relu(acc)^2 only (the pre-activation is not
+ *                    stored).
+ *   NC_EPI_RELU2_BWD_SQ C (bf16) = acc * 2 sqrt(aux) with aux = relu(u)^2,
+ *                    i.e. the relu^2 backward from the stored activation.
  * dtype NC_F32 runs the same contraction on fp32 operands (a plain path for
  * small fp32 problems; epilogues as above with fp32 everywhere).
  * ws (may be NULL): enables deterministic split-K for tall-K problems; see
  * nc_gemm_workspace_bytes. */
-typedef enum { NC_EPI_STORE = 0, NC_EPI_RELU2 = 1, NC_EPI_RELU2_BWD = 2 } nc_epilogue;
+typedef enum {
+  NC_EPI_STORE = 0,
+  NC_EPI_RELU2 = 1,
+  NC_EPI_RELU2_BWD = 2,
+  NC_EPI_RELU2_SQ = 3,
+  NC_EPI_RELU2_BWD_SQ = 4
+} nc_epilogue;
 size_t nc_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int nc_gemm_bf16(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A,
                  int64_t lda, const void* B, int64_t ldb, void* C, int cdt, int64_t ldc, float beta,

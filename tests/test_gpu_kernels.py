@@ -271,9 +271,10 @@ def test_gemm_layouts_and_store(dtype, ta, tb, M, N, K):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_gemm_relu2_epilogues(dtype):
+@pytest.mark.parametrize("K", [264, 1280])
+def test_gemm_relu2_epilogues(dtype, K):
     n = nc()
-    M, N, K = 520, 776, 264
+    M, N = 520, 776
     r = rng(77)
     A, Bm, ref = _gemm_operands(r, 0, 1, M, N, K, dtype)
     u = torch.empty((M, N), dtype=dtype, device=DEV)
@@ -289,6 +290,17 @@ def test_gemm_relu2_epilogues(dtype):
     n.nc_gemm_bf16(0, 1, M, N, K, A, K, Bm, K, C, N, epilogue=n.NC_EPI_RELU2_BWD, aux=aux)
     sync()
     assert_close(dev_to_f64(C), oracle.relu2_bwd(ref, dev_to_f64(aux)), tol, 1e-5, "relu2 bwd")
+    # square-only forward and its backward from the stored square
+    a2s = torch.empty((M, N), dtype=dtype, device=DEV)
+    n.nc_gemm_bf16(0, 1, M, N, K, A, K, Bm, K, a2s, N, epilogue=n.NC_EPI_RELU2_SQ)
+    sync()
+    assert_close(dev_to_f64(a2s), oracle.relu2(ref), 2 * tol, 1e-5, "relu2 square only")
+    aux_sq = to_dev(oracle.relu2(r.standard_normal((M, N))), dtype)
+    n.nc_gemm_bf16(0, 1, M, N, K, A, K, Bm, K, C, N, epilogue=n.NC_EPI_RELU2_BWD_SQ, aux=aux_sq)
+    sync()
+    # relu(u) recovered as the square root of the stored relu(u)^2
+    assert_close(dev_to_f64(C), oracle.relu2_bwd(ref, np.sqrt(dev_to_f64(aux_sq))), tol, 1e-5,
+                 "relu2 bwd from square")
 
 
 def test_gemm_split_k_is_deterministic():
