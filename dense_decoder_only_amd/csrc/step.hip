@@ -1,5 +1,9 @@
 // One training step of the nanochat-style dense decoder: forward and backward
-// of the mean next-token loss, all on one stream with no host sync.
+// of the mean next-token loss, with no host sync.  The weight-gradient
+// products of the backward run on a second (library-owned) stream, forked
+// from and joined back to the caller's stream with events, so they overlap
+// the activation-gradient chain; to the caller the step behaves as if it ran
+// on its own stream.
 //
 // Model (release-news page "Karpathy再放大招…", section 技術細節與問答):
 //   x = rms(E[ids])                                  token embedding + norm
@@ -13,11 +17,13 @@
 //
 // Saved for the backward (per layer, in the config dtype): the normalized
 // inputs a and m with their rstd, the post-norm qkv, the attention output o
-// and its log-sum-exp, the MLP pre-activation u and relu(u)^2.  The residual
-// stream and all gradients are fp32.
+// and its log-sum-exp, and relu(u)^2 of the MLP pre-activation u.  The
+// residual stream and all gradients are fp32.
 #include "common.h"
 #include "gemm.h"
 #include "ops.h"
+
+#include <mutex>
 
 namespace nc {
 namespace {
@@ -28,6 +34,10 @@ __global__ void check_ids_kernel(const int32_t* __restrict__ ids, int64_t n, int
     if (v < 0 || v >= V) *flag = 1;
   }
 }
+
+// Versions of a scratch buffer that the side stream may still be reading
+// while the main stream writes the next one.
+constexpr int kRing = 2;
 
 struct Layer {
   void *a, *qkv, *o, *m, *a2;  // a2 = relu(u)^2; u itself is not kept
@@ -40,15 +50,53 @@ struct StepWs {
   float *x, *x0, *rstd0;
   void* h;
   float *rstd_f, *lse_ce;
-  void* g_lp;
+  void* g_lp[kRing];  // bf16 copies of the residual gradient (read by the side stream)
   float* dm;
-  void *du, *dout, *dqkv;
+  void *du[kRing], *dout, *dqkv[kRing];
   float* dqkv_hat;
   void* wt;  // one layer's transposed weights (bf16 backward): Wqkv^T, Wo^T, W1^T, W2^T
   void *attn_ws, *gemm_ws, *xent_ws, *emb_ws;
   size_t attn_ws_bytes, gemm_ws_bytes, xent_ws_bytes, emb_ws_bytes;
   Layer* layers;  // host array filled by carve
 };
+
+#ifndef NC_STEP_SIDE_STREAM
+#define NC_STEP_SIDE_STREAM 1  // 0: the whole step on the caller's stream
+#endif
+
+// The side stream and a pool of events, one set per device, created on first
+// use and kept for the life of the process.  Enqueueing a step holds the
+// mutex, so concurrent steps on one device share the side stream in order.
+struct SideCtx {
+  hipStream_t s2 = nullptr;
+  std::vector<hipEvent_t> ev;
+  int next = 0;
+};
+std::mutex g_side_mu;
+SideCtx g_side[64];
+
+int side_ctx(SideCtx** out) {
+  int dev = 0;
+  NC_CHECK_HIP(hipGetDevice(&dev));
+  NC_REQUIRE(dev >= 0 && dev < 64, NC_ERR_UNSUPPORTED, "step: device index %d", dev);
+  SideCtx& c = g_side[dev];
+  if (!c.s2) {
+    NC_CHECK_HIP(hipStreamCreateWithFlags(&c.s2, hipStreamNonBlocking));
+    c.ev.resize(512);
+    for (auto& e : c.ev) NC_CHECK_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  }
+  *out = &c;
+  return NC_OK;
+}
+
+// `to` waits for everything enqueued on `from` so far.
+int stream_dep(SideCtx* c, hipStream_t from, hipStream_t to) {
+  hipEvent_t e = c->ev[c->next];
+  c->next = (c->next + 1) % (int)c->ev.size();
+  NC_CHECK_HIP(hipEventRecord(e, from));
+  NC_CHECK_HIP(hipStreamWaitEvent(to, e, 0));
+  return NC_OK;
+}
 
 int validate_cfg(const nc_config* c) {
   NC_REQUIRE(c, NC_ERR_INVALID_ARG, "step: null config");
@@ -82,8 +130,13 @@ size_t carve(const nc_config* c, StepWs* w, void* base) {
   const size_t o_flag = take(4), o_tab = take((size_t)c->seq_len * hd * 4);
   const size_t o_x = take(M * d * 4), o_x0 = take(M * d * 4), o_r0 = take(M * 4);
   const size_t o_h = take(M * d * e), o_rf = take(M * 4), o_lce = take(M * 4);
-  const size_t o_glp = take(M * d * e), o_dm = take(M * d * 4), o_du = take(M * F * e), o_do = take(M * H * hd * e);
-  const size_t o_dq = take(M * Q * e), o_dqh = take(M * Q * 4);
+  size_t o_glp[kRing], o_du[kRing], o_dq[kRing];
+  for (int r = 0; r < kRing; ++r) o_glp[r] = take(M * d * e);
+  const size_t o_dm = take(M * d * 4);
+  for (int r = 0; r < kRing; ++r) o_du[r] = take(M * F * e);
+  const size_t o_do = take(M * H * hd * e);
+  for (int r = 0; r < kRing; ++r) o_dq[r] = take(M * Q * e);
+  const size_t o_dqh = take(M * Q * 4);
   const size_t o_wt = take((size_t)(Q * d + d * H * hd + 2 * F * d) * e);
   const size_t attn_b = mqa_attn_bwd_workspace_bytes(c->batch, c->seq_len, (int)H);
   size_t gemm_b = 0;
@@ -103,11 +156,13 @@ size_t carve(const nc_config* c, StepWs* w, void* base) {
     w->h = ptr(o_h);
     w->rstd_f = static_cast<float*>(ptr(o_rf));
     w->lse_ce = static_cast<float*>(ptr(o_lce));
-    w->g_lp = ptr(o_glp);
+    for (int r = 0; r < kRing; ++r) {
+      w->g_lp[r] = ptr(o_glp[r]);
+      w->du[r] = ptr(o_du[r]);
+      w->dqkv[r] = ptr(o_dq[r]);
+    }
     w->dm = static_cast<float*>(ptr(o_dm));
-    w->du = ptr(o_du);
     w->dout = ptr(o_do);
-    w->dqkv = ptr(o_dq);
     w->dqkv_hat = static_cast<float*>(ptr(o_dqh));
     w->wt = ptr(o_wt);
     w->attn_ws = ptr(o_aws);
@@ -225,12 +280,52 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
                   w.xent_ws, w.xent_ws_bytes, s));
 
   // --------------------------------------------------------------- backward
+  // Side stream: the weight-gradient products dW = dY^T X, which nothing in
+  // the backward reads.  Each fork makes the side stream wait for the main
+  // stream's work so far; before the main stream rewrites a ring buffer it
+  // waits for the side stream's work so far (which includes the last reader
+  // of that buffer).
+  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+  SideCtx* side = nullptr;
+  hipStream_t s2 = s;
+  if (NC_STEP_SIDE_STREAM) {
+    side_lock.lock();
+    NC_TRY(side_ctx(&side));
+    s2 = side->s2;
+  }
+  auto fork = [&]() -> int { return side ? stream_dep(side, s, s2) : NC_OK; };
+  auto join = [&]() -> int { return side ? stream_dep(side, s2, s) : NC_OK; };
+  int gv = 0, uv = 0, qv = 0;  // ring versions of g_lp, du, dqkv
+  // read_done[buffer][slot]: recorded on the side stream after the last side
+  // reader of the version in that slot; the main stream waits for it before
+  // writing the slot's next version.
+  hipEvent_t read_done[3][kRing] = {};
+  auto mark_read = [&](int buf, int v) -> int {
+    if (!side) return NC_OK;
+    hipEvent_t e = side->ev[side->next];
+    side->next = (side->next + 1) % (int)side->ev.size();
+    NC_CHECK_HIP(hipEventRecord(e, s2));
+    read_done[buf][v % kRing] = e;
+    return NC_OK;
+  };
+  auto reuse = [&](int buf, int v) -> int {
+    if (side && read_done[buf][v % kRing]) NC_CHECK_HIP(hipStreamWaitEvent(s, read_done[buf][v % kRing], 0));
+    return NC_OK;
+  };
+  enum { B_G = 0, B_DU = 1, B_DQ = 2 };
+
   float* g = w.x;  // the residual stream is dead: reuse it for its gradient
-  void* gop = dt == NC_BF16 ? w.g_lp : static_cast<void*>(g);
-  void* glp_out = dt == NC_BF16 ? w.g_lp : nullptr;
+  auto gop_of = [&](int v) -> void* { return dt == NC_BF16 ? w.g_lp[v % kRing] : static_cast<void*>(g); };
+  auto glp_out = [&](int v) -> bf16* { return dt == NC_BF16 ? static_cast<bf16*>(w.g_lp[v % kRing]) : nullptr; };
   NC_TRY(xent_bwd(w.h, p->unembed, dt, tgt, w.lse_ce, M, (int)d, V, c->softcap, 1.f / (float)M, w.dm, 0,
                   gr->unembed, acc, w.xent_ws, w.xent_ws_bytes, s));
-  NC_TRY(rmsnorm_bwd(w.dm, NC_F32, w.h, dt, w.rstd_f, M, (int)d, g, 0, glp_out, s));
+  NC_TRY(rmsnorm_bwd(w.dm, NC_F32, w.h, dt, w.rstd_f, M, (int)d, g, 0, glp_out(gv), s));
+  // In fp32 the gradient copy is the residual gradient itself, which the
+  // main stream keeps updating: the side stream must then run in line.
+  if (dt != NC_BF16 && side) {
+    side = nullptr;
+    s2 = s;
+  }
 
   // In bf16 the activation gradients dX = dY W use the transposed weights so
   // that every product runs in the K-contiguous (x W^T) form.
@@ -240,6 +335,12 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
   void* WoT = wt + (size_t)Q * d * e;
   void* W1T = wt + (size_t)(Q * d + d * HD) * e;
   void* W2T = wt + (size_t)(Q * d + d * HD + F * d) * e;
+  auto wgrad = [&](GemmDesc gd) -> int {
+    gd.beta = (float)acc;
+    gd.ws = w.gemm_ws;
+    gd.ws_bytes = w.gemm_ws_bytes;
+    return gemm(gd, s2);
+  };
   for (int l = L - 1; l >= 0; --l) {
     Layer& ly = layers[l];
     const void* Wqkv = wl(p->w_qkv, l, Q * d);
@@ -253,40 +354,45 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
       NC_TRY(transpose(W2, d, F, 2, W2T, s));
     }
     // MLP: x_out = x_mid + relu(m W1^T)^2 W2^T
-    GemmDesc g1 = mk(1, 0, d, F, M, gop, d, ly.a2, F, gr->w_proj + (size_t)l * d * F, NC_F32, F, dt);
-    g1.beta = (float)acc;
-    g1.ws = w.gemm_ws;
-    g1.ws_bytes = w.gemm_ws_bytes;
-    NC_TRY(gemm(g1, s));
-    GemmDesc g2 = tw ? mk(0, 1, M, F, d, gop, d, W2T, d, w.du, dt, F, dt) : mk(0, 0, M, F, d, gop, d, W2, F, w.du, dt, F, dt);
+    void* gop = gop_of(gv);
+    NC_TRY(fork());
+    NC_TRY(wgrad(mk(1, 0, d, F, M, gop, d, ly.a2, F, gr->w_proj + (size_t)l * d * F, NC_F32, F, dt)));
+    NC_TRY(mark_read(B_G, gv));
+    void* du = w.du[uv % kRing];
+    NC_TRY(reuse(B_DU, uv));
+    GemmDesc g2 = tw ? mk(0, 1, M, F, d, gop, d, W2T, d, du, dt, F, dt) : mk(0, 0, M, F, d, gop, d, W2, F, du, dt, F, dt);
     g2.epi = NC_EPI_RELU2_BWD_SQ;
     g2.aux = ly.a2;
     NC_TRY(gemm(g2, s));
-    GemmDesc g3 = mk(1, 0, F, d, M, w.du, F, ly.m, d, gr->w_fc + (size_t)l * F * d, NC_F32, d, dt);
-    g3.beta = (float)acc;
-    g3.ws = w.gemm_ws;
-    g3.ws_bytes = w.gemm_ws_bytes;
-    NC_TRY(gemm(g3, s));
-    NC_TRY(gemm(tw ? mk(0, 1, M, d, F, w.du, F, W1T, F, w.dm, NC_F32, d, dt) : mk(0, 0, M, d, F, w.du, F, W1, d, w.dm, NC_F32, d, dt), s));
-    NC_TRY(rmsnorm_bwd(w.dm, NC_F32, ly.m, dt, ly.rstd_m, M, (int)d, g, 1, glp_out, s));
+    NC_TRY(fork());
+    NC_TRY(wgrad(mk(1, 0, F, d, M, du, F, ly.m, d, gr->w_fc + (size_t)l * F * d, NC_F32, d, dt)));
+    NC_TRY(mark_read(B_DU, uv));
+    ++uv;
+    NC_TRY(gemm(tw ? mk(0, 1, M, d, F, du, F, W1T, F, w.dm, NC_F32, d, dt) : mk(0, 0, M, d, F, du, F, W1, d, w.dm, NC_F32, d, dt), s));
+    ++gv;
+    NC_TRY(reuse(B_G, gv));
+    NC_TRY(rmsnorm_bwd(w.dm, NC_F32, ly.m, dt, ly.rstd_m, M, (int)d, g, 1, glp_out(gv), s));
     // attention: x_mid = x_in + mqa(...) Wo^T
-    GemmDesc g4 = mk(1, 0, d, HD, M, gop, d, ly.o, HD, gr->w_o + (size_t)l * d * HD, NC_F32, HD, dt);
-    g4.beta = (float)acc;
-    g4.ws = w.gemm_ws;
-    g4.ws_bytes = w.gemm_ws_bytes;
-    NC_TRY(gemm(g4, s));
+    gop = gop_of(gv);
+    NC_TRY(fork());
+    NC_TRY(wgrad(mk(1, 0, d, HD, M, gop, d, ly.o, HD, gr->w_o + (size_t)l * d * HD, NC_F32, HD, dt)));
+    NC_TRY(mark_read(B_G, gv));
     NC_TRY(gemm(tw ? mk(0, 1, M, HD, d, gop, d, WoT, d, w.dout, dt, HD, dt) : mk(0, 0, M, HD, d, gop, d, Wo, HD, w.dout, dt, HD, dt), s));
     NC_TRY(mqa_attn_bwd(ly.qkv, ly.o, w.dout, ly.lse, dt, B, T, H, hd, scale, w.dqkv_hat, w.attn_ws,
                         w.attn_ws_bytes, s));
-    NC_TRY(rope_qknorm_bwd(w.dqkv_hat, ly.qkv, ly.rstd_q, ly.rstd_k, w.table, dt, B, T, H, hd, w.dqkv, s));
-    GemmDesc g5 = mk(1, 0, Q, d, M, w.dqkv, Q, ly.a, d, gr->w_qkv + (size_t)l * Q * d, NC_F32, d, dt);
-    g5.beta = (float)acc;
-    g5.ws = w.gemm_ws;
-    g5.ws_bytes = w.gemm_ws_bytes;
-    NC_TRY(gemm(g5, s));
-    NC_TRY(gemm(tw ? mk(0, 1, M, d, Q, w.dqkv, Q, WqkvT, Q, w.dm, NC_F32, d, dt) : mk(0, 0, M, d, Q, w.dqkv, Q, Wqkv, d, w.dm, NC_F32, d, dt), s));
-    NC_TRY(rmsnorm_bwd(w.dm, NC_F32, ly.a, dt, ly.rstd_a, M, (int)d, g, 1, glp_out, s));
+    void* dqkv = w.dqkv[qv % kRing];
+    NC_TRY(reuse(B_DQ, qv));
+    NC_TRY(rope_qknorm_bwd(w.dqkv_hat, ly.qkv, ly.rstd_q, ly.rstd_k, w.table, dt, B, T, H, hd, dqkv, s));
+    NC_TRY(fork());
+    NC_TRY(wgrad(mk(1, 0, Q, d, M, dqkv, Q, ly.a, d, gr->w_qkv + (size_t)l * Q * d, NC_F32, d, dt)));
+    NC_TRY(mark_read(B_DQ, qv));
+    ++qv;
+    NC_TRY(gemm(tw ? mk(0, 1, M, d, Q, dqkv, Q, WqkvT, Q, w.dm, NC_F32, d, dt) : mk(0, 0, M, d, Q, dqkv, Q, Wqkv, d, w.dm, NC_F32, d, dt), s));
+    ++gv;
+    NC_TRY(reuse(B_G, gv));
+    NC_TRY(rmsnorm_bwd(w.dm, NC_F32, ly.a, dt, ly.rstd_a, M, (int)d, g, 1, glp_out(gv), s));
   }
+  NC_TRY(join());
   // embedding norm and scatter-add
   NC_TRY(rmsnorm_bwd(g, NC_F32, w.x0, NC_F32, w.rstd0, M, (int)d, w.dm, 0, nullptr, s));
   NC_TRY(embed_bwd(ids, M, w.dm, (int)d, gr->embed, V, acc, w.emb_ws, w.emb_ws_bytes, s));

@@ -30,8 +30,8 @@
  *     is enqueued and nc_last_error() returns a message (thread-local).
  *     Nothing aborts, prints or throws across this ABI.
  *   - Calls are thread-safe; the library has no mutable global state other
- *     than the thread-local error message and the kernel timer (nc_probe_*),
- *     which a mutex guards.
+ *     than the thread-local error message, the kernel timer (nc_probe_*) and
+ *     the step's side stream (below), which mutexes guard.
  *   - Out-of-range token ids are caught on the device: the row is treated as
  *     zeros and a device flag (an int32 given by the caller) is set to 1;
  *     nc_sync_status reads it.
@@ -160,7 +160,13 @@ int nc_probe_stop(double* total_ms, int64_t* launches, double* flops);
  *   grads        : fp32 gradients of `loss` w.r.t. every parameter.
  * Errors: NC_ERR_INVALID_ARG (null pointers, n_kv_head != 1, H hd != d),
  *   NC_ERR_UNSUPPORTED (head_dim not 64/128; sizes not multiples of 8),
- *   NC_ERR_WORKSPACE. */
+ *   NC_ERR_WORKSPACE.
+ * Streams: the weight-gradient products of the backward run on a second
+ *   stream that the library creates once per device (default priority) and
+ *   orders against `stream` with events; the call returns after enqueueing,
+ *   and work enqueued on `stream` afterwards sees every output.  Concurrent
+ *   calls on one device share that stream (in enqueue order).
+ */
 size_t nc_step_workspace_bytes(const nc_config* cfg);
 int nc_step_fwd_bwd(const nc_config* cfg, const nc_params* params, const nc_grads* grads,
                     const int32_t* ids, const int32_t* targets, const float* token_bytes,
