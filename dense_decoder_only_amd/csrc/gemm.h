@@ -24,10 +24,11 @@ struct GemmDesc {
   // Softcap cross-entropy epilogues on the logit product z = h U^T (bf16,
   // K-contiguous operands, K a multiple of 64).  Columns are vocabulary ids
   // xv0 + n.
-  //   xent = 1: C is not written; per row and 64-column group g (vocabulary
-  //             columns 64 g .. 64 g + 63) xpart[g * M + row] = sum of
-  //             exp(z' - c), z' = c tanh(z / c); xztgt[row] = z' at the
-  //             row's target when the target is one of these columns.
+  //   xent = 1: per row and 64-column group g (vocabulary columns
+  //             64 g .. 64 g + 63) xpart[g * M + row] = sum of exp(z' - c),
+  //             z' = c tanh(z / c); xztgt[row] = z' at the row's target when
+  //             the target is one of these columns.  If C is not null it
+  //             receives z' as int16 fixed point, round(z' / c * 32767).
   //   xent = 2: C (bf16) = xdl (exp(z' - xlse[row]) - [col == target])
   //             (1 - (z'/c)^2).
   int xent = 0;

@@ -100,13 +100,21 @@ __device__ __forceinline__ void xent_fwd4(const MfmaParams& p, float4 v, int row
   const int y = ok ? p.xtgt[row] - p.xv0 : -1;
   const float zz[4] = {v.x, v.y, v.z, v.w};
   float s = 0.f;
+  float zq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if (col + e < p.N) {
       const float zc = softcap_of(zz[e], p.xc, p.xinv_c);
       s += __builtin_amdgcn_exp2f((zc - p.xc) * kLog2e);
       if (ok && col + e == y) p.xztgt[row] = zc;
+      zq[e] = zc * p.xinv_c * 32767.f;
     }
+  }
+  if (p.C && ok && col < p.N) {  // N is a multiple of 8: the 4 columns are all in range
+    const int q0 = __float2int_rn(zq[0]), q1 = __float2int_rn(zq[1]);
+    const int q2 = __float2int_rn(zq[2]), q3 = __float2int_rn(zq[3]);
+    *reinterpret_cast<uint2*>(static_cast<int16_t*>(p.C) + (int64_t)row * p.ldc + col) =
+        make_uint2((uint32_t)(q0 & 0xffff) | ((uint32_t)q1 << 16), (uint32_t)(q2 & 0xffff) | ((uint32_t)q3 << 16));
   }
   s += __shfl_xor(s, 1, 64);
   s += __shfl_xor(s, 2, 64);
@@ -1003,7 +1011,10 @@ int gemm_xent(const GemmDesc& g, hipStream_t stream) {
              NC_ERR_UNSUPPORTED, "gemm: the cross-entropy epilogues need K a multiple of 64");
   NC_REQUIRE(aligned16(g.A) && aligned16(g.B), NC_ERR_INVALID_ARG, "gemm: A and B must be 16-byte aligned");
   NC_REQUIRE(g.xv0 % 64 == 0, NC_ERR_INVALID_ARG, "gemm: vocabulary offset must be a multiple of 64");
-  if (g.xent == 1) NC_REQUIRE(g.xpart && g.xztgt, NC_ERR_INVALID_ARG, "gemm: null cross-entropy output");
+  if (g.xent == 1) {
+    NC_REQUIRE(g.xpart && g.xztgt, NC_ERR_INVALID_ARG, "gemm: null cross-entropy output");
+    if (g.C) NC_REQUIRE(g.ldc >= g.N && g.ldc % 4 == 0, NC_ERR_INVALID_ARG, "gemm: bad stored-logit layout");
+  }
   else NC_REQUIRE(g.C && g.xlse && g.cdt == NC_BF16 && g.ldc >= g.N, NC_ERR_INVALID_ARG, "gemm: bad dz output");
   MfmaParams p{};
   p.A = static_cast<const bf16*>(g.A);

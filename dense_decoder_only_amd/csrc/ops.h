@@ -28,12 +28,16 @@ int mqa_attn_bwd(const void* qkv, const void* o, const void* dout, const float* 
                  int hd, float scale, float* dqkv, void* ws, size_t ws_bytes, hipStream_t s);
 
 size_t xent_workspace_bytes(int64_t M, int d, int V);
+// store_logits: keep the softcapped logits in ws (16-bit fixed point) when the
+// fused path covers the vocabulary in one chunk; xent_bwd with from_stored
+// then forms dz from them instead of recomputing the logit product (same ws,
+// untouched in between).  Returns whether they were stored via *stored.
 int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* token_bytes, int64_t M, int d,
              int V, float softcap, float* lse, float* loss_tok, float* loss, float* bpb, void* ws, size_t ws_bytes,
-             hipStream_t s);
+             hipStream_t s, bool store_logits = false, bool* stored = nullptr);
 int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* lse, int64_t M, int d, int V,
              float softcap, float dloss, float* dh, int dh_acc, float* dU, int dU_acc, void* ws, size_t ws_bytes,
-             hipStream_t s);
+             hipStream_t s, bool from_stored = false);
 
 int fill_zero(void* p, size_t bytes, hipStream_t s);
 

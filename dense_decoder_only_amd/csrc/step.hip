@@ -276,8 +276,9 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
     NC_TRY(gemm(gp, s));
   }
   NC_TRY(rmsnorm_fwd(w.x, NC_F32, M, (int)d, c->eps, w.h, dt, w.rstd_f, s));
+  bool logits_stored = false;
   NC_TRY(xent_fwd(w.h, p->unembed, dt, tgt, token_bytes, M, (int)d, V, c->softcap, w.lse_ce, loss_tok, loss, bpb,
-                  w.xent_ws, w.xent_ws_bytes, s));
+                  w.xent_ws, w.xent_ws_bytes, s, true, &logits_stored));
 
   // --------------------------------------------------------------- backward
   // Side stream: the weight-gradient products dW = dY^T X, which nothing in
@@ -318,7 +319,7 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
   auto gop_of = [&](int v) -> void* { return dt == NC_BF16 ? w.g_lp[v % kRing] : static_cast<void*>(g); };
   auto glp_out = [&](int v) -> bf16* { return dt == NC_BF16 ? static_cast<bf16*>(w.g_lp[v % kRing]) : nullptr; };
   NC_TRY(xent_bwd(w.h, p->unembed, dt, tgt, w.lse_ce, M, (int)d, V, c->softcap, 1.f / (float)M, w.dm, 0,
-                  gr->unembed, acc, w.xent_ws, w.xent_ws_bytes, s));
+                  gr->unembed, acc, w.xent_ws, w.xent_ws_bytes, s, logits_stored));
   NC_TRY(rmsnorm_bwd(w.dm, NC_F32, w.h, dt, w.rstd_f, M, (int)d, g, 0, glp_out(gv), s));
   // In fp32 the gradient copy is the residual gradient itself, which the
   // main stream keeps updating: the side stream must then run in line.

@@ -181,6 +181,40 @@ __global__ __launch_bounds__(256) void xent_bwd_rows_kernel(const float* __restr
   }
 }
 
+// dz from the stored logits, in place: q = round(z'/c * 32767) (int16) ->
+// dz = dloss (exp(z' - lse) - [v == y]) (1 - (z'/c)^2) (bf16), 8 per thread.
+// One chunk covering the whole vocabulary (column = vocabulary id).
+__global__ __launch_bounds__(256) void xent_dz_stored_kernel(uint16_t* __restrict__ buf, int64_t M, int N, float c,
+                                                             const int32_t* __restrict__ tgt,
+                                                             const float* __restrict__ lse, float dloss) {
+  const int64_t total8 = M * N / 8;
+  const float inv = 1.f / 32767.f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total8; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = i * 8;
+    const int64_t row = e0 / N;
+    const int col = (int)(e0 - row * N);
+    const float L2 = lse[row] * 1.4426950408889634f;
+    const float c2 = c * 1.4426950408889634f;
+    const int y = tgt[row];
+    uint4 q = *reinterpret_cast<const uint4*>(buf + e0);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float g2[2];
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        const int16_t qi = (int16_t)(hlf ? (w[k] >> 16) : (w[k] & 0xffffu));
+        const float th = (float)qi * inv;  // z' / c
+        const float pr = __builtin_amdgcn_exp2f(c2 * th - L2);  // exp(z' - lse) by the hardware exp2
+        g2[hlf] = dloss * (pr - (col + 2 * k + hlf == y ? 1.f : 0.f)) * (1.f - th * th);
+      }
+      o[k] = pack_bf16x2(g2[0], g2[1]);
+    }
+    *reinterpret_cast<uint4*>(buf + e0) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 int validate(const void* h, const void* U, int dtype, const int32_t* tgt, int64_t M, int d, int V) {
   NC_REQUIRE(h && U && tgt, NC_ERR_INVALID_ARG, "softcap_xent: null pointer");
   NC_REQUIRE(M > 0 && d > 0 && V > 0, NC_ERR_INVALID_ARG, "softcap_xent: bad shape");
@@ -198,7 +232,8 @@ size_t xent_workspace_bytes(int64_t M, int d, int V) {
 
 int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* token_bytes, int64_t M, int d,
              int V, float softcap, float* lse, float* loss_tok, float* loss, float* bpb, void* ws, size_t ws_bytes,
-             hipStream_t s) {
+             hipStream_t s, bool store_logits, bool* stored) {
+  if (stored) *stored = false;
   NC_TRY(validate(h, U, dtype, tgt, M, d, V));
   NC_REQUIRE(lse && loss && bpb, NC_ERR_INVALID_ARG, "softcap_xent_fwd: null output");
   NC_REQUIRE(softcap > 0.f, NC_ERR_INVALID_ARG, "softcap_xent_fwd: softcap must be positive");
@@ -231,6 +266,11 @@ int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
       g.xpart = w.partial;
       g.xztgt = w.ztgt;
       g.xv0 = v0;
+      if (store_logits && nch == 1) {
+        g.C = w.dz;
+        g.ldc = n;
+        if (stored) *stored = true;
+      }
       NC_TRY(gemm(g, s));
       continue;
     }
@@ -252,7 +292,7 @@ int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
 
 int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* lse, int64_t M, int d, int V,
              float softcap, float dloss, float* dh, int dh_acc, float* dU, int dU_acc, void* ws, size_t ws_bytes,
-             hipStream_t s) {
+             hipStream_t s, bool from_stored) {
   NC_TRY(validate(h, U, dtype, tgt, M, d, V));
   NC_REQUIRE(lse && dh && dU, NC_ERR_INVALID_ARG, "softcap_xent_bwd: null pointer");
   NC_REQUIRE(softcap > 0.f, NC_ERR_INVALID_ARG, "softcap_xent_bwd: softcap must be positive");
@@ -280,7 +320,13 @@ int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
     g.B = Uc;
     g.ldb = d;
     g.dtype = dtype;
-    if (fused) {
+    if (fused && from_stored) {
+      NC_REQUIRE(nch == 1, NC_ERR_INVALID_ARG, "softcap_xent_bwd: stored logits need a one-chunk vocabulary");
+      const int64_t total8 = (int64_t)M * n / 8;
+      xent_dz_stored_kernel<<<(unsigned)std::min<int64_t>(cdiv(total8, 256), 65536), 256, 0, s>>>(
+          static_cast<uint16_t*>(w.dz), M, n, softcap, tgt, lse, dloss);
+      NC_TRY(check_launch("xent_dz_stored_kernel"));
+    } else if (fused) {
       g.xent = 2;
       g.xc = softcap;
       g.xdl = dloss;
