@@ -1,9 +1,8 @@
 // One training step of the nanochat-style dense decoder: forward and backward
-// of the mean next-token loss, with no host sync.  The weight-gradient
-// products of the backward run on a second (library-owned) stream, forked
-// from and joined back to the caller's stream with events, so they overlap
-// the activation-gradient chain; to the caller the step behaves as if it ran
-// on its own stream.
+// of the mean next-token loss, with no host sync, on the caller's stream.
+// (Built with NC_STEP_SIDE_STREAM=1 the weight-gradient products of the
+// backward run on a second, library-owned stream forked from and joined back
+// to the caller's stream with events.)
 //
 // Model (release-news page "Karpathy再放大招…", section 技術細節與問答):
 //   x = rms(E[ids])                                  token embedding + norm
@@ -35,9 +34,17 @@ __global__ void check_ids_kernel(const int32_t* __restrict__ ids, int64_t n, int
   }
 }
 
+// Weight-gradient products on a side stream overlapping the
+// activation-gradient chain.  Measured at d20 it gains 1.2% of step time but
+// stretches every concurrent kernel (both streams share the CUs), so the
+// per-kernel timings stop describing the kernels; off by default.
+#ifndef NC_STEP_SIDE_STREAM
+#define NC_STEP_SIDE_STREAM 0
+#endif
+
 // Versions of a scratch buffer that the side stream may still be reading
 // while the main stream writes the next one.
-constexpr int kRing = 2;
+constexpr int kRing = NC_STEP_SIDE_STREAM ? 2 : 1;
 
 struct Layer {
   void *a, *qkv, *o, *m, *a2;  // a2 = relu(u)^2; u itself is not kept
@@ -60,9 +67,6 @@ struct StepWs {
   Layer* layers;  // host array filled by carve
 };
 
-#ifndef NC_STEP_SIDE_STREAM
-#define NC_STEP_SIDE_STREAM 1  // 0: the whole step on the caller's stream
-#endif
 
 // The side stream and a pool of events, one set per device, created on first
 // use and kept for the life of the process.  Enqueueing a step holds the

@@ -31,7 +31,7 @@
  *     Nothing aborts, prints or throws across this ABI.
  *   - Calls are thread-safe; the library has no mutable global state other
  *     than the thread-local error message, the kernel timer (nc_probe_*) and
- *     the step's side stream (below), which mutexes guard.
+ *     the step's optional side stream, which mutexes guard.
  *   - Out-of-range token ids are caught on the device: the row is treated as
  *     zeros and a device flag (an int32 given by the caller) is set to 1;
  *     nc_sync_status reads it.
@@ -161,11 +161,10 @@ int nc_probe_stop(double* total_ms, int64_t* launches, double* flops);
  * Errors: NC_ERR_INVALID_ARG (null pointers, n_kv_head != 1, H hd != d),
  *   NC_ERR_UNSUPPORTED (head_dim not 64/128; sizes not multiples of 8),
  *   NC_ERR_WORKSPACE.
- * Streams: the weight-gradient products of the backward run on a second
- *   stream that the library creates once per device (default priority) and
- *   orders against `stream` with events; the call returns after enqueueing,
- *   and work enqueued on `stream` afterwards sees every output.  Concurrent
- *   calls on one device share that stream (in enqueue order).
+ * Streams: everything runs on `stream` (a build with NC_STEP_SIDE_STREAM=1
+ *   moves the weight-gradient products to a second stream that the library
+ *   creates once per device and orders against `stream` with events; work
+ *   enqueued on `stream` afterwards still sees every output).
  */
 size_t nc_step_workspace_bytes(const nc_config* cfg);
 int nc_step_fwd_bwd(const nc_config* cfg, const nc_params* params, const nc_grads* grads,
