@@ -765,6 +765,63 @@ __device__ __forceinline__ void pipe_stage(const MfmaParams& p, int m0, int n0, 
   }
 }
 
+// Buffer-resource form of the same staging: per stage a scalar base (the
+// tile's first row and column) and per lane loop-invariant 32-bit byte
+// offsets, computed once per block.
+#ifndef NC_GEMM_BUFDMA
+#define NC_GEMM_BUFDMA 1
+#endif
+struct StageOff {
+  uint32_t a[4], b[4];
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+template <bool TN>
+__device__ __forceinline__ void stage_offsets(const MfmaParams& p, int m0, int n0, int wave, int lane, StageOff& o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (TN) {
+      const int g = wave * 4 + i;
+      const int row = g * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (row & 3));
+      const int ca = min(m0 + c * 8, p.M - 8) - m0, cb = min(n0 + c * 8, p.N - 8) - n0;
+      o.a[i] = (uint32_t)(((int64_t)row * p.lda + ca) * 2);
+      o.b[i] = (uint32_t)(((int64_t)row * p.ldb + cb) * 2);
+    } else {
+      const int grp = wave * 4 + i, rsub = lane >> 3;
+      const int c = (lane & 7) ^ swz(grp * 8 + rsub);
+      const int ra = min(m0 + grp * 8 + rsub, p.M - 1) - m0, rb = min(n0 + grp * 8 + rsub, p.N - 1) - n0;
+      o.a[i] = (uint32_t)(((int64_t)ra * p.lda + c * 8) * 2);
+      o.b[i] = (uint32_t)(((int64_t)rb * p.ldb + c * 8) * 2);
+    }
+  }
+}
+
+template <bool TN>
+__device__ __forceinline__ void pipe_stage_buf(const MfmaParams& p, int m0, int n0, int k0, bf16* a_buf, bf16* b_buf,
+                                               int wave, const StageOff& o) {
+  const bf16* pa = TN ? p.A + (int64_t)k0 * p.lda + m0 : p.A + (int64_t)m0 * p.lda + k0;
+  const bf16* pb = TN ? p.B + (int64_t)k0 * p.ldb + n0 : p.B + (int64_t)n0 * p.ldb + k0;
+  const __amdgpu_buffer_rsrc_t ra = tile_rsrc(pa), rb = tile_rsrc(pb);
+  // LDS destination of instruction i of this wave (1 KB each)
+  const int step = TN ? 2 * TROW : 8 * BK;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = wave * 4 + i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(a_buf + g * step), 16,
+                                             o.a[i], 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = wave * 4 + i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(b_buf + g * step), 16,
+                                             o.b[i], 0, 0, 0);
+  }
+}
+
 template <bool TN>
 __device__ __forceinline__ void pipe_frags(const bf16* a_buf, const bf16* b_buf, int ks, int wm, int wn, int lane,
                                            bf16x8_t (&fa)[4], bf16x8_t (&fb)[2]) {
@@ -836,8 +893,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  pipe_stage<TN>(p, m0, n0, kbeg, As, Bs, wave, lane);
-  pipe_stage<TN>(p, m0, n0, nk > 1 ? kbeg + BK : kbeg, As + BM * BK, Bs + BN * BK, wave, lane);
+#if NC_GEMM_BUFDMA
+  StageOff so;
+  stage_offsets<TN>(p, m0, n0, wave, lane, so);
+#define PIPE_STAGE(k0, abuf, bbuf) pipe_stage_buf<TN>(p, m0, n0, k0, abuf, bbuf, wave, so)
+#else
+#define PIPE_STAGE(k0, abuf, bbuf) pipe_stage<TN>(p, m0, n0, k0, abuf, bbuf, wave, lane)
+#endif
+  PIPE_STAGE(kbeg, As, Bs);
+  PIPE_STAGE(nk > 1 ? kbeg + BK : kbeg, As + BM * BK, Bs + BN * BK);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -879,7 +943,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     const int k2 = kt + 2 < nk ? kbeg + (kt + 2) * BK : klast;
-    pipe_stage<TN>(p, m0, n0, k2, As + cur * (BM * BK), Bs + cur * (BN * BK), wave, lane);
+    PIPE_STAGE(k2, As + cur * (BM * BK), Bs + cur * (BN * BK));
     pipe_frags<TN>(As + (cur ^ 1) * (BM * BK), Bs + (cur ^ 1) * (BN * BK), 0, wm, wn, lane, fa[0], fb[0]);
 #pragma unroll
     for (int q = NC_GEMM_PIPE_PRE; q < 8; ++q)
@@ -915,6 +979,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
   }
+#undef PIPE_STAGE
 }
 
 template <bool TN>
