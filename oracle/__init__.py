@@ -39,3 +39,4 @@ from .model import (  # noqa: F401
     step,
     to_f64_params,
 )
+from .optim import adamw_step  # noqa: F401
