@@ -52,6 +52,7 @@ _SIGS = {
     "nc_last_error": (ctypes.c_char_p, []),
     "nc_version": (ctypes.c_char_p, []),
     "nc_sync_status": (c_int, [c_p, c_p]),
+    "nc_adamw_step": (c_int, [c_p, c_p, c_p, c_p, c_p, c_i64, c_int, c_f, c_f, c_f, c_f, c_f, c_f, c_p]),
     "nc_probe_start": (c_int, [c_int, c_int]),
     "nc_probe_stop": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64),
                               ctypes.POINTER(ctypes.c_double)]),
@@ -152,6 +153,12 @@ def nc_last_error() -> str:
 def nc_sync_status(flag, stream=None) -> int:
     """Returns the status code (NC_OK or NC_ERR_DEVICE_FLAG) instead of raising on the flag."""
     return load().nc_sync_status(_p(flag), _stream(stream))
+
+
+def nc_adamw_step(master, m, v, grad, weights_lp, t, lr, beta1, beta2, eps, weight_decay, grad_scale=1.0,
+                  stream=None) -> None:
+    _check(load().nc_adamw_step(_p(master), _p(m), _p(v), _p(grad), _p(weights_lp), master.numel(), int(t),
+                                lr, beta1, beta2, eps, weight_decay, grad_scale, _stream(stream)))
 
 
 def nc_probe_start(family: int, max_launches: int) -> None:

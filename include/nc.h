@@ -325,6 +325,25 @@ int nc_softcap_xent_bwd(const void* h, const void* U, int dtype, const int32_t* 
                         float* dh, int dh_accumulate, float* dU, int dU_accumulate, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * AdamW parameter update with the bf16 weight refresh, for the training loop
+ * that follows the step.  [NEWS] names Muon + AdamW as the optimizers without
+ * defining them; this is the published AdamW (decoupled weight decay, bias-
+ * corrected moments), with every hyperparameter an argument:
+ *   g  = grad_scale * grad
+ *   m  = beta1 m + (1 - beta1) g ;  v = beta2 v + (1 - beta2) g^2
+ *   p  = p (1 - lr weight_decay) - lr (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ *   weights_lp (bf16, may be NULL) = p rounded to nearest, ties to even.
+ *   master, m, v, grad: fp32 [n] device arrays, 16-byte aligned; master, m
+ *   and v are updated in place.  t >= 1 is the step count (1 on the first
+ *   update).  One pass over HBM: 28 bytes per parameter (30 with the bf16
+ *   copy).
+ * n == 0 is a no-op (the pointers may then be NULL).
+ * Errors: NC_ERR_INVALID_ARG (null or misaligned pointers, n < 0, t < 1). */
+int nc_adamw_step(float* master, float* m, float* v, const float* grad, void* weights_lp, int64_t n, int t,
+                  float lr, float beta1, float beta2, float eps, float weight_decay, float grad_scale,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

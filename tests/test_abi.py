@@ -80,3 +80,10 @@ def test_step_workspace_query_and_config_validation():
     rc = lib.nc_step_fwd_bwd(ctypes.byref(ok), ctypes.byref(p), ctypes.byref(g), None, None, None, None, 0, None,
                              None, None, None)
     assert rc == nc.NC_ERR_INVALID_ARG
+
+
+def test_adamw_host_validation():
+    from dense_decoder_only_amd import nc
+    lib = nc.load()
+    rc = lib.nc_adamw_step(None, None, None, None, None, 16, 1, 1e-3, 0.9, 0.95, 1e-8, 0.0, 1.0, None)
+    assert rc == nc.NC_ERR_INVALID_ARG and "null" in nc.nc_last_error()

@@ -1,0 +1,154 @@
+"""AdamW kernel and a short training loop on the GPU, against the fp64 oracle.
+
+* nc_adamw_step: several steps on random data (ragged tail), moments and
+  master weights against oracle.adamw_step, the bf16 refresh against the
+  rounded oracle weights.
+* Training loop: nc_step_fwd_bwd + nc_adamw_step on every parameter for a few
+  steps (tiny fp32, small bf16 on one sequence), losses and final weights
+  against the oracle running the same loop (oracle.step + oracle.adamw_step).
+* Gradient accumulation: two half batches with accumulate = 1 give the sum of
+  the two half-batch mean gradients, i.e. twice the full-batch gradient of
+  the oracle.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, PARAM_NAMES, assert_close, bf16_tensor_from_bits, dev_to_f64, run_step, to_dev
+from synthetic import CONFIGS, make_inputs, to_bf16_bits, bf16_bits_to_f32
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+
+
+def _nc():
+    from dense_decoder_only_amd import nc
+    nc.load()
+    return nc
+
+
+@pytest.mark.parametrize("n", [4096, 10003])
+def test_adamw_kernel_matches_oracle(n):
+    nc = _nc()
+    r = np.random.default_rng(n)
+    p0 = r.standard_normal(n).astype(np.float32)
+    P = torch.from_numpy(p0.copy()).to(DEV)
+    M = torch.zeros(n, device=DEV)
+    V = torch.zeros(n, device=DEV)
+    W = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    p, m, v = p0.astype(np.float64), np.zeros(n), np.zeros(n)
+    lr, gs = 2e-3, 0.5
+    for t in range(1, 6):
+        g = (r.standard_normal(n) * (1.0 + t)).astype(np.float32)
+        nc.nc_adamw_step(P, M, V, torch.from_numpy(g).to(DEV), W, t, lr, grad_scale=gs, **HP)
+        p, m, v = oracle.adamw_step(p, g.astype(np.float64), m, v, t, lr, grad_scale=gs, **HP)
+    torch.cuda.synchronize()
+    assert_close(dev_to_f64(M), m, 1e-5, 1e-7, "adamw m")
+    assert_close(dev_to_f64(V), v, 1e-5, 1e-7, "adamw v")
+    assert_close(dev_to_f64(P), p, 1e-6, 1e-6, "adamw master")
+    # the bf16 copy is within half a bf16 ulp (plus the fp32 difference) of the oracle's weights
+    w = dev_to_f64(W)
+    assert np.all(np.abs(w - p) <= np.abs(p) * 2.0 ** -8 + 1e-6)
+    # and exactly the round-to-nearest-even of the fp32 master it was written from
+    got_bits = W.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got_bits, to_bf16_bits(P.cpu().numpy()))
+
+
+def test_adamw_kernel_empty_and_errors():
+    nc = _nc()
+    x = torch.zeros(8, device=DEV)
+    nc.nc_adamw_step(x[:0], x[:0], x[:0], x[:0], None, 1, 1e-3, **HP)  # n = 0: nothing to do
+    with pytest.raises(nc.NcError):
+        nc.nc_adamw_step(x, x, x, x, None, 0, 1e-3, **HP)  # t must be >= 1
+
+
+def _loop(cfg, batch, steps, lr):
+    nc = _nc()
+    c = dataclasses.replace(cfg, batch=batch)
+    inp = make_inputs(cfg, batch)
+    bf16 = cfg.dtype == "bf16"
+    master = {k: to_dev(inp["weights"][k], torch.float32) for k in PARAM_NAMES}
+    m = {k: torch.zeros_like(master[k]) for k in PARAM_NAMES}
+    v = {k: torch.zeros_like(master[k]) for k in PARAM_NAMES}
+    if bf16:
+        params = {k: bf16_tensor_from_bits(inp["weights_bf16"][k]) for k in PARAM_NAMES}
+    else:
+        params = master
+    grads = {k: torch.empty_like(master[k]) for k in PARAM_NAMES}
+    ccfg = nc.make_config(c)
+    ws = torch.empty(nc.nc_step_workspace_bytes(ccfg), dtype=torch.uint8, device=DEV)
+    loss = torch.empty(1, device=DEV)
+    bpb = torch.empty(1, device=DEV)
+    ids = torch.from_numpy(inp["ids"]).to(DEV)
+    tgt = torch.from_numpy(inp["targets"]).to(DEV)
+    tb = torch.from_numpy(inp["token_bytes"]).to(DEV)
+    losses = []
+    # oracle loop on the same batch
+    op = oracle.to_f64_params(inp["weights"])
+    om = {k: np.zeros_like(op[k]) for k in PARAM_NAMES}
+    ov = {k: np.zeros_like(op[k]) for k in PARAM_NAMES}
+    olosses = []
+    for t in range(1, steps + 1):
+        nc.nc_step_fwd_bwd(ccfg, params, grads, 0, ids, tgt, tb, ws, loss, bpb)
+        losses.append(float(loss))
+        for k in PARAM_NAMES:
+            nc.nc_adamw_step(master[k], m[k], v[k], grads[k], params[k] if bf16 else None, t, lr, **HP)
+        ref = oracle.step(c, op, inp["ids"], inp["targets"], inp["token_bytes"])
+        olosses.append(ref["loss"])
+        for k in PARAM_NAMES:
+            op[k], om[k], ov[k] = oracle.adamw_step(op[k], ref["grads"][k], om[k], ov[k], t, lr, **HP)
+    assert nc.nc_sync_status(ws) == nc.NC_OK
+    return np.array(losses), np.array(olosses), master, op
+
+
+def test_training_loop_tiny_fp32():
+    losses, olosses, master, op = _loop(CONFIGS["tiny"], CONFIGS["tiny"].batch, 5, 1e-3)
+    np.testing.assert_allclose(losses, olosses, rtol=1e-4)
+    assert np.all(np.diff(olosses) < 0) and np.all(np.diff(losses) < 0), losses  # same batch: loss falls
+    w0 = oracle.to_f64_params(make_inputs(CONFIGS["tiny"])["weights"])
+    for k in PARAM_NAMES:
+        # An Adam step moves every weight by about lr whatever the size of its
+        # gradient, so where a gradient is at rounding level the fp32 and fp64
+        # loops may step opposite ways: the updates must agree closely on the
+        # whole (cosine, median) and differ nowhere by more than 2 lr a step.
+        d_got, d_ref = dev_to_f64(master[k]) - w0[k], op[k] - w0[k]
+        cos = float(np.sum(d_got * d_ref) / np.sqrt(np.sum(d_got ** 2) * np.sum(d_ref ** 2)))
+        diff = np.abs(d_got - d_ref)
+        print(k, "cos", cos, "median", np.median(diff), "p99", np.quantile(diff, 0.99), "max", diff.max())
+        assert cos > 0.999, (k, cos)
+        assert np.median(diff) <= 1e-2 * 1e-3, k
+        assert diff.max() <= 2 * 5 * 1e-3 + 1e-6, k
+
+
+def test_training_loop_small_bf16():
+    losses, olosses, master, op = _loop(CONFIGS["small"], 1, 3, 1e-3)
+    np.testing.assert_allclose(losses, olosses, rtol=3e-3)
+    assert np.all(np.diff(losses) < 0), losses
+    for k in PARAM_NAMES:
+        # Adam steps are ~lr in size whatever the gradient, so a weight whose
+        # gradient is near zero may step either way: compare the updates in
+        # aggregate (cosine) and bound the largest difference by a few lr.
+        d_got = dev_to_f64(master[k]) - oracle.to_f64_params(make_inputs(CONFIGS["small"], 1)["weights"])[k]
+        d_ref = op[k] - oracle.to_f64_params(make_inputs(CONFIGS["small"], 1)["weights"])[k]
+        cos = float(np.sum(d_got * d_ref) / np.sqrt(np.sum(d_got ** 2) * np.sum(d_ref ** 2)))
+        assert cos > 0.95, (k, cos)
+        assert np.max(np.abs(d_got - d_ref)) <= 6 * 1e-3 + 1e-6, k
+
+
+def test_gradient_accumulation_tiny():
+    cfg = CONFIGS["tiny"]
+    inp = make_inputs(cfg)
+    half = cfg.batch // 2
+    assert half >= 1
+    cfg_h = dataclasses.replace(cfg, batch=half)
+    r1 = run_step(cfg_h, inp, batch=half, ids=inp["ids"][:half], targets=inp["targets"][:half])
+    r2 = run_step(cfg_h, inp, batch=half, accumulate=1, grads=r1["grads"], ids=inp["ids"][half:],
+                  targets=inp["targets"][half:])
+    full = oracle.step(cfg, oracle.to_f64_params(inp["weights"]), inp["ids"], inp["targets"], inp["token_bytes"])
+    for k in PARAM_NAMES:
+        # the fp32 reading of the single-step gradient tests (max-rel 1e-3), elementwise
+        assert_close(dev_to_f64(r2["grads"][k]), 2.0 * full["grads"][k], 1e-4, 1e-5, f"accumulated {k}")
