@@ -135,6 +135,55 @@ def cpu_baseline(cfg, inp, budget_tokens=None):
     }
 
 
+ADAMW_BYTES_PER_PARAM = 30   # read p, m, v, g (fp32); write p, m, v (fp32) and the bf16 copy
+
+
+def optimizer_leg(cfg, inp, torch, nc, params, grads, step, s, reps=5):
+    """Times nc_adamw_step over every parameter tensor (HBM-bound: 30 B per
+    parameter in a bf16 configuration, 28 B in fp32), then whole training
+    iterations (forward + backward + AdamW with the bf16 refresh).  Runs after
+    the timed region of the headline metric and leaves it untouched."""
+    names = ("embed", "w_qkv", "w_o", "w_fc", "w_proj", "unembed")
+    bf16 = cfg.dtype == "bf16"
+    master = {k: torch.from_numpy(inp["master"][k]).to("cuda") for k in names}
+    m = {k: torch.zeros_like(master[k]) for k in names}
+    v = {k: torch.zeros_like(master[k]) for k in names}
+    n = sum(master[k].numel() for k in names)
+    hp = dict(beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0)
+
+    def adamw(t):
+        for k in names:
+            nc.nc_adamw_step(master[k], m[k], v[k], grads[k], params[k] if bf16 else None, t, 1e-4,
+                             stream=s, **hp)
+
+    adamw(1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for t in range(2, 2 + reps):
+        adamw(t)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    bpp = ADAMW_BYTES_PER_PARAM if bf16 else ADAMW_BYTES_PER_PARAM - 2
+    gbs = n * bpp / (ms * 1e-3) / 1e9
+    e0.record(s)
+    for t in range(2 + reps, 2 + 2 * reps):
+        step()
+        adamw(t)
+    e1.record(s)
+    torch.cuda.synchronize()
+    it_ms = e0.elapsed_time(e1) / reps
+    for k in names:
+        del master[k], m[k], v[k]
+    log(f"[bench] adamw over {n} parameters: {ms:.3f} ms, {gbs:.0f} GB/s; "
+        f"training iteration {it_ms:.2f} ms ({cfg.tokens / (it_ms * 1e-3):.0f} tok/s)")
+    return {"kernel": "adamw_kernel", "params": n, "bytes_per_param": bpp, "ms": round(ms, 4),
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "launches": 6,
+            "iteration_ms": round(it_ms, 3), "iteration_tokens_per_s": round(cfg.tokens / (it_ms * 1e-3), 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +193,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None)
     ap.add_argument("--roofline-kernel", default=DOMINANT, choices=sorted(FAMILIES))
+    ap.add_argument("--no-optimizer", action="store_true", help="skip the AdamW and full-iteration timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with one 1 GiB device-to-device copy (counter calibration runs)")
     a = ap.parse_args()
@@ -196,6 +246,7 @@ def main():
 
     log(f"[bench] {roof['kernel']}: {roof['launches']} launches, {roof['avg_launch_us']:.1f} us/launch, "
         f"{roof['achieved']} TFLOP/s")
+    opt = None if a.no_optimizer else optimizer_leg(cfg, inp, torch, nc, params, grads, step, s)
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -233,6 +284,7 @@ def main():
         "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "roofline_kernel": {k: roof[k] for k in ("kernel", "launches", "avg_launch_us", "flops_per_launch")},
         "cpu_baseline": base,
+        "optimizer": opt,
     }
     print(json.dumps(out), flush=True)
 

@@ -4,9 +4,8 @@
 // Weight Decay Regularization"): bias-corrected Adam moments and a weight
 // decay applied to the parameter, not the gradient.
 //
-// One pass over HBM, four parameters per thread (16-byte loads of p, m, v, g;
-// 16-byte stores of p, m, v; one 8-byte store of the bf16 copy), a grid-stride
-// loop sized to the chip.  The bias corrections are folded into two scalars
+// One pass over HBM: 16-byte loads of p, m, v, g, 16-byte stores of p, m, v
+// and an 8-byte store of the bf16 copy per four parameters.  The bias corrections are folded into two scalars
 // on the host in double precision.  Bound by HBM bandwidth (28-30 bytes per
 // parameter).
 #include "common.h"
@@ -30,27 +29,58 @@ __device__ __forceinline__ float adamw1(float p, float& m, float& v, float g, co
   return p * a.decay - a.lr * mh / (sqrtf(vh) + a.eps);
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kAdamWUnroll = 2;  // float4 groups per thread, all loads issued before the math
+
+// Each thread owns kAdamWUnroll float4 groups 256 apart, so every load of a
+// wave is a contiguous 1 KiB.  The data is touched once: loads and stores are
+// nontemporal, so the stream does not evict what the step keeps in L2/MALL.
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ P, float* __restrict__ Mo,
                                                     float* __restrict__ Vo, const float* __restrict__ G,
                                                     bf16* __restrict__ W, int64_t n, AdamWArgs a) {
   const int64_t n4 = n >> 2;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    float4 p = reinterpret_cast<const float4*>(P)[i];
-    float4 m = reinterpret_cast<const float4*>(Mo)[i];
-    float4 v = reinterpret_cast<const float4*>(Vo)[i];
-    const float4 g = reinterpret_cast<const float4*>(G)[i];
-    p.x = adamw1(p.x, m.x, v.x, g.x, a);
-    p.y = adamw1(p.y, m.y, v.y, g.y, a);
-    p.z = adamw1(p.z, m.z, v.z, g.z, a);
-    p.w = adamw1(p.w, m.w, v.w, g.w, a);
-    reinterpret_cast<float4*>(P)[i] = p;
-    reinterpret_cast<float4*>(Mo)[i] = m;
-    reinterpret_cast<float4*>(Vo)[i] = v;
-    if (W) reinterpret_cast<uint2*>(W)[i] = make_uint2(pack_bf16x2(p.x, p.y), pack_bf16x2(p.z, p.w));
+  f32x4* P4 = reinterpret_cast<f32x4*>(P);
+  f32x4* M4 = reinterpret_cast<f32x4*>(Mo);
+  f32x4* V4 = reinterpret_cast<f32x4*>(Vo);
+  const f32x4* G4 = reinterpret_cast<const f32x4*>(G);
+  u32x2* W2 = reinterpret_cast<u32x2*>(W);
+  const int64_t stride = (int64_t)gridDim.x * 256 * kAdamWUnroll;
+  for (int64_t i0 = (int64_t)blockIdx.x * 256 * kAdamWUnroll + threadIdx.x; i0 < n4; i0 += stride) {
+    f32x4 p[kAdamWUnroll], m[kAdamWUnroll], v[kAdamWUnroll], g[kAdamWUnroll];
+#pragma unroll
+    for (int u = 0; u < kAdamWUnroll; ++u) {
+      const int64_t i = i0 + u * 256;
+      if (i < n4) {
+        p[u] = __builtin_nontemporal_load(P4 + i);
+        m[u] = __builtin_nontemporal_load(M4 + i);
+        v[u] = __builtin_nontemporal_load(V4 + i);
+        g[u] = __builtin_nontemporal_load(G4 + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kAdamWUnroll; ++u) {
+      const int64_t i = i0 + u * 256;
+      if (i < n4) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float mc = m[u][c], vc = v[u][c];
+          p[u][c] = adamw1(p[u][c], mc, vc, g[u][c], a);
+          m[u][c] = mc;
+          v[u][c] = vc;
+        }
+        __builtin_nontemporal_store(p[u], P4 + i);
+        __builtin_nontemporal_store(m[u], M4 + i);
+        __builtin_nontemporal_store(v[u], V4 + i);
+        if (W) {
+          const u32x2 w = {pack_bf16x2(p[u][0], p[u][1]), pack_bf16x2(p[u][2], p[u][3])};
+          __builtin_nontemporal_store(w, W2 + i);
+        }
+      }
+    }
   }
   // tail (n not a multiple of 4)
-  for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+  for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     float m = Mo[i], v = Vo[i];
     const float p = adamw1(P[i], m, v, G[i], a);
     P[i] = p;
@@ -80,7 +110,9 @@ int adamw_step(float* P, float* M, float* V, const float* G, void* W, int64_t n,
   a.inv_bc1 = (float)(1.0 / (1.0 - std::pow((double)beta1, (double)t)));
   a.inv_bc2 = (float)(1.0 / (1.0 - std::pow((double)beta2, (double)t)));
   a.gscale = gscale;
-  const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(std::max<int64_t>(n >> 2, 1), 256), 256 * 16);
+  // one pass: a workgroup per 256 * kAdamWUnroll float4 groups (the loop only strides past 2^30 groups)
+  const unsigned blocks =
+      (unsigned)std::min<int64_t>(cdiv(std::max<int64_t>(n >> 2, 1), 256 * kAdamWUnroll), int64_t(1) << 30);
   adamw_kernel<<<blocks, 256, 0, s>>>(P, M, V, G, static_cast<bf16*>(W), n, a);
   return check_launch("adamw_kernel");
 }

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 from gpu_util import DEV, PARAM_NAMES, assert_close, bf16_tensor_from_bits, dev_to_f64, run_step, to_dev
-from synthetic import CONFIGS, make_inputs, to_bf16_bits, bf16_bits_to_f32
+from synthetic import CONFIGS, make_inputs, make_tokens, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -152,3 +152,94 @@ def test_gradient_accumulation_tiny():
     for k in PARAM_NAMES:
         # the fp32 reading of the single-step gradient tests (max-rel 1e-3), elementwise
         assert_close(dev_to_f64(r2["grads"][k]), 2.0 * full["grads"][k], 1e-4, 1e-5, f"accumulated {k}")
+
+
+def _alloc_loop_state(nc, cfg, inp):
+    bf16 = cfg.dtype == "bf16"
+    master = {k: to_dev(inp["weights"][k], torch.float32) for k in PARAM_NAMES}
+    st = dict(master=master,
+              m={k: torch.zeros_like(master[k]) for k in PARAM_NAMES},
+              v={k: torch.zeros_like(master[k]) for k in PARAM_NAMES},
+              params={k: bf16_tensor_from_bits(inp["weights_bf16"][k]) for k in PARAM_NAMES} if bf16 else master,
+              grads={k: torch.empty_like(master[k]) for k in PARAM_NAMES},
+              ws=torch.empty(nc.nc_step_workspace_bytes(nc.make_config(cfg)), dtype=torch.uint8, device=DEV),
+              loss=torch.empty(1, device=DEV), bpb=torch.empty(1, device=DEV),
+              tb=torch.from_numpy(inp["token_bytes"]).to(DEV))
+    return st
+
+
+def _accumulated_iteration(nc, ccfg, st, S_parts, t, lr, bf16):
+    """One optimizer step over len(S_parts) micro-batches: the first
+    overwrites the gradients, the rest accumulate; AdamW then scales the sum
+    by 1/len(S_parts), which gives the gradient of the mean over the whole
+    batch (every micro-batch has the same number of tokens)."""
+    losses = []
+    for j, S in enumerate(S_parts):
+        ids = torch.from_numpy(np.ascontiguousarray(S[:, :-1])).to(DEV)
+        tgt = torch.from_numpy(np.ascontiguousarray(S[:, 1:])).to(DEV)
+        nc.nc_step_fwd_bwd(ccfg, st["params"], st["grads"], 1 if j else 0, ids, tgt, st["tb"], st["ws"],
+                           st["loss"], st["bpb"])
+        losses.append((float(st["loss"]), float(st["bpb"])))
+    for k in PARAM_NAMES:
+        nc.nc_adamw_step(st["master"][k], st["m"][k], st["v"][k], st["grads"][k],
+                         st["params"][k] if bf16 else None, t, lr, grad_scale=1.0 / len(S_parts), **HP)
+    return losses
+
+
+def test_accumulated_training_loop_tiny_fp32():
+    """Three optimizer steps, each over two half batches accumulated on the
+    GPU, against the oracle taking the same steps on the whole batch."""
+    nc = _nc()
+    cfg = CONFIGS["tiny"]
+    inp = make_inputs(cfg)
+    half = cfg.batch // 2
+    cfg_h = dataclasses.replace(cfg, batch=half)
+    ccfg = nc.make_config(cfg_h)
+    st = _alloc_loop_state(nc, cfg_h, inp)
+    op = oracle.to_f64_params(inp["weights"])
+    om = {k: np.zeros_like(op[k]) for k in PARAM_NAMES}
+    ov = {k: np.zeros_like(op[k]) for k in PARAM_NAMES}
+    lr = 1e-3
+    for t in range(1, 4):
+        S = make_tokens(cfg, seed=7000 + t)
+        got = _accumulated_iteration(nc, ccfg, st, [S[:half], S[half:]], t, lr, False)
+        ref = oracle.step(cfg, op, np.ascontiguousarray(S[:, :-1]), np.ascontiguousarray(S[:, 1:]), inp["token_bytes"])
+        assert np.mean([g[0] for g in got]) == pytest.approx(ref["loss"], rel=1e-4)
+        for k in PARAM_NAMES:
+            op[k], om[k], ov[k] = oracle.adamw_step(op[k], ref["grads"][k], om[k], ov[k], t, lr, **HP)
+    assert nc.nc_sync_status(st["ws"]) == nc.NC_OK
+    w0 = oracle.to_f64_params(inp["weights"])
+    for k in PARAM_NAMES:
+        d_got, d_ref = dev_to_f64(st["master"][k]) - w0[k], op[k] - w0[k]
+        cos = float(np.sum(d_got * d_ref) / np.sqrt(np.sum(d_got ** 2) * np.sum(d_ref ** 2)))
+        assert cos > 0.999, (k, cos)
+        assert np.abs(d_got - d_ref).max() <= 2 * 3 * lr + 1e-6, k
+
+
+def test_loss_curve_small_bf16():
+    """Forty optimizer steps (two accumulated micro-batches each) on fresh
+    Zipf(1.1) batches.  The tokens are drawn independently, so no model can
+    do better on new data than the entropy of the Zipf source; training must
+    take the loss from above ln V to below it, stay above that entropy, keep
+    bpb = loss / (ln 2 * 4.8), and stay finite throughout."""
+    nc = _nc()
+    cfg = CONFIGS["small"]
+    inp = make_inputs(cfg)
+    ccfg = nc.make_config(cfg)
+    st = _alloc_loop_state(nc, cfg, inp)
+    r = np.arange(1, cfg.vocab + 1, dtype=np.float64) ** -cfg.zipf_s
+    p = r / r.sum()
+    entropy = float(-(p * np.log(p)).sum())
+    curve = []
+    for t in range(1, 41):
+        parts = [make_tokens(cfg, seed=9000 + 2 * t + j) for j in range(2)]
+        losses = _accumulated_iteration(nc, ccfg, st, parts, t, 3e-3, True)
+        for lo, bp in losses:
+            assert np.isfinite(lo) and bp == pytest.approx(lo / (np.log(2.0) * cfg.bytes_per_token), rel=1e-5)
+        curve.append(np.mean([lo for lo, _ in losses]))
+    assert nc.nc_sync_status(st["ws"]) == nc.NC_OK
+    print("loss curve", np.round(curve, 3).tolist(), "entropy", entropy, "ln V", np.log(cfg.vocab))
+    assert curve[0] > np.log(cfg.vocab) - 0.5
+    tail = float(np.mean(curve[-5:]))
+    assert tail < np.log(cfg.vocab) - 1.0, curve
+    assert tail > entropy - 0.1, curve
