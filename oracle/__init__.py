@@ -40,3 +40,4 @@ from .model import (  # noqa: F401
     to_f64_params,
 )
 from .optim import adamw_step  # noqa: F401
+from .decode import decode_attention, prefix_logits  # noqa: F401
