@@ -73,7 +73,7 @@ void probe_end(int family, hipStream_t s, double flops) {
 }  // namespace nc
 
 extern "C" int nc_probe_start(int family, int max_launches) {
-  NC_REQUIRE(family >= NC_PROBE_OFF && family <= NC_PROBE_ATTN_DKV, NC_ERR_INVALID_ARG, "probe: unknown family %d",
+  NC_REQUIRE(family >= NC_PROBE_OFF && family <= NC_PROBE_DECODE_ATTN, NC_ERR_INVALID_ARG, "probe: unknown family %d",
              family);
   NC_REQUIRE(max_launches >= 0 && max_launches <= (1 << 20), NC_ERR_INVALID_ARG, "probe: max_launches %d",
              max_launches);

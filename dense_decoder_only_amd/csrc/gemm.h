@@ -38,6 +38,9 @@ struct GemmDesc {
   float* xpart = nullptr;
   float* xztgt = nullptr;
   int xv0 = 0;
+  // capc > 0: C (fp32) = capc tanh(acc / capc), the logit softcap; only for
+  // the small-M form (bf16, x W^T, M <= 128), which decoding uses.
+  float capc = 0.f;
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);

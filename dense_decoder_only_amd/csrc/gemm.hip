@@ -1055,6 +1055,168 @@ int split_k_per(int64_t K, int splits) { return (int)(cdiv(cdiv(K, splits), BK) 
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// ---------------------------------------------------------------------------
+// Small-M products (decoding: one new token per sequence), C[M, N] =
+// A[M, K] W[N, K]^T with M <= 128 and both operands K-contiguous.  The work
+// is reading W once from HBM (2 N K bytes against 2 M N K FLOPs), so the
+// kernel is organised around that stream, not around MFMA reuse:
+//  * a block owns 32 rows of W (32 output columns) and every row of A; its
+//    8 waves take the 64-wide k-chunks in turn (chunk c to wave c mod 8) and
+//    add their partial sums in LDS in a fixed order (deterministic);
+//  * per chunk, lane l reads 64 contiguous bytes of W row n0 + l mod 32 at
+//    k offset 32 (l / 32); the next chunk's W is loaded before the current
+//    chunk's MFMAs;
+//  * the MFMA k-slots are permuted the same way for both operands: MFMA s of
+//    a chunk covers k = 8 s + {0..7} (lanes 0-31) and 32 + 8 s + {0..7}
+//    (lanes 32-63), so the four MFMAs sum all 64;
+//  * the product is issued as C^T (W fragment first): lane l ends with output
+//    column group n0 + 8 (q / 4) + 4 (l / 32) + q mod 4 of token row l mod 32.
+// A (at most 128 x K bf16) stays in L2 across the blocks that re-read it.
+// ---------------------------------------------------------------------------
+constexpr int SK_WAVES = 8, SK_MMAX = 128;
+enum { E_SOFTCAP_F32 = 10 };  // small-M only: C (fp32) = c tanh(acc / c)
+
+struct SkinnyParams {
+  const bf16* A;
+  int64_t lda;
+  const bf16* W;
+  int64_t ldw;
+  void* C;
+  int64_t ldc;
+  int M, N, K;
+  float capc, inv_capc;
+};
+
+template <int EPI>
+__device__ __forceinline__ void skinny_store2(const SkinnyParams& p, int m, int n, float v0, float v1) {
+  const int64_t off = (int64_t)m * p.ldc + n;
+  if constexpr (EPI == E_STORE_F32) {
+    *reinterpret_cast<float2*>(static_cast<float*>(p.C) + off) = make_float2(v0, v1);
+  } else if constexpr (EPI == E_ACC_F32) {
+    float2* c = reinterpret_cast<float2*>(static_cast<float*>(p.C) + off);
+    const float2 o = *c;
+    *c = make_float2(o.x + v0, o.y + v1);
+  } else if constexpr (EPI == E_STORE_BF16) {
+    *reinterpret_cast<uint32_t*>(static_cast<bf16*>(p.C) + off) = pack_bf16x2(v0, v1);
+  } else if constexpr (EPI == E_RELU2_SQ) {
+    const float a = fmaxf(v0, 0.f), b = fmaxf(v1, 0.f);
+    *reinterpret_cast<uint32_t*>(static_cast<bf16*>(p.C) + off) = pack_bf16x2(a * a, b * b);
+  } else {  // E_SOFTCAP_F32
+    *reinterpret_cast<float2*>(static_cast<float*>(p.C) + off) =
+        make_float2(softcap_of(v0, p.capc, p.inv_capc), softcap_of(v1, p.capc, p.inv_capc));
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny_kernel(SkinnyParams p) {
+  __shared__ float red[SK_WAVES][16][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 31, h = lane >> 5;
+  const int n0 = blockIdx.x * 32;
+  const int nmt = (p.M + 31) >> 5;
+  f32x16 acc[SK_MMAX / 32];
+#pragma unroll
+  for (int i = 0; i < SK_MMAX / 32; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
+  const bf16* wrow = p.W + (int64_t)(n0 + r) * p.ldw + 32 * h;
+  const int nch = p.K >> 6;
+  bf16x8_t wc[4], wn[4];
+  int c = wave;
+  if (c < nch) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) wc[s] = *reinterpret_cast<const bf16x8_t*>(wrow + (c << 6) + 8 * s);
+  }
+  for (; c < nch; c += SK_WAVES) {
+    const bool more = c + SK_WAVES < nch;
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        wn[s] = *reinterpret_cast<const bf16x8_t*>(wrow + ((c + SK_WAVES) << 6) + 8 * s);
+    }
+    const int kc = (c << 6) + 32 * h;
+#pragma unroll
+    for (int mt = 0; mt < SK_MMAX / 32; ++mt) {
+      if (mt < nmt) {
+        const int m = mt * 32 + r;
+        bf16x8_t x[4];
+        if (m < p.M) {
+          const bf16* xr = p.A + (int64_t)m * p.lda + kc;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) x[s] = *reinterpret_cast<const bf16x8_t*>(xr + 8 * s);
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) x[s] = bf16x8_t{};
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wc[s], x[s], acc[mt], 0, 0, 0);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wc[s] = wn[s];
+    }
+  }
+  // fixed-order reduction over the waves, one 32 x 32 tile at a time
+  const int t = threadIdx.x, pl = t & 63, q0 = 2 * (t >> 6);
+  const int n = n0 + 8 * (q0 >> 2) + 4 * (pl >> 5) + (q0 & 3);
+#pragma unroll
+  for (int mt = 0; mt < SK_MMAX / 32; ++mt) {
+    if (mt < nmt) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) red[wave][q][lane] = acc[mt][q];
+      __syncthreads();
+      float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < SK_WAVES; ++w) {
+        v0 += red[w][q0][pl];
+        v1 += red[w][q0 + 1][pl];
+      }
+      const int m = mt * 32 + (pl & 31);
+      if (m < p.M) skinny_store2<EPI>(p, m, n, v0, v1);
+      __syncthreads();
+    }
+  }
+}
+
+// Small-M form if the shapes and epilogue allow it; returns false to let the
+// caller take the general path.
+bool skinny_ok(const GemmDesc& g) {
+  if (g.dtype != NC_BF16 || g.transA != 0 || g.transB != 1 || g.xent) return false;
+  if (g.M < 1 || g.M > SK_MMAX || g.N % 32 != 0 || g.K % 64 != 0) return false;
+  if (g.lda % 8 != 0 || g.ldb % 8 != 0 || g.ldc % 2 != 0) return false;
+  if (!aligned16(g.A) || !aligned16(g.B) || (reinterpret_cast<uintptr_t>(g.C) & 7u) != 0) return false;
+  if (g.capc > 0.f) return g.cdt == NC_F32 && g.beta == 0.f && g.epi == NC_EPI_STORE;
+  if (g.epi == NC_EPI_RELU2_SQ) return g.cdt == NC_BF16;
+  return g.epi == NC_EPI_STORE;
+}
+
+int gemm_skinny(const GemmDesc& g, hipStream_t s) {
+  SkinnyParams p;
+  p.A = static_cast<const bf16*>(g.A);
+  p.lda = g.lda;
+  p.W = static_cast<const bf16*>(g.B);
+  p.ldw = g.ldb;
+  p.C = g.C;
+  p.ldc = g.ldc;
+  p.M = (int)g.M;
+  p.N = (int)g.N;
+  p.K = (int)g.K;
+  p.capc = g.capc;
+  p.inv_capc = g.capc > 0.f ? 1.f / g.capc : 0.f;
+  const unsigned blocks = (unsigned)(g.N / 32);
+  const double bytes = 2.0 * (double)g.N * g.K + 2.0 * (double)g.M * g.K +
+                       (double)g.M * g.N * (g.cdt == NC_BF16 ? 2 : (g.beta == 1.f ? 8 : 4));
+  probe_begin(NC_PROBE_GEMM_SKINNY, s);
+  if (g.capc > 0.f) gemm_skinny_kernel<E_SOFTCAP_F32><<<blocks, SK_WAVES * 64, 0, s>>>(p);
+  else if (g.epi == NC_EPI_RELU2_SQ) gemm_skinny_kernel<E_RELU2_SQ><<<blocks, SK_WAVES * 64, 0, s>>>(p);
+  else if (g.cdt == NC_BF16) gemm_skinny_kernel<E_STORE_BF16><<<blocks, SK_WAVES * 64, 0, s>>>(p);
+  else if (g.beta == 1.f) gemm_skinny_kernel<E_ACC_F32><<<blocks, SK_WAVES * 64, 0, s>>>(p);
+  else gemm_skinny_kernel<E_STORE_F32><<<blocks, SK_WAVES * 64, 0, s>>>(p);
+  probe_end(NC_PROBE_GEMM_SKINNY, s, bytes);
+  return check_launch("gemm_skinny_kernel");
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -1132,6 +1294,10 @@ int gemm(const GemmDesc& g, hipStream_t stream) {
   if (g.beta == 1.f)
     NC_REQUIRE(g.cdt == NC_F32 && g.epi == NC_EPI_STORE, NC_ERR_INVALID_ARG,
                "gemm: beta = 1 needs an fp32 C and the plain store epilogue");
+  if (g.capc > 0.f)
+    NC_REQUIRE(skinny_ok(g), NC_ERR_UNSUPPORTED, "gemm: the softcap epilogue is for bf16 products with M <= %d",
+               SK_MMAX);
+  if (skinny_ok(g)) return gemm_skinny(g, stream);
 
   if (g.dtype == NC_F32) {
     NC_REQUIRE(g.cdt == NC_F32, NC_ERR_INVALID_ARG, "gemm: fp32 operands need an fp32 C");

@@ -1,0 +1,559 @@
+// Inference with a key/value cache: prefill of a prompt and one-token decode
+// steps of the same model as the training step (release-news page
+// "Karpathy再放大招…", section 技術細節與問答: multi-query attention, rotary
+// embeddings, QK norm, logit softcap; the page's serving engine keeps such a
+// cache).  By causality, the logits at a position depend only on the tokens
+// up to it.  Keeping each layer's post-RoPE, post-norm key and its value for
+// every earlier position therefore lets a new position be computed without
+// recomputing the prefix.
+//
+// Supported: bf16 weights, head_dim 128, one K/V head, at most 16 query heads
+// and 128 sequences.
+//
+// Cache layout (bf16, caller-owned): [L][2][B][max_len][128], keys then values
+// per layer, position-major within a sequence, so one position's key is one
+// contiguous 256-byte row.
+//
+// Decode is bound by HBM: every step reads all projection weights once
+// (small-M GEMMs, gemm.hip) and each sequence's cached keys and values once
+// (the attention below).
+#include "common.h"
+#include "gemm.h"
+#include "ops.h"
+
+#include <cmath>
+
+namespace nc {
+namespace {
+
+constexpr int kHd = 128;    // head_dim of the inference path
+constexpr int kChunk = 64;  // cached positions per decode-attention wave
+constexpr int kMaxHeads = 16;
+constexpr int kMaxSeqs = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 16);
+  return v;
+}
+
+__device__ __forceinline__ void unpack8(const uint4& u, float (&f)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ void unpack4(uint2 u, float (&f)[4]) {
+  f[0] = __uint_as_float(u.x << 16);
+  f[1] = __uint_as_float(u.x & 0xffff0000u);
+  f[2] = __uint_as_float(u.y << 16);
+  f[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+
+// RoPE + per-head RMS norm of one new token per sequence, at its own
+// position pos[b]; the key and the value are appended to the cache at that
+// position, the query heads go to qhat [B, H, 128].  A 16-lane group per head
+// (lane j owns the pairs (i, i + 64), i = 4 j .. 4 j + 3); the angles are
+// computed in fp64 and rounded to fp32 as for the training table, so a
+// position gets the same rotation in both paths.  A position outside
+// [0, max_len) raises the flag and leaves that sequence's outputs unwritten.
+__global__ __launch_bounds__(256) void decode_rope_append_kernel(const bf16* __restrict__ qkv,
+                                                                 const int32_t* __restrict__ pos, int H, double base,
+                                                                 float eps, int max_len, bf16* __restrict__ qhat,
+                                                                 bf16* __restrict__ kc, bf16* __restrict__ vc,
+                                                                 int32_t* __restrict__ flag) {
+  const int b = blockIdx.x;
+  const int p = pos[b];
+  if (p < 0 || p >= max_len) {
+    if (threadIdx.x == 0 && flag) *flag = 1;
+    return;
+  }
+  const int j = threadIdx.x & 15;
+  const bf16* row = qkv + (int64_t)b * (H + 2) * kHd;
+  const int64_t cache_row = ((int64_t)b * max_len + p) * kHd;
+  for (int head = threadIdx.x >> 4; head < H + 2; head += 16) {
+    const bf16* x = row + head * kHd;
+    if (head == H + 1) {  // value: copied as is
+      *reinterpret_cast<uint4*>(vc + cache_row + 8 * j) = *reinterpret_cast<const uint4*>(x + 8 * j);
+      continue;
+    }
+    float a[4], c[4];
+    unpack4(*reinterpret_cast<const uint2*>(x + 4 * j), a);
+    unpack4(*reinterpret_cast<const uint2*>(x + 64 + 4 * j), c);
+    float ya[4], yb[4], ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double th = (double)p * pow(base, -2.0 * (double)(4 * j + e) / (double)kHd);
+      const float cs = (float)cos(th), sn = (float)sin(th);
+      ya[e] = a[e] * cs - c[e] * sn;
+      yb[e] = a[e] * sn + c[e] * cs;
+      ss += ya[e] * ya[e] + yb[e] * yb[e];
+    }
+    const float r = 1.f / sqrtf(sum16(ss) / (float)kHd + eps);
+    bf16* dst = head < H ? qhat + ((int64_t)b * H + head) * kHd : kc + cache_row;
+    *reinterpret_cast<uint2*>(dst + 4 * j) =
+        make_uint2(pack_bf16x2(ya[0] * r, ya[1] * r), pack_bf16x2(ya[2] * r, ya[3] * r));
+    *reinterpret_cast<uint2*>(dst + 64 + 4 * j) =
+        make_uint2(pack_bf16x2(yb[0] * r, yb[1] * r), pack_bf16x2(yb[2] * r, yb[3] * r));
+  }
+}
+
+__device__ __forceinline__ int seq_len_of(const int32_t* lens, int b, int len_add, int max_len) {
+  const int n = lens[b] + len_add;
+  return n < 0 ? 0 : (n > max_len ? max_len : n);
+}
+
+// Decode attention, split over the cache: block (chunk, b) is one wave over
+// positions 64 chunk .. 64 chunk + 63 of sequence b, for all H query heads
+// at once (they share the one K/V head, so each cached row is read once).
+//  scores: lane = position; its 256-byte key row is held in registers and
+//          dotted with each head's query (from LDS, broadcast) by bf16 dot2
+//          instructions with fp32 accumulation;
+//  softmax: per head over the wave's 64 positions, in base 2 (scores are
+//          pre-multiplied by scale log2 e);
+//  values:  lane = (8 dims, one of 4 position phases); each value row is
+//          read as 16-byte pieces and scaled by the probabilities (LDS);
+//          the 4 phases are summed by shuffles.
+// Writes the unnormalised partial output and (max, sum) per head; chunks at or
+// beyond the sequence's length do nothing.
+__global__ __launch_bounds__(64) void decode_attn_split_kernel(const bf16* __restrict__ q,
+                                                               const bf16* __restrict__ kc,
+                                                               const bf16* __restrict__ vc,
+                                                               const int32_t* __restrict__ lens, int len_add, int H,
+                                                               int max_len, float scale_log2,
+                                                               float* __restrict__ part_o,
+                                                               float* __restrict__ part_ml) {
+  __shared__ uint4 qs[kMaxHeads][kHd / 8];
+  __shared__ float ps[kChunk][kMaxHeads + 1];
+  const int chunk = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int nch = gridDim.x;
+  const int len = seq_len_of(lens, b, len_add, max_len);
+  const int t0 = chunk * kChunk;
+  if (t0 >= len) return;
+  const uint4* q4 = reinterpret_cast<const uint4*>(q + (int64_t)b * H * kHd);
+  for (int i = lane; i < H * (kHd / 8); i += 64) qs[i >> 4][i & 15] = q4[i];
+  const int64_t seq = (int64_t)b * max_len * kHd;
+  const int t = t0 + lane;
+  const bool valid = t < len;
+  uint4 kr[kHd / 8];
+  if (valid) {
+    const uint4* k4 = reinterpret_cast<const uint4*>(kc + seq + (int64_t)t * kHd);
+#pragma unroll
+    for (int i = 0; i < kHd / 8; ++i) kr[i] = k4[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < kHd / 8; ++i) kr[i] = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  float mh[kMaxHeads], lh[kMaxHeads];
+#pragma unroll
+  for (int h = 0; h < kMaxHeads; ++h) {
+    if (h < H) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < kHd / 8; ++i) {
+        const uint4 qq = qs[h][i];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qq.x), __builtin_bit_cast(bf16x2_t, kr[i].x),
+                                              acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qq.y), __builtin_bit_cast(bf16x2_t, kr[i].y),
+                                              acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qq.z), __builtin_bit_cast(bf16x2_t, kr[i].z),
+                                              acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qq.w), __builtin_bit_cast(bf16x2_t, kr[i].w),
+                                              acc, false);
+      }
+      const float s = valid ? acc * scale_log2 : -INFINITY;
+      const float m = wave_max(s);  // finite: position t0 < len is valid
+      const float e = valid ? __builtin_amdgcn_exp2f(s - m) : 0.f;
+      mh[h] = m;
+      lh[h] = wave_sum(e);
+      ps[lane][h] = e;
+    }
+  }
+  __syncthreads();
+  const int d8 = 8 * (lane & 15), ph = lane >> 4;
+  float o[kMaxHeads][8];
+#pragma unroll
+  for (int h = 0; h < kMaxHeads; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  const int nvalid = min(kChunk, len - t0);
+  for (int i = ph; i < nvalid; i += 4) {
+    float v[8];
+    unpack8(*reinterpret_cast<const uint4*>(vc + seq + (int64_t)(t0 + i) * kHd + d8), v);
+#pragma unroll
+    for (int h = 0; h < kMaxHeads; ++h) {
+      if (h < H) {
+        const float pw = ps[i][h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] += pw * v[e];
+      }
+    }
+  }
+  const int64_t pbase = ((int64_t)b * nch + chunk) * H;
+#pragma unroll
+  for (int h = 0; h < kMaxHeads; ++h) {
+    if (h < H) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[h][e] += __shfl_xor(o[h][e], 16, 64);
+        o[h][e] += __shfl_xor(o[h][e], 32, 64);
+      }
+      if (ph == 0) {
+        float4* dst = reinterpret_cast<float4*>(part_o + (pbase + h) * kHd + d8);
+        dst[0] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+        dst[1] = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+      }
+      if (lane == 0) {
+        part_ml[2 * (pbase + h)] = mh[h];
+        part_ml[2 * (pbase + h) + 1] = lh[h];
+      }
+    }
+  }
+}
+
+// Combine the chunks of each (sequence, head) in increasing chunk order:
+// o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c, M = max_c m_c.  One
+// thread per output element; a sequence of length 0 gets zeros.
+__global__ __launch_bounds__(kHd) void decode_attn_combine_kernel(const float* __restrict__ part_o,
+                                                                  const float* __restrict__ part_ml,
+                                                                  const int32_t* __restrict__ lens, int len_add,
+                                                                  int H, int max_len, int nch,
+                                                                  bf16* __restrict__ out) {
+  const int h = blockIdx.x, b = blockIdx.y, dim = threadIdx.x;
+  const int len = seq_len_of(lens, b, len_add, max_len);
+  const int used = (int)cdiv(len, kChunk);
+  bf16* dst = out + ((int64_t)b * H + h) * kHd + dim;
+  if (used == 0) {
+    *dst = 0;
+    return;
+  }
+  const int64_t base = (int64_t)b * nch * H + h;
+  float M = -INFINITY;
+  for (int c = 0; c < used; ++c) M = fmaxf(M, part_ml[2 * (base + (int64_t)c * H)]);
+  float L = 0.f, O = 0.f;
+  for (int c = 0; c < used; ++c) {
+    const int64_t i = base + (int64_t)c * H;
+    const float w = __builtin_amdgcn_exp2f(part_ml[2 * i] - M);
+    L += w * part_ml[2 * i + 1];
+    O += w * part_o[i * kHd + dim];
+  }
+  *dst = f2bf(O / L);
+}
+
+// Prefill: copy each token's post-norm key and its value (columns H 128 and
+// (H + 1) 128 of the packed qkv rows) into the cache; 16 bytes per thread.
+__global__ __launch_bounds__(256) void cache_fill_kernel(const bf16* __restrict__ qkv, int64_t M, int T, int H,
+                                                         bf16* __restrict__ kc, bf16* __restrict__ vc, int max_len) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tok = i >> 5;
+  if (tok >= M) return;
+  const int c = (int)(i & 31);
+  const int64_t b = tok / T, t = tok - b * T;
+  const uint4 v = *reinterpret_cast<const uint4*>(qkv + tok * (H + 2) * kHd + (int64_t)(H + (c >> 4)) * kHd +
+                                                  8 * (c & 15));
+  bf16* dst = (c < 16 ? kc : vc) + (b * max_len + t) * kHd + 8 * (c & 15);
+  *reinterpret_cast<uint4*>(dst) = v;
+}
+
+// rows_out[b] = x[b T + T - 1] (fp32 rows of width d): the last position of
+// every prompt.
+__global__ __launch_bounds__(256) void last_rows_kernel(const float* __restrict__ x, int B, int T, int d,
+                                                        float* __restrict__ rows_out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)B * d) return;
+  const int64_t b = i / d, c = i - b * d;
+  rows_out[i] = x[(b * T + T - 1) * d + c];
+}
+
+int validate_infer(const nc_config* c, int max_len) {
+  NC_REQUIRE(c, NC_ERR_INVALID_ARG, "infer: null config");
+  NC_REQUIRE(c->dtype == NC_BF16 && c->head_dim == kHd, NC_ERR_UNSUPPORTED,
+             "infer: the cache path needs bf16 and head_dim 128");
+  NC_REQUIRE(c->n_kv_head == 1, NC_ERR_INVALID_ARG, "infer: n_kv_head must be 1");
+  NC_REQUIRE(c->n_layer > 0 && c->n_head > 0 && c->batch > 0 && c->seq_len > 0 && c->vocab > 0, NC_ERR_INVALID_ARG,
+             "infer: bad shape");
+  NC_REQUIRE((int64_t)c->n_head * kHd == c->d_model, NC_ERR_INVALID_ARG, "infer: n_head * head_dim != d_model");
+  NC_REQUIRE(c->n_head <= kMaxHeads, NC_ERR_UNSUPPORTED, "infer: at most %d query heads", kMaxHeads);
+  NC_REQUIRE(c->batch <= kMaxSeqs, NC_ERR_UNSUPPORTED, "infer: at most %d sequences", kMaxSeqs);
+  NC_REQUIRE(c->d_model % 64 == 0 && c->d_ff % 64 == 0 && c->vocab % 32 == 0, NC_ERR_UNSUPPORTED,
+             "infer: d_model and d_ff must be multiples of 64, vocab of 32");
+  NC_REQUIRE(max_len >= c->seq_len, NC_ERR_INVALID_ARG, "infer: max_len %d is below the prompt length %d", max_len,
+             c->seq_len);
+  return NC_OK;
+}
+
+struct InferWs {
+  int32_t* flag;
+  // decode (one token per sequence)
+  float *dx, *drstd;
+  void *da, *dqkv, *dq, *dout, *dm, *da2, *dh;
+  float *part_o, *part_ml;
+  // prefill (B T tokens)
+  float *x, *rstd, *rstd_q, *rstd_k, *lse, *table, *xl;
+  void *a, *qkv, *o, *a2, *hl;
+  void* gemm_ws;
+  size_t gemm_ws_bytes;
+};
+
+size_t decode_part_floats(int B, int H, int max_len) { return (size_t)B * cdiv(max_len, kChunk) * H; }
+
+size_t carve_infer(const nc_config* c, int max_len, InferWs* w, void* base) {
+  const int64_t B = c->batch, T = c->seq_len, M = B * T;
+  const int64_t d = c->d_model, H = c->n_head, F = c->d_ff, Q = (H + 2) * kHd, HD = H * kHd;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes, 256);
+    return o;
+  };
+  char* p = static_cast<char*>(base);
+  auto at = [&](size_t o) -> void* { return p ? p + o : nullptr; };
+  const size_t o_flag = take(4);
+  const size_t o_dx = take(B * d * 4), o_dr = take(B * 4), o_da = take(B * d * 2), o_dqkv = take(B * Q * 2),
+               o_dq = take(B * HD * 2), o_do = take(B * HD * 2), o_dm = take(B * d * 2), o_da2 = take(B * F * 2),
+               o_dh = take(B * d * 2);
+  const size_t parts = decode_part_floats((int)B, (int)H, max_len);
+  const size_t o_po = take(parts * kHd * 4), o_pml = take(parts * 2 * 4);
+  const size_t o_x = take(M * d * 4), o_r = take(M * 4), o_rq = take(M * H * 4), o_rk = take(M * 4),
+               o_lse = take(M * H * 4), o_tab = take((size_t)T * kHd * 4), o_xl = take(B * d * 4),
+               o_a = take(M * d * 2), o_qkv = take(M * Q * 2), o_o = take(M * HD * 2), o_a2 = take(M * F * 2),
+               o_hl = take(B * d * 2);
+  const size_t gb = std::max(gemm_workspace_bytes(M, d, HD), gemm_workspace_bytes(M, d, F));
+  const size_t o_g = take(gb);
+  if (w) {
+    w->flag = static_cast<int32_t*>(at(o_flag));
+    w->dx = static_cast<float*>(at(o_dx));
+    w->drstd = static_cast<float*>(at(o_dr));
+    w->da = at(o_da);
+    w->dqkv = at(o_dqkv);
+    w->dq = at(o_dq);
+    w->dout = at(o_do);
+    w->dm = at(o_dm);
+    w->da2 = at(o_da2);
+    w->dh = at(o_dh);
+    w->part_o = static_cast<float*>(at(o_po));
+    w->part_ml = static_cast<float*>(at(o_pml));
+    w->x = static_cast<float*>(at(o_x));
+    w->rstd = static_cast<float*>(at(o_r));
+    w->rstd_q = static_cast<float*>(at(o_rq));
+    w->rstd_k = static_cast<float*>(at(o_rk));
+    w->lse = static_cast<float*>(at(o_lse));
+    w->table = static_cast<float*>(at(o_tab));
+    w->xl = static_cast<float*>(at(o_xl));
+    w->a = at(o_a);
+    w->qkv = at(o_qkv);
+    w->o = at(o_o);
+    w->a2 = at(o_a2);
+    w->hl = at(o_hl);
+    w->gemm_ws = gb ? at(o_g) : nullptr;
+    w->gemm_ws_bytes = gb;
+  }
+  return off;
+}
+
+GemmDesc nt(int64_t M, int64_t N, int64_t K, const void* A, const void* W, void* C, int cdt) {
+  GemmDesc g;
+  g.transA = 0;
+  g.transB = 1;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.A = A;
+  g.lda = K;
+  g.B = W;
+  g.ldb = K;
+  g.C = C;
+  g.cdt = cdt;
+  g.ldc = N;
+  g.dtype = NC_BF16;
+  return g;
+}
+
+struct CacheView {
+  bf16* base;
+  int64_t per;  // elements of one [B][max_len][128] block
+  bf16* k(int l) const { return base + (int64_t)(2 * l) * per; }
+  bf16* v(int l) const { return base + (int64_t)(2 * l + 1) * per; }
+};
+
+int check_params(const nc_params* p) {
+  NC_REQUIRE(p && p->embed && p->w_qkv && p->w_o && p->w_fc && p->w_proj && p->unembed, NC_ERR_INVALID_ARG,
+             "infer: null parameter");
+  return NC_OK;
+}
+
+}  // namespace
+
+size_t mqa_decode_workspace_bytes(int B, int H, int max_len) {
+  if (B <= 0 || H <= 0 || max_len <= 0) return 0;
+  const size_t parts = decode_part_floats(B, H, max_len);
+  return align_up(parts * kHd * 4, 256) + parts * 2 * 4;
+}
+
+int mqa_decode_attn(const void* q, const void* kc, const void* vc, const int32_t* lens, int len_add, int B, int H,
+                    int hd, int max_len, float scale, void* o, float* part_o, float* part_ml, hipStream_t s) {
+  NC_REQUIRE(q && kc && vc && lens && o && part_o && part_ml, NC_ERR_INVALID_ARG, "decode_attn: null pointer");
+  NC_REQUIRE(B > 0 && H > 0 && max_len > 0, NC_ERR_INVALID_ARG, "decode_attn: bad shape");
+  NC_REQUIRE(hd == kHd, NC_ERR_UNSUPPORTED, "decode_attn: head_dim must be 128");
+  NC_REQUIRE(H <= kMaxHeads, NC_ERR_UNSUPPORTED, "decode_attn: at most %d query heads", kMaxHeads);
+  NC_REQUIRE((int64_t)B * max_len <= (int64_t)1 << 31, NC_ERR_UNSUPPORTED, "decode_attn: cache too large");
+  const int nch = (int)cdiv(max_len, kChunk);
+  NC_REQUIRE(nch < 65536 && B < 65536, NC_ERR_UNSUPPORTED, "decode_attn: grid too large");
+  const double bytes = (double)B * max_len * kHd * 2 * 2 + 2.0 * 2 * B * H * kHd;  // cache capacity, q and o
+  probe_begin(NC_PROBE_DECODE_ATTN, s);
+  decode_attn_split_kernel<<<dim3(nch, B), 64, 0, s>>>(static_cast<const bf16*>(q), static_cast<const bf16*>(kc),
+                                                       static_cast<const bf16*>(vc), lens, len_add, H, max_len,
+                                                       scale * kLog2e, part_o, part_ml);
+  decode_attn_combine_kernel<<<dim3(H, B), kHd, 0, s>>>(part_o, part_ml, lens, len_add, H, max_len, nch,
+                                                        static_cast<bf16*>(o));
+  probe_end(NC_PROBE_DECODE_ATTN, s, bytes);
+  return check_launch("decode_attn kernels");
+}
+
+size_t kv_cache_bytes(const nc_config* c, int max_len) {
+  if (validate_infer(c, max_len) != NC_OK) return 0;
+  return (size_t)c->n_layer * 2 * c->batch * max_len * kHd * 2;
+}
+
+size_t infer_workspace_bytes(const nc_config* c, int max_len) {
+  if (validate_infer(c, max_len) != NC_OK) return 0;
+  return carve_infer(c, max_len, nullptr, nullptr);
+}
+
+int prefill(const nc_config* c, const nc_params* p, const int32_t* ids, void* kv, int max_len, float* logits,
+            void* ws, size_t ws_bytes, hipStream_t s) {
+  NC_TRY(validate_infer(c, max_len));
+  NC_TRY(check_params(p));
+  NC_REQUIRE(ids && kv && logits && ws, NC_ERR_INVALID_ARG, "prefill: null pointer");
+  NC_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255u) == 0 && (reinterpret_cast<uintptr_t>(kv) & 15u) == 0,
+             NC_ERR_INVALID_ARG, "prefill: ws must be 256-byte and the cache 16-byte aligned");
+  const size_t need = carve_infer(c, max_len, nullptr, nullptr);
+  NC_REQUIRE(ws_bytes >= need, NC_ERR_WORKSPACE, "prefill: workspace too small (%zu < %zu)", ws_bytes, need);
+  InferWs w;
+  carve_infer(c, max_len, &w, ws);
+  const int B = c->batch, T = c->seq_len, H = c->n_head, L = c->n_layer, V = c->vocab;
+  const int64_t M = (int64_t)B * T, d = c->d_model, F = c->d_ff, Q = (int64_t)(H + 2) * kHd, HD = (int64_t)H * kHd;
+  const float scale = 1.f / sqrtf((float)kHd);
+  const CacheView cv{static_cast<bf16*>(kv), (int64_t)B * max_len * kHd};
+  auto W = [&](const void* base, int l, int64_t per) { return static_cast<const bf16*>(base) + (int64_t)l * per; };
+
+  NC_TRY(fill_zero(w.flag, 4, s));
+  NC_TRY(embed_fwd(ids, M, p->embed, NC_BF16, V, (int)d, nullptr, w.x, w.rstd, c->eps, w.flag, s));
+  NC_TRY(rope_table(w.table, T, kHd, c->rope_base, s));
+  for (int l = 0; l < L; ++l) {
+    NC_TRY(rmsnorm_fwd(w.x, NC_F32, M, (int)d, c->eps, w.a, NC_BF16, w.rstd, s));
+    NC_TRY(gemm(nt(M, Q, d, w.a, W(p->w_qkv, l, Q * d), w.qkv, NC_BF16), s));
+    NC_TRY(rope_qknorm_fwd(w.qkv, NC_BF16, B, T, H, kHd, w.table, c->eps, w.rstd_q, w.rstd_k, s));
+    NC_TRY(mqa_attn_fwd(w.qkv, NC_BF16, B, T, H, kHd, scale, w.o, w.lse, s));
+    cache_fill_kernel<<<(unsigned)cdiv(M * 32, 256), 256, 0, s>>>(static_cast<const bf16*>(w.qkv), M, T, H,
+                                                                 cv.k(l), cv.v(l), max_len);
+    NC_TRY(check_launch("cache_fill_kernel"));
+    GemmDesc go = nt(M, d, HD, w.o, W(p->w_o, l, d * HD), w.x, NC_F32);
+    go.beta = 1.f;
+    go.ws = w.gemm_ws;
+    go.ws_bytes = w.gemm_ws_bytes;
+    NC_TRY(gemm(go, s));
+    NC_TRY(rmsnorm_fwd(w.x, NC_F32, M, (int)d, c->eps, w.a, NC_BF16, w.rstd, s));
+    GemmDesc gf = nt(M, F, d, w.a, W(p->w_fc, l, F * d), w.a2, NC_BF16);
+    gf.epi = NC_EPI_RELU2_SQ;
+    NC_TRY(gemm(gf, s));
+    GemmDesc gp = nt(M, d, F, w.a2, W(p->w_proj, l, d * F), w.x, NC_F32);
+    gp.beta = 1.f;
+    gp.ws = w.gemm_ws;
+    gp.ws_bytes = w.gemm_ws_bytes;
+    NC_TRY(gemm(gp, s));
+  }
+  last_rows_kernel<<<(unsigned)cdiv((int64_t)B * d, 256), 256, 0, s>>>(w.x, B, T, (int)d, w.xl);
+  NC_TRY(check_launch("last_rows_kernel"));
+  NC_TRY(rmsnorm_fwd(w.xl, NC_F32, B, (int)d, c->eps, w.hl, NC_BF16, w.drstd, s));
+  GemmDesc gu = nt(B, V, d, w.hl, p->unembed, logits, NC_F32);
+  gu.capc = c->softcap;
+  return gemm(gu, s);
+}
+
+int decode_step(const nc_config* c, const nc_params* p, const int32_t* ids, const int32_t* pos, void* kv,
+                int max_len, float* logits, void* ws, size_t ws_bytes, hipStream_t s) {
+  NC_TRY(validate_infer(c, max_len));
+  NC_TRY(check_params(p));
+  NC_REQUIRE(ids && pos && kv && logits && ws, NC_ERR_INVALID_ARG, "decode: null pointer");
+  NC_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255u) == 0 && (reinterpret_cast<uintptr_t>(kv) & 15u) == 0,
+             NC_ERR_INVALID_ARG, "decode: ws must be 256-byte and the cache 16-byte aligned");
+  const size_t need = carve_infer(c, max_len, nullptr, nullptr);
+  NC_REQUIRE(ws_bytes >= need, NC_ERR_WORKSPACE, "decode: workspace too small (%zu < %zu)", ws_bytes, need);
+  InferWs w;
+  carve_infer(c, max_len, &w, ws);
+  const int B = c->batch, H = c->n_head, L = c->n_layer, V = c->vocab;
+  const int64_t d = c->d_model, F = c->d_ff, Q = (int64_t)(H + 2) * kHd, HD = (int64_t)H * kHd;
+  const float scale = 1.f / sqrtf((float)kHd);
+  const CacheView cv{static_cast<bf16*>(kv), (int64_t)B * max_len * kHd};
+  auto W = [&](const void* base, int l, int64_t per) { return static_cast<const bf16*>(base) + (int64_t)l * per; };
+
+  NC_TRY(fill_zero(w.flag, 4, s));
+  NC_TRY(embed_fwd(ids, B, p->embed, NC_BF16, V, (int)d, nullptr, w.dx, w.drstd, c->eps, w.flag, s));
+  for (int l = 0; l < L; ++l) {
+    NC_TRY(rmsnorm_fwd(w.dx, NC_F32, B, (int)d, c->eps, w.da, NC_BF16, w.drstd, s));
+    NC_TRY(gemm(nt(B, Q, d, w.da, W(p->w_qkv, l, Q * d), w.dqkv, NC_BF16), s));
+    decode_rope_append_kernel<<<B, 256, 0, s>>>(static_cast<const bf16*>(w.dqkv), pos, H, (double)c->rope_base,
+                                                c->eps, max_len, static_cast<bf16*>(w.dq), cv.k(l), cv.v(l), w.flag);
+    NC_TRY(check_launch("decode_rope_append_kernel"));
+    NC_TRY(mqa_decode_attn(w.dq, cv.k(l), cv.v(l), pos, 1, B, H, kHd, max_len, scale, w.dout, w.part_o, w.part_ml,
+                           s));
+    GemmDesc go = nt(B, d, HD, w.dout, W(p->w_o, l, d * HD), w.dx, NC_F32);
+    go.beta = 1.f;
+    NC_TRY(gemm(go, s));
+    NC_TRY(rmsnorm_fwd(w.dx, NC_F32, B, (int)d, c->eps, w.dm, NC_BF16, w.drstd, s));
+    GemmDesc gf = nt(B, F, d, w.dm, W(p->w_fc, l, F * d), w.da2, NC_BF16);
+    gf.epi = NC_EPI_RELU2_SQ;
+    NC_TRY(gemm(gf, s));
+    GemmDesc gp = nt(B, d, F, w.da2, W(p->w_proj, l, d * F), w.dx, NC_F32);
+    gp.beta = 1.f;
+    NC_TRY(gemm(gp, s));
+  }
+  NC_TRY(rmsnorm_fwd(w.dx, NC_F32, B, (int)d, c->eps, w.dh, NC_BF16, w.drstd, s));
+  GemmDesc gu = nt(B, V, d, w.dh, p->unembed, logits, NC_F32);
+  gu.capc = c->softcap;
+  return gemm(gu, s);
+}
+
+}  // namespace nc
+
+extern "C" size_t nc_kv_cache_bytes(const nc_config* cfg, int max_len) { return nc::kv_cache_bytes(cfg, max_len); }
+
+extern "C" size_t nc_infer_workspace_bytes(const nc_config* cfg, int max_len) {
+  return nc::infer_workspace_bytes(cfg, max_len);
+}
+
+extern "C" int nc_prefill(const nc_config* cfg, const nc_params* params, const int32_t* ids, void* kv_cache,
+                          int max_len, float* logits, void* ws, size_t ws_bytes, void* stream) {
+  return nc::prefill(cfg, params, ids, kv_cache, max_len, logits, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int nc_decode_step(const nc_config* cfg, const nc_params* params, const int32_t* ids,
+                              const int32_t* pos, void* kv_cache, int max_len, float* logits, void* ws,
+                              size_t ws_bytes, void* stream) {
+  return nc::decode_step(cfg, params, ids, pos, kv_cache, max_len, logits, ws, ws_bytes,
+                         static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t nc_mqa_decode_workspace_bytes(int B, int H, int max_len) {
+  return nc::mqa_decode_workspace_bytes(B, H, max_len);
+}
+
+extern "C" int nc_mqa_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* lens,
+                                  int B, int H, int hd, int max_len, float scale, void* o, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  const size_t need = nc::mqa_decode_workspace_bytes(B, H, max_len);
+  NC_REQUIRE(ws && need > 0, NC_ERR_INVALID_ARG, "decode_attn: null workspace or bad shape");
+  NC_REQUIRE(ws_bytes >= need, NC_ERR_WORKSPACE, "decode_attn: workspace too small (%zu < %zu)", ws_bytes, need);
+  NC_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255u) == 0, NC_ERR_INVALID_ARG, "decode_attn: ws must be 256-byte aligned");
+  const size_t parts = (size_t)B * nc::cdiv(max_len, 64) * H;
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + nc::align_up(parts * 128 * 4, 256));
+  return nc::mqa_decode_attn(q, k_cache, v_cache, lens, 0, B, H, hd, max_len, scale, o, part_o, part_ml,
+                             static_cast<hipStream_t>(stream));
+}

@@ -22,7 +22,7 @@ NC_OK, NC_ERR_INVALID_ARG, NC_ERR_UNSUPPORTED, NC_ERR_WORKSPACE, NC_ERR_HIP, NC_
 NC_F32, NC_BF16 = 0, 1
 NC_EPI_STORE, NC_EPI_RELU2, NC_EPI_RELU2_BWD, NC_EPI_RELU2_SQ, NC_EPI_RELU2_BWD_SQ = 0, 1, 2, 3, 4
 (NC_PROBE_OFF, NC_PROBE_GEMM_WGRAD, NC_PROBE_GEMM_NT, NC_PROBE_ATTN_FWD, NC_PROBE_ATTN_DQ,
- NC_PROBE_ATTN_DKV) = range(6)
+ NC_PROBE_ATTN_DKV, NC_PROBE_GEMM_SKINNY, NC_PROBE_DECODE_ATTN) = range(8)
 
 c_int, c_i64, c_f, c_sz, c_p = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -76,6 +76,14 @@ _SIGS = {
     "nc_relu2_mlp": (c_int, [c_p, c_p, c_p, c_int, c_i64, c_int, c_int, c_p, c_p, c_p, c_p]),
     "nc_relu2_mlp_bwd": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_int, c_i64, c_int, c_int, c_p, c_p, c_p, c_int,
                                  c_p, c_p, c_sz, c_p]),
+    "nc_kv_cache_bytes": (c_sz, [ctypes.POINTER(nc_config), c_int]),
+    "nc_infer_workspace_bytes": (c_sz, [ctypes.POINTER(nc_config), c_int]),
+    "nc_prefill": (c_int, [ctypes.POINTER(nc_config), ctypes.POINTER(nc_params), c_p, c_p, c_int, c_p, c_p, c_sz,
+                           c_p]),
+    "nc_decode_step": (c_int, [ctypes.POINTER(nc_config), ctypes.POINTER(nc_params), c_p, c_p, c_p, c_int, c_p, c_p,
+                               c_sz, c_p]),
+    "nc_mqa_decode_workspace_bytes": (c_sz, [c_int, c_int, c_int]),
+    "nc_mqa_decode_attn": (c_int, [c_p, c_p, c_p, c_p, c_int, c_int, c_int, c_int, c_f, c_p, c_p, c_sz, c_p]),
     "nc_softcap_xent_workspace_bytes": (c_sz, [c_i64, c_int, c_int]),
     "nc_softcap_xent_fwd": (c_int, [c_p, c_p, c_int, c_p, c_p, c_i64, c_int, c_int, c_f, c_p, c_p, c_p, c_p, c_p,
                                     c_sz, c_p]),
@@ -290,3 +298,35 @@ def nc_softcap_xent_bwd(h, U, tgt, lse, softcap, dloss, dh, dh_accumulate, dU, d
     _check(load().nc_softcap_xent_bwd(_p(h), _p(U), dtype_code(h.dtype), _p(tgt), _p(lse), M, d, V, softcap, dloss,
                                       _p(dh), int(dh_accumulate), _p(dU), int(dU_accumulate), _p(ws),
                                       ws.numel() * ws.element_size(), _stream(stream)))
+
+
+_PARAM_NAMES = ("embed", "w_qkv", "w_o", "w_fc", "w_proj", "unembed")
+
+
+def nc_kv_cache_bytes(cfg: nc_config, max_len: int) -> int:
+    return load().nc_kv_cache_bytes(ctypes.byref(cfg), max_len)
+
+
+def nc_infer_workspace_bytes(cfg: nc_config, max_len: int) -> int:
+    return load().nc_infer_workspace_bytes(ctypes.byref(cfg), max_len)
+
+
+def nc_prefill(cfg: nc_config, params: dict, ids, kv_cache, max_len: int, logits, ws, stream=None) -> None:
+    p = nc_params(*[_p(params[n]) for n in _PARAM_NAMES])
+    _check(load().nc_prefill(ctypes.byref(cfg), ctypes.byref(p), _p(ids), _p(kv_cache), max_len, _p(logits), _p(ws),
+                             ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def nc_decode_step(cfg: nc_config, params: dict, ids, pos, kv_cache, max_len: int, logits, ws, stream=None) -> None:
+    p = nc_params(*[_p(params[n]) for n in _PARAM_NAMES])
+    _check(load().nc_decode_step(ctypes.byref(cfg), ctypes.byref(p), _p(ids), _p(pos), _p(kv_cache), max_len,
+                                 _p(logits), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def nc_mqa_decode_workspace_bytes(B: int, H: int, max_len: int) -> int:
+    return load().nc_mqa_decode_workspace_bytes(B, H, max_len)
+
+
+def nc_mqa_decode_attn(q, k_cache, v_cache, lens, B, H, hd, max_len, scale, o, ws, stream=None) -> None:
+    _check(load().nc_mqa_decode_attn(_p(q), _p(k_cache), _p(v_cache), _p(lens), B, H, hd, max_len, scale, _p(o),
+                                     _p(ws), ws.numel() * ws.element_size(), _stream(stream)))

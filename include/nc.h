@@ -120,6 +120,9 @@ int nc_sync_status(const int32_t* flag, void* stream);
  * by a pair of HIP events recorded on the stream it is launched on, and the
  * library adds up the algorithmic FLOPs of those launches:
  *   GEMM families: 2 M N K per launch (a split-K launch counts its whole K);
+ *   HBM-bound families (small-M GEMM, decode attention): algorithmic bytes
+ *   instead of FLOPs (W, A and C once for the GEMM; the cached keys and
+ *   values up to each sequence's length, q and o for the attention);
  *   attention (causal, per launch over B sequences of T tokens, H heads of
  *   width hd, counting half of the T x T score square): forward
  *   2 B H hd T^2 (two products), dQ 2 B H hd T^2 (dP and dQ), dK/dV
@@ -139,7 +142,9 @@ typedef enum {
   NC_PROBE_GEMM_NT = 2,    /* K-contiguous GEMMs (forward projections, dX)           */
   NC_PROBE_ATTN_FWD = 3,   /* causal MQA attention forward                           */
   NC_PROBE_ATTN_DQ = 4,    /* attention backward, dQ kernel                          */
-  NC_PROBE_ATTN_DKV = 5    /* attention backward, dK/dV kernel                       */
+  NC_PROBE_ATTN_DKV = 5,   /* attention backward, dK/dV kernel                       */
+  NC_PROBE_GEMM_SKINNY = 6, /* small-M GEMMs (M <= 128, decoding): counts bytes       */
+  NC_PROBE_DECODE_ATTN = 7  /* decode attention over the key/value cache: bytes       */
 } nc_probe_family;
 
 int nc_probe_start(int family, int max_launches);
@@ -171,6 +176,60 @@ int nc_step_fwd_bwd(const nc_config* cfg, const nc_params* params, const nc_grad
                     const int32_t* ids, const int32_t* targets, const float* token_bytes,
                     void* ws, size_t ws_bytes, float* loss, float* bpb, float* loss_tok,
                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Inference with a key/value cache [NEWS, section 技術細節與問答: the model
+ * (multi-query attention, RoPE, QK norm, logit softcap) and its serving
+ * engine].  The cache holds each layer's post-RoPE, post-norm key and its
+ * value for every position already seen.  By causality the logits at a
+ * position depend on tokens up to it only, so prefill and decode return the
+ * full forward's softcapped logits row at that position.
+ * Supported: dtype NC_BF16, head_dim 128, n_kv_head 1, n_head <= 16,
+ * batch <= 128; d_model and d_ff multiples of 64, vocab a multiple of 32.
+ *   kv_cache: nc_kv_cache_bytes(cfg, max_len) bytes, 16-byte aligned, bf16
+ *             [L][2][B][max_len][128] (keys, then values, of each layer).
+ *   ws:       nc_infer_workspace_bytes(cfg, max_len) bytes, 256-byte aligned;
+ *             its first int32 is the device flag (nc_sync_status(ws)).
+ * Both are caller-owned; the size queries return 0 for an unsupported
+ * configuration (or max_len < cfg->seq_len).
+ *
+ * nc_prefill: ids [B, T] int32 with B = cfg->batch and T = cfg->seq_len, the
+ *   prompts.  Runs the forward over all B T tokens, writes positions 0..T-1
+ *   of the cache and writes logits [B, V] fp32 = the softcapped logits at
+ *   position T-1 of each prompt.  Token ids outside [0, V) raise the flag.
+ * nc_decode_step: ids [B] int32, one new token per sequence, at the position
+ *   pos[b] (int32, device); positions 0..pos[b]-1 of sequence b must already be
+ *   in the cache.  Writes that token's key and value at position pos[b] and
+ *   logits [B, V] fp32 = the softcapped logits at pos[b].  The positions may
+ *   differ between sequences.  A position outside [0, max_len) or an id
+ *   outside [0, V) raises the flag (that sequence's outputs are then
+ *   undefined, memory outside the buffers is never touched).
+ * Errors: NC_ERR_INVALID_ARG (null or misaligned pointers, n_head hd !=
+ *   d_model, max_len < seq_len), NC_ERR_UNSUPPORTED (outside the supported
+ *   shapes), NC_ERR_WORKSPACE.
+ */
+size_t nc_kv_cache_bytes(const nc_config* cfg, int max_len);
+size_t nc_infer_workspace_bytes(const nc_config* cfg, int max_len);
+int nc_prefill(const nc_config* cfg, const nc_params* params, const int32_t* ids, void* kv_cache,
+               int max_len, float* logits, void* ws, size_t ws_bytes, void* stream);
+int nc_decode_step(const nc_config* cfg, const nc_params* params, const int32_t* ids, const int32_t* pos,
+                   void* kv_cache, int max_len, float* logits, void* ws, size_t ws_bytes, void* stream);
+
+/* Decode attention over a cache [NEWS: multi-query attention]: for every
+ * sequence b and query head h,
+ *   o[b, h] = sum_{u < lens[b]} softmax_u(q[b, h] . k[b, u] * scale) v[b, u].
+ *   q, o: bf16 [B, H, 128]; k_cache, v_cache: bf16 [B, max_len, 128];
+ *   lens: int32 [B] (device), clamped to [0, max_len]; a sequence with no
+ *   positions gets o = 0.
+ *   ws: nc_mqa_decode_workspace_bytes(B, H, max_len) bytes, 256-byte aligned
+ *   (fp32 partial results per 64 cached positions).
+ * Work is split over 64-position chunks and the chunks are combined in a
+ * fixed order (deterministic).  Errors: NC_ERR_INVALID_ARG,
+ * NC_ERR_UNSUPPORTED (head_dim != 128, H > 16), NC_ERR_WORKSPACE. */
+size_t nc_mqa_decode_workspace_bytes(int B, int H, int max_len);
+int nc_mqa_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* lens, int B,
+                       int H, int hd, int max_len, float scale, void* o, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* ---------------------------------------------------------------------------
  * Token-embedding gather and the norm that follows it [NEWS: untied
