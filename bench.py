@@ -10,7 +10,12 @@ timed region.  Besides the throughput it reports
   * roofline: the dominant kernel's achieved TFLOP/s against the bf16 matrix
     peak, timed live with HIP events on the stream it runs on;
   * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
-    sample of the same workload.
+    sample of the same workload;
+  * optimizer: the AdamW update over every parameter (HBM roofline) and the
+    whole training iteration;
+  * decode: prefill and one-token decode steps of the same model with a
+    key/value cache (HBM rooflines of the decode attention and the small-M
+    GEMMs).
 """
 from __future__ import annotations
 
@@ -184,6 +189,89 @@ def optimizer_leg(cfg, inp, torch, nc, params, grads, step, s, reps=5):
             "iteration_ms": round(it_ms, 3), "iteration_tokens_per_s": round(cfg.tokens / (it_ms * 1e-3), 1)}
 
 
+def decode_leg(cfg, torch, nc, params, s, steps=64, max_len=2048):
+    """Inference on the same model: prefill of B prompts of max_len - steps
+    tokens, then `steps` decode steps (one token per sequence, positions
+    max_len - steps .. max_len - 1).  HBM-bound: a step reads every projection
+    weight and U once (small-M GEMMs) and each sequence's cached keys and
+    values once per layer (decode attention).  Timed with HIP events on the
+    launch stream; the per-kernel times come from the library's kernel timer
+    in two extra passes (one family each), the bytes are counted here from
+    the known positions."""
+    import dataclasses
+    from synthetic import make_tokens
+    T0 = max_len - steps
+    icfg = dataclasses.replace(cfg, seq_len=T0)
+    ccfg = nc.make_config(icfg)
+    B, L, d, H, F, V = cfg.batch, cfg.n_layer, cfg.d_model, cfg.n_head, cfg.d_ff, cfg.vocab
+    kv = torch.empty(nc.nc_kv_cache_bytes(ccfg, max_len), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(nc.nc_infer_workspace_bytes(ccfg, max_len), dtype=torch.uint8, device="cuda")
+    logits = torch.empty(B, V, device="cuda")
+    toks = torch.from_numpy(make_tokens(cfg, seed=4242)).to("cuda")  # [B, 2049], Zipf(1.1)
+    prompts = toks[:, :T0].contiguous()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def prefill():
+        nc.nc_prefill(ccfg, params, prompts, kv, max_len, logits, ws, stream=s)
+
+    prefill()
+    torch.cuda.synchronize()
+    e0.record(s)
+    prefill()
+    e1.record(s)
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    pos = [torch.full((B,), T0 + j, dtype=torch.int32, device="cuda") for j in range(steps)]
+    ids = [toks[:, T0 + j].contiguous() for j in range(steps)]
+
+    def run(family=None):
+        if family is not None:
+            nc.nc_probe_start(getattr(nc, family), 512 * steps)
+        e0.record(s)
+        for j in range(steps):
+            nc.nc_decode_step(ccfg, params, ids[j], pos[j], kv, max_len, logits, ws, stream=s)
+        e1.record(s)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        return ms, (nc.nc_probe_stop() if family is not None else None)
+
+    run()
+    ms, _ = run()
+    if nc.nc_sync_status(ws) != nc.NC_OK:
+        raise RuntimeError("device flag raised during decoding")
+    _, (att_ms, att_n, _) = run("NC_PROBE_DECODE_ATTN")
+    _, (gem_ms, gem_n, gem_bytes) = run("NC_PROBE_GEMM_SKINNY")
+    # algorithmic bytes
+    Q, HD = (H + 2) * 128, H * 128
+    w_bytes = 2 * (L * (Q * d + d * HD + F * d + d * F) + V * d)
+    mean_len = T0 + (steps + 1) / 2.0                    # positions T0 .. T0 + steps - 1, lengths pos + 1
+    kv_bytes_launch = B * mean_len * 128 * 2 * 2 + 2 * B * H * 128 * 2
+    act_bytes = 2 * L * B * (Q + HD + F + d) * 2 + B * V * 4
+    step_bytes = w_bytes + L * kv_bytes_launch + act_bytes
+    att_us = 1e3 * att_ms / att_n
+    att_gbs = kv_bytes_launch / (att_us * 1e-6) / 1e9
+    gem_gbs = gem_bytes / (gem_ms * 1e-3) / 1e9
+    step_gbs = step_bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] decode d20: {ms:.3f} ms/step ({B / (ms * 1e-3):.0f} tok/s), {step_gbs:.0f} GB/s over "
+        f"{step_bytes / 1e9:.3f} GB; attention {att_us:.1f} us/launch {att_gbs:.0f} GB/s; small-M GEMMs "
+        f"{gem_gbs:.0f} GB/s; prefill {prefill_ms:.1f} ms")
+    return {
+        "workload": f"{cfg.name} decode: {B} sequences, one token each at positions {T0}..{max_len - 1} "
+                    f"(cache max_len {max_len}), after a {T0}-token prefill",
+        "tokens_per_s": round(B / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+        "step_bytes": int(step_bytes), "step_achieved_GBs": round(step_gbs, 1),
+        "step_frac": round(step_gbs / PEAK_HBM_GBS, 4),
+        "attention": {"kernel": "decode_attn_split_kernel + decode_attn_combine_kernel", "bound": "hbm",
+                      "achieved": round(att_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(att_gbs / PEAK_HBM_GBS, 4), "avg_launch_us": round(att_us, 2),
+                      "bytes_per_launch": int(kv_bytes_launch)},
+        "gemm": {"kernel": "gemm_skinny_kernel", "bound": "hbm", "achieved": round(gem_gbs, 1),
+                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gem_gbs / PEAK_HBM_GBS, 4),
+                 "launches_per_step": gem_n // steps, "avg_launch_us": round(1e3 * gem_ms / gem_n, 2)},
+        "prefill_tokens_per_s": round(B * T0 / (prefill_ms * 1e-3), 1),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +281,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None)
     ap.add_argument("--roofline-kernel", default=DOMINANT, choices=sorted(FAMILIES))
+    ap.add_argument("--no-decode", action="store_true", help="skip the prefill / decode timings")
     ap.add_argument("--no-optimizer", action="store_true", help="skip the AdamW and full-iteration timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with one 1 GiB device-to-device copy (counter calibration runs)")
@@ -247,6 +336,9 @@ def main():
     log(f"[bench] {roof['kernel']}: {roof['launches']} launches, {roof['avg_launch_us']:.1f} us/launch, "
         f"{roof['achieved']} TFLOP/s")
     opt = None if a.no_optimizer else optimizer_leg(cfg, inp, torch, nc, params, grads, step, s)
+    dec = None
+    if not a.no_decode and cfg.dtype == "bf16" and cfg.head_dim == 128:
+        dec = decode_leg(cfg, torch, nc, params, s)
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -285,6 +377,7 @@ def main():
         "roofline_kernel": {k: roof[k] for k in ("kernel", "launches", "avg_launch_us", "flops_per_launch")},
         "cpu_baseline": base,
         "optimizer": opt,
+        "decode": dec,
     }
     print(json.dumps(out), flush=True)
 

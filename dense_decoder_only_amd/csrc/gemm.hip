@@ -26,6 +26,7 @@
 //     results are bitwise reproducible.
 #include "common.h"
 #include "gemm.h"
+#include "ops.h"
 
 #include <algorithm>
 
@@ -1059,22 +1060,25 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Small-M products (decoding: one new token per sequence), C[M, N] =
 // A[M, K] W[N, K]^T with M <= 128 and both operands K-contiguous.  The work
 // is reading W once from HBM (2 N K bytes against 2 M N K FLOPs), so the
-// kernel is organised around that stream, not around MFMA reuse:
-//  * a block owns 32 rows of W (32 output columns) and every row of A; its
-//    8 waves take the 64-wide k-chunks in turn (chunk c to wave c mod 8) and
-//    add their partial sums in LDS in a fixed order (deterministic);
-//  * per chunk, lane l reads 64 contiguous bytes of W row n0 + l mod 32 at
-//    k offset 32 (l / 32); the next chunk's W is loaded before the current
-//    chunk's MFMAs;
-//  * the MFMA k-slots are permuted the same way for both operands: MFMA s of
-//    a chunk covers k = 8 s + {0..7} (lanes 0-31) and 32 + 8 s + {0..7}
-//    (lanes 32-63), so the four MFMAs sum all 64;
+// kernel is organised around that stream and its latency, not MFMA reuse:
+//  * a block of 16 waves owns 16 rows of W (16 output columns) and every row
+//    of A; the 64-wide k-chunks go round-robin over the waves, and each wave
+//    issues the loads of up to 4 chunks (W and A) before its first MFMA, so a
+//    block has up to 64 chunks (128 KB of W) in flight;
+//  * per chunk, lane l reads 32 contiguous bytes of W row n0 + l mod 16 at k
+//    offset 16 (l / 16); v_mfma_f32_16x16x32_bf16 takes k-slots 8 (l / 16) ..
+//    + 7 from lane l, so MFMA s (0, 1) of a chunk is fed the lane's bytes
+//    16 s .. 16 s + 15 of both operands: the k-slot order is permuted the
+//    same way for W and A and the two MFMAs sum all 64 k;
 //  * the product is issued as C^T (W fragment first): lane l ends with output
-//    column group n0 + 8 (q / 4) + 4 (l / 32) + q mod 4 of token row l mod 32.
+//    columns n0 + 4 (l / 16) + q (q = 0..3) of token row l mod 16;
+//  * the 16 waves add their sums in LDS in a fixed order (deterministic), one
+//    16 x 16 tile at a time, and 256 threads apply the epilogue.
 // A (at most 128 x K bf16) stays in L2 across the blocks that re-read it.
 // ---------------------------------------------------------------------------
-constexpr int SK_WAVES = 8, SK_MMAX = 128;
+constexpr int SK_WAVES = 16, SK_MMAX = 128, SK_CPW = 4;
 enum { E_SOFTCAP_F32 = 10 };  // small-M only: C (fp32) = c tanh(acc / c)
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct SkinnyParams {
   const bf16* A;
@@ -1088,104 +1092,115 @@ struct SkinnyParams {
 };
 
 template <int EPI>
-__device__ __forceinline__ void skinny_store2(const SkinnyParams& p, int m, int n, float v0, float v1) {
+__device__ __forceinline__ void skinny_store1(const SkinnyParams& p, int m, int n, float v) {
   const int64_t off = (int64_t)m * p.ldc + n;
   if constexpr (EPI == E_STORE_F32) {
-    *reinterpret_cast<float2*>(static_cast<float*>(p.C) + off) = make_float2(v0, v1);
+    static_cast<float*>(p.C)[off] = v;
   } else if constexpr (EPI == E_ACC_F32) {
-    float2* c = reinterpret_cast<float2*>(static_cast<float*>(p.C) + off);
-    const float2 o = *c;
-    *c = make_float2(o.x + v0, o.y + v1);
+    static_cast<float*>(p.C)[off] += v;
   } else if constexpr (EPI == E_STORE_BF16) {
-    *reinterpret_cast<uint32_t*>(static_cast<bf16*>(p.C) + off) = pack_bf16x2(v0, v1);
+    static_cast<bf16*>(p.C)[off] = f2bf(v);
   } else if constexpr (EPI == E_RELU2_SQ) {
-    const float a = fmaxf(v0, 0.f), b = fmaxf(v1, 0.f);
-    *reinterpret_cast<uint32_t*>(static_cast<bf16*>(p.C) + off) = pack_bf16x2(a * a, b * b);
+    const float a = fmaxf(v, 0.f);
+    static_cast<bf16*>(p.C)[off] = f2bf(a * a);
   } else {  // E_SOFTCAP_F32
-    *reinterpret_cast<float2*>(static_cast<float*>(p.C) + off) =
-        make_float2(softcap_of(v0, p.capc, p.inv_capc), softcap_of(v1, p.capc, p.inv_capc));
+    static_cast<float*>(p.C)[off] = softcap_of(v, p.capc, p.inv_capc);
+  }
+}
+
+// NMT: 16-row tiles of A held per wave (1, 2, 4 or 8; rows >= M are zero).
+template <int EPI, int NMT>
+__global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny_kernel(SkinnyParams p) {
+  __shared__ float red[SK_WAVES][4][64];
+  // The wave index is made wave-uniform explicitly: the chunk guards below
+  // must compile to scalar branches.  Under an EXEC-masked branch an MFMA
+  // still runs (it ignores EXEC) and would add whatever the skipped loads
+  // left in its registers.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  constexpr int nmt = NMT;
+  const int nch = p.K >> 6;
+  f32x4_t acc[NMT];
+#pragma unroll
+  for (int i = 0; i < NMT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bf16* wrow = p.W + (int64_t)(n0 + r) * p.ldw + 16 * g;
+  for (int cb = wave; cb < nch; cb += SK_CPW * SK_WAVES) {
+    bf16x8_t w[SK_CPW][2];
+#pragma unroll
+    for (int j = 0; j < SK_CPW; ++j) {
+      const int c = cb + j * SK_WAVES;
+      if (c < nch) {
+        w[j][0] = *reinterpret_cast<const bf16x8_t*>(wrow + (c << 6));
+        w[j][1] = *reinterpret_cast<const bf16x8_t*>(wrow + (c << 6) + 8);
+      } else {  // never multiplied (the MFMAs below are skipped), but defined
+        w[j][0] = bf16x8_t{};
+        w[j][1] = bf16x8_t{};
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      {
+        const int m = mt * 16 + r;
+        bf16x8_t x[SK_CPW][2];
+#pragma unroll
+        for (int j = 0; j < SK_CPW; ++j) {
+          const int c = cb + j * SK_WAVES;
+          if (c < nch && m < p.M) {
+            const bf16* xr = p.A + (int64_t)m * p.lda + (c << 6) + 16 * g;
+            x[j][0] = *reinterpret_cast<const bf16x8_t*>(xr);
+            x[j][1] = *reinterpret_cast<const bf16x8_t*>(xr + 8);
+          } else {
+            x[j][0] = bf16x8_t{};
+            x[j][1] = bf16x8_t{};
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < SK_CPW; ++j) {
+          if (cb + j * SK_WAVES < nch) {
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[j][0], x[j][0], acc[mt], 0, 0, 0);
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[j][1], x[j][1], acc[mt], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  // fixed-order reduction over the waves, one 16 x 16 tile at a time
+  const int t = threadIdx.x, pl = t & 63, q = (t >> 6) & 3;
+#pragma unroll
+  for (int mt = 0; mt < nmt; ++mt) {
+    if (mt * 16 < p.M) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[mt][i];
+      __syncthreads();
+      if (t < 256) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < SK_WAVES; ++w) v += red[w][q][pl];
+        const int m = mt * 16 + (pl & 15);
+        if (m < p.M) skinny_store1<EPI>(p, m, n0 + 4 * (pl >> 4) + q, v);
+      }
+      __syncthreads();
+    }
   }
 }
 
 template <int EPI>
-__global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny_kernel(SkinnyParams p) {
-  __shared__ float red[SK_WAVES][16][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = lane & 31, h = lane >> 5;
-  const int n0 = blockIdx.x * 32;
-  const int nmt = (p.M + 31) >> 5;
-  f32x16 acc[SK_MMAX / 32];
-#pragma unroll
-  for (int i = 0; i < SK_MMAX / 32; ++i)
-#pragma unroll
-    for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
-  const bf16* wrow = p.W + (int64_t)(n0 + r) * p.ldw + 32 * h;
-  const int nch = p.K >> 6;
-  bf16x8_t wc[4], wn[4];
-  int c = wave;
-  if (c < nch) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) wc[s] = *reinterpret_cast<const bf16x8_t*>(wrow + (c << 6) + 8 * s);
-  }
-  for (; c < nch; c += SK_WAVES) {
-    const bool more = c + SK_WAVES < nch;
-    if (more) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        wn[s] = *reinterpret_cast<const bf16x8_t*>(wrow + ((c + SK_WAVES) << 6) + 8 * s);
-    }
-    const int kc = (c << 6) + 32 * h;
-#pragma unroll
-    for (int mt = 0; mt < SK_MMAX / 32; ++mt) {
-      if (mt < nmt) {
-        const int m = mt * 32 + r;
-        bf16x8_t x[4];
-        if (m < p.M) {
-          const bf16* xr = p.A + (int64_t)m * p.lda + kc;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) x[s] = *reinterpret_cast<const bf16x8_t*>(xr + 8 * s);
-        } else {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) x[s] = bf16x8_t{};
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wc[s], x[s], acc[mt], 0, 0, 0);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) wc[s] = wn[s];
-    }
-  }
-  // fixed-order reduction over the waves, one 32 x 32 tile at a time
-  const int t = threadIdx.x, pl = t & 63, q0 = 2 * (t >> 6);
-  const int n = n0 + 8 * (q0 >> 2) + 4 * (pl >> 5) + (q0 & 3);
-#pragma unroll
-  for (int mt = 0; mt < SK_MMAX / 32; ++mt) {
-    if (mt < nmt) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) red[wave][q][lane] = acc[mt][q];
-      __syncthreads();
-      float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-      for (int w = 0; w < SK_WAVES; ++w) {
-        v0 += red[w][q0][pl];
-        v1 += red[w][q0 + 1][pl];
-      }
-      const int m = mt * 32 + (pl & 31);
-      if (m < p.M) skinny_store2<EPI>(p, m, n, v0, v1);
-      __syncthreads();
-    }
-  }
+void launch_skinny(const SkinnyParams& p, int nmt, hipStream_t s) {
+  const unsigned blocks = (unsigned)(p.N / 16);
+  if (nmt <= 1) gemm_skinny_kernel<EPI, 1><<<blocks, SK_WAVES * 64, 0, s>>>(p);
+  else if (nmt <= 2) gemm_skinny_kernel<EPI, 2><<<blocks, SK_WAVES * 64, 0, s>>>(p);
+  else if (nmt <= 4) gemm_skinny_kernel<EPI, 4><<<blocks, SK_WAVES * 64, 0, s>>>(p);
+  else gemm_skinny_kernel<EPI, 8><<<blocks, SK_WAVES * 64, 0, s>>>(p);
 }
 
 // Small-M form if the shapes and epilogue allow it; returns false to let the
 // caller take the general path.
 bool skinny_ok(const GemmDesc& g) {
   if (g.dtype != NC_BF16 || g.transA != 0 || g.transB != 1 || g.xent) return false;
-  if (g.M < 1 || g.M > SK_MMAX || g.N % 32 != 0 || g.K % 64 != 0) return false;
-  if (g.lda % 8 != 0 || g.ldb % 8 != 0 || g.ldc % 2 != 0) return false;
-  if (!aligned16(g.A) || !aligned16(g.B) || (reinterpret_cast<uintptr_t>(g.C) & 7u) != 0) return false;
+  if (g.M < 1 || g.M > SK_MMAX || g.N % 16 != 0 || g.K % 64 != 0) return false;
+  if (g.lda % 8 != 0 || g.ldb % 8 != 0) return false;
+  if (!aligned16(g.A) || !aligned16(g.B)) return false;
   if (g.capc > 0.f) return g.cdt == NC_F32 && g.beta == 0.f && g.epi == NC_EPI_STORE;
   if (g.epi == NC_EPI_RELU2_SQ) return g.cdt == NC_BF16;
   return g.epi == NC_EPI_STORE;
@@ -1204,26 +1219,29 @@ int gemm_skinny(const GemmDesc& g, hipStream_t s) {
   p.K = (int)g.K;
   p.capc = g.capc;
   p.inv_capc = g.capc > 0.f ? 1.f / g.capc : 0.f;
-  const unsigned blocks = (unsigned)(g.N / 32);
   const double bytes = 2.0 * (double)g.N * g.K + 2.0 * (double)g.M * g.K +
                        (double)g.M * g.N * (g.cdt == NC_BF16 ? 2 : (g.beta == 1.f ? 8 : 4));
+  const int nmt = (int)cdiv(g.M, 16);
   probe_begin(NC_PROBE_GEMM_SKINNY, s);
-  if (g.capc > 0.f) gemm_skinny_kernel<E_SOFTCAP_F32><<<blocks, SK_WAVES * 64, 0, s>>>(p);
-  else if (g.epi == NC_EPI_RELU2_SQ) gemm_skinny_kernel<E_RELU2_SQ><<<blocks, SK_WAVES * 64, 0, s>>>(p);
-  else if (g.cdt == NC_BF16) gemm_skinny_kernel<E_STORE_BF16><<<blocks, SK_WAVES * 64, 0, s>>>(p);
-  else if (g.beta == 1.f) gemm_skinny_kernel<E_ACC_F32><<<blocks, SK_WAVES * 64, 0, s>>>(p);
-  else gemm_skinny_kernel<E_STORE_F32><<<blocks, SK_WAVES * 64, 0, s>>>(p);
+  if (g.capc > 0.f) launch_skinny<E_SOFTCAP_F32>(p, nmt, s);
+  else if (g.epi == NC_EPI_RELU2_SQ) launch_skinny<E_RELU2_SQ>(p, nmt, s);
+  else if (g.cdt == NC_BF16) launch_skinny<E_STORE_BF16>(p, nmt, s);
+  else if (g.beta == 1.f) launch_skinny<E_ACC_F32>(p, nmt, s);
+  else launch_skinny<E_STORE_F32>(p, nmt, s);
   probe_end(NC_PROBE_GEMM_SKINNY, s, bytes);
   return check_launch("gemm_skinny_kernel");
 }
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+// fp32 partial products of the general path's split-K.
+size_t split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   const int s = choose_splits(M, N, K);
   if (s <= 1) return 0;
   return (size_t)s * (size_t)M * (size_t)N * sizeof(float);
 }
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { return split_workspace_bytes(M, N, K); }
 
 // Logit product with a softcap cross-entropy epilogue (internal; the
 // pipelined kernel's K-contiguous form only).
@@ -1361,7 +1379,7 @@ int gemm(const GemmDesc& g, hipStream_t stream) {
   int splits = 1;
   if (epi == E_STORE_F32 || epi == E_ACC_F32) {
     splits = choose_splits(g.M, g.N, g.K);
-    if (splits > 1 && (g.ws == nullptr || g.ws_bytes < gemm_workspace_bytes(g.M, g.N, g.K))) splits = 1;
+    if (splits > 1 && (g.ws == nullptr || g.ws_bytes < split_workspace_bytes(g.M, g.N, g.K))) splits = 1;
   }
   p.k_per_split = splits > 1 ? split_k_per(g.K, splits) : (int)g.K;
   if (splits > 1) splits = (int)cdiv(g.K, p.k_per_split);

@@ -7,7 +7,7 @@
 // every earlier position therefore lets a new position be computed without
 // recomputing the prefix.
 //
-// Supported: bf16 weights, head_dim 128, one K/V head, at most 16 query heads
+// Supported: bf16 weights, head_dim 128, one K/V head, at most 32 query heads
 // and 128 sequences.
 //
 // Cache layout (bf16, caller-owned): [L][2][B][max_len][128], keys then values
@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kHd = 128;    // head_dim of the inference path
 constexpr int kChunk = 64;  // cached positions per decode-attention wave
-constexpr int kMaxHeads = 16;
+constexpr int kMaxHeads = 32;  // query heads: the 32 columns of the attention MFMAs
 constexpr int kMaxSeqs = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -36,15 +36,6 @@ __device__ __forceinline__ float sum16(float v) {
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 16);
   return v;
-}
-
-__device__ __forceinline__ void unpack8(const uint4& u, float (&f)[8]) {
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
 }
 
 __device__ __forceinline__ void unpack4(uint2 u, float (&f)[4]) {
@@ -110,16 +101,48 @@ __device__ __forceinline__ int seq_len_of(const int32_t* lens, int b, int len_ad
 // Decode attention, split over the cache: block (chunk, b) is one wave over
 // positions 64 chunk .. 64 chunk + 63 of sequence b, for all H query heads
 // at once (they share the one K/V head, so each cached row is read once).
-//  scores: lane = position; its 256-byte key row is held in registers and
-//          dotted with each head's query (from LDS, broadcast) by bf16 dot2
-//          instructions with fp32 accumulation;
-//  softmax: per head over the wave's 64 positions, in base 2 (scores are
-//          pre-multiplied by scale log2 e);
-//  values:  lane = (8 dims, one of 4 position phases); each value row is
-//          read as 16-byte pieces and scaled by the probabilities (LDS);
-//          the 4 phases are summed by shuffles.
+// Both products run on the matrix cores (v_mfma_f32_32x32x16_bf16), with
+// the heads as the 32 columns (heads >= H have a zero query):
+//  * the chunk's key and value rows are loaded 4 rows (1 KB) per instruction
+//    and written to LDS in [64][128] tiles whose 16-byte pieces are
+//    XOR-swizzled by row; rows at or past the sequence's length are written
+//    as zeros (so stale cache contents never reach a product);
+//  * S^T = K Q^T: A = key rows (8 consecutive dims per lane from LDS),
+//    B = the query (registers, loaded once); lane l ends with head l mod 32
+//    and 32 of the 64 positions;
+//  * softmax per head in base 2 (scores pre-multiplied by scale log2 e): the
+//    lane's 32 values, then one shuffle with the other half-wave;
+//  * O^T = V^T P: A = V^T read transposed from the row-major value tile
+//    (ds_read_b64_tr_b16), B = the probabilities, rounded to bf16, taken
+//    straight from the score registers (the k-slot order of both operands is
+//    the same permutation of the 64 positions).
 // Writes the unnormalised partial output and (max, sum) per head; chunks at or
 // beyond the sequence's length do nothing.
+typedef __bf16 bf16x4_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
+
+__device__ __forceinline__ int tswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// element offset of (row, 8-dim piece c) in a swizzled [rows][128] tile
+__device__ __forceinline__ int toff(int row, int c) { return row * kHd + ((c ^ tswz(row)) << 3); }
+
+// A operand of X^T from the row-major tile X: output rows are the columns
+// col0 .. col0 + 31 of X; the k-slots of lane l are rows
+// rbase + 8 (e / 4) + 4 (l / 32) + e mod 4, e = 0..7.
+__device__ __forceinline__ bf16x8_t frag_tr(const bf16* S, int rbase, int col0, int lane) {
+  const int g = lane >> 4, p = lane & 15, h = lane >> 5;
+  const int col = col0 + 16 * (g & 1) + 4 * (p & 3);
+  const int r1 = rbase + 4 * h + (p >> 2);
+  const bf16* a1 = S + toff(r1, col >> 3) + (col & 7);
+  const bf16* a2 = S + toff(r1 + 8, col >> 3) + (col & 7);
+  const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)a1);
+  const bf16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)a2);
+  const uint2 u = __builtin_bit_cast(uint2, x), v = __builtin_bit_cast(uint2, y);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(u.x, u.y, v.x, v.y));
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8_t a, bf16x8_t b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 __global__ __launch_bounds__(64) void decode_attn_split_kernel(const bf16* __restrict__ q,
                                                                const bf16* __restrict__ kc,
                                                                const bf16* __restrict__ vc,
@@ -127,120 +150,152 @@ __global__ __launch_bounds__(64) void decode_attn_split_kernel(const bf16* __res
                                                                int max_len, float scale_log2,
                                                                float* __restrict__ part_o,
                                                                float* __restrict__ part_ml) {
-  __shared__ uint4 qs[kMaxHeads][kHd / 8];
-  __shared__ float ps[kChunk][kMaxHeads + 1];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kChunk * kHd];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[kChunk * kHd];
   const int chunk = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int nch = gridDim.x;
   const int len = seq_len_of(lens, b, len_add, max_len);
   const int t0 = chunk * kChunk;
   if (t0 >= len) return;
-  const uint4* q4 = reinterpret_cast<const uint4*>(q + (int64_t)b * H * kHd);
-  for (int i = lane; i < H * (kHd / 8); i += 64) qs[i >> 4][i & 15] = q4[i];
-  const int64_t seq = (int64_t)b * max_len * kHd;
-  const int t = t0 + lane;
-  const bool valid = t < len;
-  uint4 kr[kHd / 8];
-  if (valid) {
-    const uint4* k4 = reinterpret_cast<const uint4*>(kc + seq + (int64_t)t * kHd);
-#pragma unroll
-    for (int i = 0; i < kHd / 8; ++i) kr[i] = k4[i];
-  } else {
-#pragma unroll
-    for (int i = 0; i < kHd / 8; ++i) kr[i] = make_uint4(0, 0, 0, 0);
-  }
-  __syncthreads();
-  float mh[kMaxHeads], lh[kMaxHeads];
-#pragma unroll
-  for (int h = 0; h < kMaxHeads; ++h) {
-    if (h < H) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < kHd / 8; ++i) {
-        const uint4 qq = qs[h][i];
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qq.x), __builtin_bit_cast(bf16x2_t, kr[i].x),
-                                              acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qq.y), __builtin_bit_cast(bf16x2_t, kr[i].y),
-                                              acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qq.z), __builtin_bit_cast(bf16x2_t, kr[i].z),
-                                              acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qq.w), __builtin_bit_cast(bf16x2_t, kr[i].w),
-                                              acc, false);
-      }
-      const float s = valid ? acc * scale_log2 : -INFINITY;
-      const float m = wave_max(s);  // finite: position t0 < len is valid
-      const float e = valid ? __builtin_amdgcn_exp2f(s - m) : 0.f;
-      mh[h] = m;
-      lh[h] = wave_sum(e);
-      ps[lane][h] = e;
-    }
-  }
-  __syncthreads();
-  const int d8 = 8 * (lane & 15), ph = lane >> 4;
-  float o[kMaxHeads][8];
-#pragma unroll
-  for (int h = 0; h < kMaxHeads; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
   const int nvalid = min(kChunk, len - t0);
-  for (int i = ph; i < nvalid; i += 4) {
-    float v[8];
-    unpack8(*reinterpret_cast<const uint4*>(vc + seq + (int64_t)(t0 + i) * kHd + d8), v);
+  const int64_t seq = (int64_t)b * max_len * kHd;
+  // stage the chunk: every load of the wave is 4 whole rows
+  const int rsub = lane >> 4, cp = lane & 15;
+  uint4 kl[kChunk / 4], vl[kChunk / 4];
 #pragma unroll
-    for (int h = 0; h < kMaxHeads; ++h) {
-      if (h < H) {
-        const float pw = ps[i][h];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] += pw * v[e];
-      }
-    }
+  for (int g = 0; g < kChunk / 4; ++g) {
+    const int row = 4 * g + rsub;
+    const int64_t off = seq + (int64_t)(t0 + row) * kHd + 8 * cp;
+    const bool ok = row < nvalid;
+    kl[g] = ok ? *reinterpret_cast<const uint4*>(kc + off) : make_uint4(0, 0, 0, 0);
+    vl[g] = ok ? *reinterpret_cast<const uint4*>(vc + off) : make_uint4(0, 0, 0, 0);
   }
-  const int64_t pbase = ((int64_t)b * nch + chunk) * H;
+  // the query of head lane mod 32, dims 16 ks + 8 h .. + 7 (zero past H)
+  const int hcol = lane & 31, h = lane >> 5;
+  bf16x8_t qreg[kHd / 16];
 #pragma unroll
-  for (int h = 0; h < kMaxHeads; ++h) {
-    if (h < H) {
+  for (int ks = 0; ks < kHd / 16; ++ks)
+    qreg[ks] = hcol < H ? *reinterpret_cast<const bf16x8_t*>(q + ((int64_t)b * H + hcol) * kHd + 16 * ks + 8 * h)
+                        : bf16x8_t{};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        o[h][e] += __shfl_xor(o[h][e], 16, 64);
-        o[h][e] += __shfl_xor(o[h][e], 32, 64);
-      }
-      if (ph == 0) {
-        float4* dst = reinterpret_cast<float4*>(part_o + (pbase + h) * kHd + d8);
-        dst[0] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
-        dst[1] = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
-      }
-      if (lane == 0) {
-        part_ml[2 * (pbase + h)] = mh[h];
-        part_ml[2 * (pbase + h) + 1] = lh[h];
-      }
+  for (int g = 0; g < kChunk / 4; ++g) {
+    const int row = 4 * g + rsub;
+    *reinterpret_cast<uint4*>(Ks + toff(row, cp)) = kl[g];
+    *reinterpret_cast<uint4*>(Vs + toff(row, cp)) = vl[g];
+  }
+  __syncthreads();
+  f32x16 s[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kHd / 16; ++ks)
+      s[st] = mfma32(*reinterpret_cast<const bf16x8_t*>(Ks + toff(st * 32 + hcol, 2 * ks + h)), qreg[ks], s[st]);
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int pos = st * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const float x = pos < nvalid ? s[st][r] * scale_log2 : -INFINITY;
+      s[st][r] = x;
+      m = fmaxf(m, x);
+    }
+  m = fmaxf(m, __shfl_xor(m, 32, 64));  // finite: position 0 of the chunk is valid
+  float l = 0.f;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = __builtin_amdgcn_exp2f(s[st][r] - m);
+      s[st][r] = pr;
+      l += pr;
+    }
+  l += __shfl_xor(l, 32, 64);
+  f32x16 o[kHd / 32];
+#pragma unroll
+  for (int ht = 0; ht < kHd / 32; ++ht)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[ht][i] = 0.f;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const int bb = 8 * jp;
+      const bf16x8_t pb = __builtin_bit_cast(
+          bf16x8_t, make_uint4(pack_bf16x2(s[st][bb], s[st][bb + 1]), pack_bf16x2(s[st][bb + 2], s[st][bb + 3]),
+                               pack_bf16x2(s[st][bb + 4], s[st][bb + 5]), pack_bf16x2(s[st][bb + 6], s[st][bb + 7])));
+#pragma unroll
+      for (int ht = 0; ht < kHd / 32; ++ht) o[ht] = mfma32(frag_tr(Vs, st * 32 + 16 * jp, ht * 32, lane), pb, o[ht]);
+    }
+  if (hcol < H) {
+    const int64_t pi = ((int64_t)b * nch + chunk) * H + hcol;
+    float* dst = part_o + pi * kHd;
+#pragma unroll
+    for (int ht = 0; ht < kHd / 32; ++ht)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        *reinterpret_cast<float4*>(dst + ht * 32 + 8 * rq + 4 * h) =
+            make_float4(o[ht][4 * rq], o[ht][4 * rq + 1], o[ht][4 * rq + 2], o[ht][4 * rq + 3]);
+    if (h == 0) {
+      part_ml[2 * pi] = m;
+      part_ml[2 * pi + 1] = l;
     }
   }
 }
 
-// Combine the chunks of each (sequence, head) in increasing chunk order:
-// o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c, M = max_c m_c.  One
-// thread per output element; a sequence of length 0 gets zeros.
+// Combine the chunks of each (sequence, head): o = sum_c 2^(m_c - M) o_c /
+// sum_c 2^(m_c - M) l_c, M = max_c m_c.  One block per (head, sequence),
+// one thread per output dimension; the chunk statistics are reduced across
+// the block in a fixed tree order, the outputs summed in chunk order
+// (deterministic), with the independent chunk loads unrolled so that their
+// latencies overlap.  A sequence of length 0 gets zeros.
 __global__ __launch_bounds__(kHd) void decode_attn_combine_kernel(const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml,
                                                                   const int32_t* __restrict__ lens, int len_add,
                                                                   int H, int max_len, int nch,
                                                                   bf16* __restrict__ out) {
-  const int h = blockIdx.x, b = blockIdx.y, dim = threadIdx.x;
+  __shared__ float red[kHd];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int len = seq_len_of(lens, b, len_add, max_len);
   const int used = (int)cdiv(len, kChunk);
-  bf16* dst = out + ((int64_t)b * H + h) * kHd + dim;
+  bf16* dst = out + ((int64_t)b * H + h) * kHd + tid;
   if (used == 0) {
     *dst = 0;
     return;
   }
   const int64_t base = (int64_t)b * nch * H + h;
-  float M = -INFINITY;
-  for (int c = 0; c < used; ++c) M = fmaxf(M, part_ml[2 * (base + (int64_t)c * H)]);
-  float L = 0.f, O = 0.f;
+  float mx = -INFINITY;
+  for (int c = tid; c < used; c += kHd) mx = fmaxf(mx, part_ml[2 * (base + (int64_t)c * H)]);
+  red[tid] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int w = kHd / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float ls = 0.f;
+  for (int c = tid; c < used; c += kHd) {
+    const int64_t i = base + (int64_t)c * H;
+    ls += __builtin_amdgcn_exp2f(part_ml[2 * i] - M) * part_ml[2 * i + 1];
+  }
+  red[tid] = ls;
+  __syncthreads();
+#pragma unroll
+  for (int w = kHd / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  const float L = red[0];
+  float O = 0.f;
+#pragma unroll 8
   for (int c = 0; c < used; ++c) {
     const int64_t i = base + (int64_t)c * H;
-    const float w = __builtin_amdgcn_exp2f(part_ml[2 * i] - M);
-    L += w * part_ml[2 * i + 1];
-    O += w * part_o[i * kHd + dim];
+    O += __builtin_amdgcn_exp2f(part_ml[2 * i] - M) * part_o[i * kHd + tid];
   }
   *dst = f2bf(O / L);
 }

@@ -184,7 +184,7 @@ int nc_step_fwd_bwd(const nc_config* cfg, const nc_params* params, const nc_grad
  * value for every position already seen.  By causality the logits at a
  * position depend on tokens up to it only, so prefill and decode return the
  * full forward's softcapped logits row at that position.
- * Supported: dtype NC_BF16, head_dim 128, n_kv_head 1, n_head <= 16,
+ * Supported: dtype NC_BF16, head_dim 128, n_kv_head 1, n_head <= 32,
  * batch <= 128; d_model and d_ff multiples of 64, vocab a multiple of 32.
  *   kv_cache: nc_kv_cache_bytes(cfg, max_len) bytes, 16-byte aligned, bf16
  *             [L][2][B][max_len][128] (keys, then values, of each layer).
@@ -225,7 +225,7 @@ int nc_decode_step(const nc_config* cfg, const nc_params* params, const int32_t*
  *   (fp32 partial results per 64 cached positions).
  * Work is split over 64-position chunks and the chunks are combined in a
  * fixed order (deterministic).  Errors: NC_ERR_INVALID_ARG,
- * NC_ERR_UNSUPPORTED (head_dim != 128, H > 16), NC_ERR_WORKSPACE. */
+ * NC_ERR_UNSUPPORTED (head_dim != 128, H > 32), NC_ERR_WORKSPACE. */
 size_t nc_mqa_decode_workspace_bytes(int B, int H, int max_len);
 int nc_mqa_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* lens, int B,
                        int H, int hd, int max_len, float scale, void* o, void* ws, size_t ws_bytes,
@@ -327,6 +327,9 @@ int nc_mqa_attn_bwd(const void* qkv, const void* o, const void* dout, const floa
  *                    i.e. the relu^2 backward from the stored activation.
  * dtype NC_F32 runs the same contraction on fp32 operands (a plain path for
  * small fp32 problems; epilogues as above with fp32 everywhere).
+ * Small M (decoding): bf16 (transA=0, transB=1) products with 1 <= M <= 128,
+ * N a multiple of 16 and K of 64, with NC_EPI_STORE or NC_EPI_RELU2_SQ, take
+ * a kernel that streams B once (M, ldc and C need no alignment there).
  * ws (may be NULL): enables deterministic split-K for tall-K problems; see
  * nc_gemm_workspace_bytes. */
 typedef enum {
