@@ -45,6 +45,10 @@ struct GemmDesc {
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int gemm(const GemmDesc& g, hipStream_t stream);
+// Small-M form (gemm_small.hip): bf16 x W^T with M <= 128; gemm() routes
+// eligible shapes there.
+bool skinny_ok(const GemmDesc& g);
+int gemm_skinny(const GemmDesc& g, hipStream_t stream);
 // dst [C, R] = src [R, C]^T for 2- or 4-byte elements.
 int transpose(const void* src, int64_t R, int64_t C, int elem_bytes, void* dst, hipStream_t s);
 
