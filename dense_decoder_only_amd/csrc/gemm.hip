@@ -64,6 +64,9 @@ struct MfmaParams {
   const float* xlse;
   float* xpart;
   float* xztgt;
+  // > 0: split-K launched as one flat grid of tiles x kxcd blocks, split s
+  // on XCD s mod 8 (gemm_pipe_kernel only; kxcd a multiple of 8)
+  int kxcd = 0;
   int xv0;
 };
 
@@ -195,6 +198,12 @@ __device__ __forceinline__ void store_tile(bf16* __restrict__ S, int tid, const 
 #endif
 #ifndef NC_GEMM_XCD
 #define NC_GEMM_XCD 1     // XCD-aware grouped tile order
+#endif
+#ifndef NC_GEMM_KXCD
+#define NC_GEMM_KXCD 1    // split-K with a multiple of 8 splits: whole k-splits per XCD
+#endif
+#ifndef NC_GEMM_SPLIT_MODEL
+#define NC_GEMM_SPLIT_MODEL 1  // split count from the rounds x k-length model
 #endif
 #ifndef NC_GEMM_GROUP_M
 #define NC_GEMM_GROUP_M 4
@@ -865,9 +874,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
-  int bid = blockIdx.x;
+  int bid = blockIdx.x, split = blockIdx.z;
 #if NC_GEMM_XCD
-  {
+  if (p.kxcd) {
+    // Split-K: blocks are dealt round-robin to the 8 XCDs, so block id i runs
+    // on XCD i mod 8.  Give every XCD whole k-splits (split s on XCD s mod 8):
+    // an XCD then reads only its own k-ranges of the panels, and its tiles
+    // (in the grouped order below) share those ranges in its L2.
+    const int nb = p.tiles_m * p.tiles_n;
+    const int j = bid >> 3;
+    split = (bid & 7) + 8 * (j / nb);
+    bid = j % nb;
+    // the partial-product epilogue indexes its slice by blockIdx.z (0 here)
+    p.C = static_cast<float*>(p.C) + (int64_t)split * p.M * p.N;
+  } else {
     const int nb = p.tiles_m * p.tiles_n;
     const int per = nb >> 3;
     if (bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
@@ -880,7 +900,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
 #endif
   const int m0 = tm * BM, n0 = tn * BN;
-  const int kbeg = blockIdx.z * p.k_per_split;
+  const int kbeg = split * p.k_per_split;
   int kend = kbeg + p.k_per_split;
   kend = kend < p.K ? kend : p.K;
   const int nk = (kend - kbeg) / BK;
@@ -984,8 +1004,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 template <bool TN>
-hipError_t launch_pipe(int epi, const MfmaParams& p, int splits, hipStream_t s) {
+hipError_t launch_pipe(int epi, const MfmaParams& p0, int splits, hipStream_t s) {
+  MfmaParams p = p0;
   dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
+  p.kxcd = 0;
+  if (NC_GEMM_KXCD && NC_GEMM_XCD && epi == E_PARTIAL && splits > 1 && splits % 8 == 0) {
+    p.kxcd = splits;
+    grid = dim3(p.tiles_m * p.tiles_n * splits, 1, 1);
+  }
   switch (epi) {
     case E_STORE_F32: gemm_pipe_kernel<E_STORE_F32, TN><<<grid, 512, 0, s>>>(p); break;
     case E_ACC_F32: gemm_pipe_kernel<E_ACC_F32, TN><<<grid, 512, 0, s>>>(p); break;
@@ -1043,13 +1069,27 @@ hipError_t launch_mfma(int epi, const MfmaParams& p, int splits, bool direct, hi
   return launch_mfma<AK, BKC, false>(epi, p, splits, s);
 }
 
+// Split-K count for few-tile, long-K products.  One 512-thread block fits a
+// CU (128 KB of LDS), so blocks run in rounds of 256; the estimated time is
+// rounds x (k per split + a fixed per-block cost of ~8 k-steps: prologue,
+// drain and the fp32 partial store), minimised over the split count.
 int choose_splits(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = cdiv(M, BM) * cdiv(N, BN);
   if (tiles >= 512 || K < 4096) return 1;
-  int64_t s = cdiv(640, tiles);
   const int64_t max_s = K / 1024;
+#if NC_GEMM_SPLIT_MODEL
+  int64_t best = 1, best_cost = -1;
+  for (int64_t s = 1; s <= max_s; ++s) {
+    const int64_t kps = cdiv(cdiv(K, s), BK) * BK;
+    const int64_t cost = cdiv(tiles * s, 256) * (kps + 8 * BK);
+    if (best_cost < 0 || cost < best_cost) best = s, best_cost = cost;
+  }
+  return (int)best;
+#else
+  int64_t s = cdiv(640, tiles);
   if (s > max_s) s = max_s;
   return s < 1 ? 1 : (int)s;
+#endif
 }
 
 int split_k_per(int64_t K, int splits) { return (int)(cdiv(cdiv(K, splits), BK) * BK); }
