@@ -981,8 +981,49 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   constexpr int SROW = 68;
   float* stage = reinterpret_cast<float*>(lds) + wave * (32 * SROW);
+  // Epilogue inputs read from memory are loaded ahead of their use so that
+  // their latency overlaps the LDS staging: the relu^2 backward's stored
+  // activation for the whole sub-tile up front, the accumulated fp32 C one
+  // 32-row slab ahead.  Element (i, it) of this lane is row
+  // m0 + wm 128 + 32 i + (64 it + lane) / 16, columns n0 + wn 64 + 4 (lane % 16) + 0..3.
+  constexpr bool PF_AUX = EPI == E_RELU2_BWD || EPI == E_RELU2_BWD_SQ;
+  constexpr bool PF_C = EPI == E_ACC_F32;
+  const int er0 = m0 + wm * 128 + (lane >> 4), ec = n0 + wn * 64 + (lane & 15) * 4;
+  uint2 pa[PF_AUX ? 4 : 1][8];
+  float4 pc[2][8];
+  if constexpr (PF_AUX) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int grow = er0 + i * 32 + 4 * it;
+        pa[i][it] = grow < p.M && ec < p.N ? *reinterpret_cast<const uint2*>(p.aux + (int64_t)grow * p.ldc + ec)
+                                           : make_uint2(0, 0);
+      }
+  }
+  if constexpr (PF_C) {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int grow = er0 + 4 * it;
+      pc[0][it] = grow < p.M && ec < p.N
+                      ? *reinterpret_cast<const float4*>(static_cast<const float*>(p.C) + (int64_t)grow * p.ldc + ec)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    if constexpr (PF_C) {
+      if (i + 1 < 4) {
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int grow = er0 + (i + 1) * 32 + 4 * it;
+          pc[(i + 1) & 1][it] =
+              grow < p.M && ec < p.N
+                  ? *reinterpret_cast<const float4*>(static_cast<const float*>(p.C) + (int64_t)grow * p.ldc + ec)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -990,13 +1031,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         *reinterpret_cast<float4*>(stage + (lane & 31) * SROW + j * 32 + 8 * q + 4 * (lane >> 5)) =
             make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
     __syncthreads();
+#pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int idx = it * 64 + lane;
       const int row = idx >> 4, c4 = (idx & 15) * 4;
       const float4 v = *reinterpret_cast<const float4*>(stage + row * SROW + c4);
       const int grow = m0 + wm * 128 + i * 32 + row, gcol = n0 + wn * 64 + c4;
-      if constexpr (EPI == E_XENT_FWD) xent_fwd4(p, v, grow, gcol, n0 + wn * 64);
-      else if (grow < p.M && gcol < p.N) epilogue4<EPI>(p, v, grow, gcol);
+      if constexpr (EPI == E_XENT_FWD) {
+        xent_fwd4(p, v, grow, gcol, n0 + wn * 64);
+      } else if (grow < p.M && gcol < p.N) {
+        const int64_t off = (int64_t)grow * p.ldc + gcol;
+        if constexpr (EPI == E_RELU2_BWD_SQ) {
+          const uint2 q = pa[i][it];
+          const float r0 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.x & 0xffffu)));
+          const float r1 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.x >> 16)));
+          const float r2 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.y & 0xffffu)));
+          const float r3 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.y >> 16)));
+          *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + off) =
+              make_uint2(pack_bf16x2(v.x * 2.f * r0, v.y * 2.f * r1), pack_bf16x2(v.z * 2.f * r2, v.w * 2.f * r3));
+        } else if constexpr (EPI == E_RELU2_BWD) {
+          const uint2 u = pa[i][it];
+          const float u0 = bf2f((bf16)(u.x & 0xffffu)), u1 = bf2f((bf16)(u.x >> 16));
+          const float u2 = bf2f((bf16)(u.y & 0xffffu)), u3 = bf2f((bf16)(u.y >> 16));
+          *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + off) =
+              make_uint2(pack_bf16x2(v.x * 2.f * fmaxf(u0, 0.f), v.y * 2.f * fmaxf(u1, 0.f)),
+                         pack_bf16x2(v.z * 2.f * fmaxf(u2, 0.f), v.w * 2.f * fmaxf(u3, 0.f)));
+        } else if constexpr (EPI == E_ACC_F32) {
+          const float4 o = pc[i & 1][it];
+          *reinterpret_cast<float4*>(static_cast<float*>(p.C) + off) =
+              make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+        } else {
+          epilogue4<EPI>(p, v, grow, gcol);
+        }
+      }
     }
     __syncthreads();
   }
