@@ -205,6 +205,9 @@ __device__ __forceinline__ void store_tile(bf16* __restrict__ S, int tid, const 
 #ifndef NC_GEMM_SPLIT_MODEL
 #define NC_GEMM_SPLIT_MODEL 1  // split count from the rounds x k-length model
 #endif
+#ifndef NC_GEMM_SPLIT_C0
+#define NC_GEMM_SPLIT_C0 8     // fixed per-block cost in the model, in k-steps
+#endif
 #ifndef NC_GEMM_GROUP_M
 #define NC_GEMM_GROUP_M 4
 #endif
@@ -1148,7 +1151,7 @@ int choose_splits(int64_t M, int64_t N, int64_t K) {
   int64_t best = 1, best_cost = -1;
   for (int64_t s = 1; s <= max_s; ++s) {
     const int64_t kps = cdiv(cdiv(K, s), BK) * BK;
-    const int64_t cost = cdiv(tiles * s, 256) * (kps + 8 * BK);
+    const int64_t cost = cdiv(tiles * s, 256) * (kps + NC_GEMM_SPLIT_C0 * BK);
     if (best_cost < 0 || cost < best_cost) best = s, best_cost = cost;
   }
   return (int)best;
