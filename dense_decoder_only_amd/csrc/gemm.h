@@ -41,6 +41,10 @@ struct GemmDesc {
   // capc > 0: C (fp32) = capc tanh(acc / capc), the logit softcap; only for
   // the small-M form (bf16, x W^T, M <= 128), which decoding uses.
   float capc = 0.f;
+  // sk_split > 1 (small-M form only, fp32 C, plain store): K is split over
+  // sk_split blocks per column slab and C receives sk_split fp32 partial
+  // products [sk_split][M][ldc] for the consumer to add in a fixed order.
+  int sk_split = 1;
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);

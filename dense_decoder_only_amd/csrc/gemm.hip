@@ -1249,6 +1249,8 @@ int gemm(const GemmDesc& g, hipStream_t stream) {
                "gemm: beta = 1 needs an fp32 C and the plain store epilogue");
   if (g.capc > 0.f)
     NC_REQUIRE(skinny_ok(g), NC_ERR_UNSUPPORTED, "gemm: the softcap epilogue is for bf16 products with M <= 128");
+  if (g.sk_split > 1)
+    NC_REQUIRE(skinny_ok(g), NC_ERR_UNSUPPORTED, "gemm: split partial products are for bf16 products with M <= 128");
   if (skinny_ok(g)) return gemm_skinny(g, stream);
 
   if (g.dtype == NC_F32) {

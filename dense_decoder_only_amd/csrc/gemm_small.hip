@@ -52,6 +52,7 @@ struct SkinnyParams {
   int64_t ldc;
   int M, N, K;
   float capc, inv_capc;
+  int ksplit;
 };
 
 template <int EPI>
@@ -72,9 +73,13 @@ __device__ __forceinline__ void skinny_store1(const SkinnyParams& p, int m, int 
 }
 
 // NMT: 16-row tiles of A held per wave (1, 2, 4 or 8; rows >= M are zero).
-template <int EPI, int NMT>
-__global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny_kernel(SkinnyParams p) {
-  __shared__ float red[SK_WAVES][4][64];
+// WAVES: 16 (few output columns: more waves share a slab's k-chunks) or 8
+// (many columns: two blocks fit a CU).  blockIdx.y = k-split: block (x, y)
+// covers k-chunks [y cps, (y + 1) cps) and, with p.ksplit > 1, writes its
+// plain fp32 sums to slice y of C ([ksplit][M][ldc]).
+template <int EPI, int NMT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(SkinnyParams p) {
+  __shared__ float red[WAVES][4][64];
   // The wave index is made wave-uniform explicitly: the chunk guards below
   // must compile to scalar branches.  Under an EXEC-masked branch an MFMA
   // still runs (it ignores EXEC) and would add whatever the skipped loads
@@ -82,18 +87,20 @@ __global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny_kernel(SkinnyParams
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 16;
-  constexpr int nmt = NMT;
   const int nch = p.K >> 6;
+  const int cps = (nch + p.ksplit - 1) / p.ksplit;
+  const int c_lo = blockIdx.y * cps, c_hi = min(nch, c_lo + cps);
+  if (p.ksplit > 1) p.C = static_cast<float*>(p.C) + (int64_t)blockIdx.y * p.M * p.ldc;
   f32x4_t acc[NMT];
 #pragma unroll
   for (int i = 0; i < NMT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const bf16* wrow = p.W + (int64_t)(n0 + r) * p.ldw + 16 * g;
-  for (int cb = wave; cb < nch; cb += SK_CPW * SK_WAVES) {
+  for (int cb = c_lo + wave; cb < c_hi; cb += SK_CPW * WAVES) {
     bf16x8_t w[SK_CPW][2];
 #pragma unroll
     for (int j = 0; j < SK_CPW; ++j) {
-      const int c = cb + j * SK_WAVES;
-      if (c < nch) {
+      const int c = cb + j * WAVES;
+      if (c < c_hi) {
         w[j][0] = *reinterpret_cast<const bf16x8_t*>(wrow + (c << 6));
         w[j][1] = *reinterpret_cast<const bf16x8_t*>(wrow + (c << 6) + 8);
       } else {  // never multiplied (the MFMAs below are skipped), but defined
@@ -103,27 +110,25 @@ __global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny_kernel(SkinnyParams
     }
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
-      {
-        const int m = mt * 16 + r;
-        bf16x8_t x[SK_CPW][2];
+      const int m = mt * 16 + r;
+      bf16x8_t x[SK_CPW][2];
 #pragma unroll
-        for (int j = 0; j < SK_CPW; ++j) {
-          const int c = cb + j * SK_WAVES;
-          if (c < nch && m < p.M) {
-            const bf16* xr = p.A + (int64_t)m * p.lda + (c << 6) + 16 * g;
-            x[j][0] = *reinterpret_cast<const bf16x8_t*>(xr);
-            x[j][1] = *reinterpret_cast<const bf16x8_t*>(xr + 8);
-          } else {
-            x[j][0] = bf16x8_t{};
-            x[j][1] = bf16x8_t{};
-          }
+      for (int j = 0; j < SK_CPW; ++j) {
+        const int c = cb + j * WAVES;
+        if (c < c_hi && m < p.M) {
+          const bf16* xr = p.A + (int64_t)m * p.lda + (c << 6) + 16 * g;
+          x[j][0] = *reinterpret_cast<const bf16x8_t*>(xr);
+          x[j][1] = *reinterpret_cast<const bf16x8_t*>(xr + 8);
+        } else {
+          x[j][0] = bf16x8_t{};
+          x[j][1] = bf16x8_t{};
         }
+      }
 #pragma unroll
-        for (int j = 0; j < SK_CPW; ++j) {
-          if (cb + j * SK_WAVES < nch) {
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[j][0], x[j][0], acc[mt], 0, 0, 0);
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[j][1], x[j][1], acc[mt], 0, 0, 0);
-          }
+      for (int j = 0; j < SK_CPW; ++j) {
+        if (cb + j * WAVES < c_hi) {
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[j][0], x[j][0], acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[j][1], x[j][1], acc[mt], 0, 0, 0);
         }
       }
     }
@@ -131,7 +136,7 @@ __global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny_kernel(SkinnyParams
   // fixed-order reduction over the waves, one 16 x 16 tile at a time
   const int t = threadIdx.x, pl = t & 63, q = (t >> 6) & 3;
 #pragma unroll
-  for (int mt = 0; mt < nmt; ++mt) {
+  for (int mt = 0; mt < NMT; ++mt) {
     if (mt * 16 < p.M) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[mt][i];
@@ -139,7 +144,7 @@ __global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny_kernel(SkinnyParams
       if (t < 256) {
         float v = 0.f;
 #pragma unroll
-        for (int w = 0; w < SK_WAVES; ++w) v += red[w][q][pl];
+        for (int w = 0; w < WAVES; ++w) v += red[w][q][pl];
         const int m = mt * 16 + (pl & 15);
         if (m < p.M) skinny_store1<EPI>(p, m, n0 + 4 * (pl >> 4) + q, v);
       }
@@ -148,13 +153,20 @@ __global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny_kernel(SkinnyParams
   }
 }
 
+template <int EPI, int WAVES>
+void launch_skinny_w(const SkinnyParams& p, int nmt, hipStream_t s) {
+  const dim3 grid((unsigned)(p.N / 16), (unsigned)p.ksplit);
+  if (nmt <= 1) gemm_skinny_kernel<EPI, 1, WAVES><<<grid, WAVES * 64, 0, s>>>(p);
+  else if (nmt <= 2) gemm_skinny_kernel<EPI, 2, WAVES><<<grid, WAVES * 64, 0, s>>>(p);
+  else if (nmt <= 4) gemm_skinny_kernel<EPI, 4, WAVES><<<grid, WAVES * 64, 0, s>>>(p);
+  else gemm_skinny_kernel<EPI, 8, WAVES><<<grid, WAVES * 64, 0, s>>>(p);
+}
+
 template <int EPI>
 void launch_skinny(const SkinnyParams& p, int nmt, hipStream_t s) {
-  const unsigned blocks = (unsigned)(p.N / 16);
-  if (nmt <= 1) gemm_skinny_kernel<EPI, 1><<<blocks, SK_WAVES * 64, 0, s>>>(p);
-  else if (nmt <= 2) gemm_skinny_kernel<EPI, 2><<<blocks, SK_WAVES * 64, 0, s>>>(p);
-  else if (nmt <= 4) gemm_skinny_kernel<EPI, 4><<<blocks, SK_WAVES * 64, 0, s>>>(p);
-  else gemm_skinny_kernel<EPI, 8><<<blocks, SK_WAVES * 64, 0, s>>>(p);
+  // products with blocks to spare (>= 256 slabs x splits): 8-wave blocks, two per CU
+  if ((p.N / 16) * p.ksplit >= 256) launch_skinny_w<EPI, 8>(p, nmt, s);
+  else launch_skinny_w<EPI, 16>(p, nmt, s);
 }
 
 // Small-M form if the shapes and epilogue allow it; returns false to let the
@@ -166,6 +178,8 @@ bool skinny_ok(const GemmDesc& g) {
   if (g.M < 1 || g.M > SK_MMAX || g.N % 16 != 0 || g.K % 64 != 0) return false;
   if (g.lda % 8 != 0 || g.ldb % 8 != 0) return false;
   if (!aligned16(g.A) || !aligned16(g.B)) return false;
+  if (g.sk_split > 1)
+    return g.sk_split <= g.K / 64 && g.cdt == NC_F32 && g.beta == 0.f && g.epi == NC_EPI_STORE && g.capc == 0.f;
   if (g.capc > 0.f) return g.cdt == NC_F32 && g.beta == 0.f && g.epi == NC_EPI_STORE;
   if (g.epi == NC_EPI_RELU2_SQ) return g.cdt == NC_BF16;
   return g.epi == NC_EPI_STORE;
@@ -184,8 +198,9 @@ int gemm_skinny(const GemmDesc& g, hipStream_t s) {
   p.K = (int)g.K;
   p.capc = g.capc;
   p.inv_capc = g.capc > 0.f ? 1.f / g.capc : 0.f;
+  p.ksplit = g.sk_split > 1 ? g.sk_split : 1;
   const double bytes = 2.0 * (double)g.N * g.K + 2.0 * (double)g.M * g.K +
-                       (double)g.M * g.N * (g.cdt == NC_BF16 ? 2 : (g.beta == 1.f ? 8 : 4));
+                       (double)g.M * g.N * (g.cdt == NC_BF16 ? 2 : (g.beta == 1.f ? 8 : 4)) * p.ksplit;
   const int nmt = (int)cdiv(g.M, 16);
   probe_begin(NC_PROBE_GEMM_SKINNY, s);
   if (g.capc > 0.f) launch_skinny<E_SOFTCAP_F32>(p, nmt, s);

@@ -46,13 +46,27 @@ __device__ __forceinline__ void unpack4(uint2 u, float (&f)[4]) {
 }
 
 // RoPE + per-head RMS norm of one new token per sequence, at its own
-// position pos[b]; the key and the value are appended to the cache at that
-// position, the query heads go to qhat [B, H, 128].  A 16-lane group per head
+// position pos[b]; the key and the value (rounded to bf16) are appended to
+// the cache at that position, the query heads go to qhat [B, H, 128].  A 16-lane group per head
 // (lane j owns the pairs (i, i + 64), i = 4 j .. 4 j + 3); the angles are
 // computed in fp64 and rounded to fp32 as for the training table, so a
 // position gets the same rotation in both paths.  A position outside
 // [0, max_len) raises the flag and leaves that sequence's outputs unwritten.
-__global__ __launch_bounds__(256) void decode_rope_append_kernel(const bf16* __restrict__ qkv,
+// The projection arrives as `parts` fp32 partial sums [parts][B][(H+2) 128]
+// (k-split small-M GEMM); they are added in order here.
+__device__ __forceinline__ float4 sum_parts4(const float* x, int parts, int64_t stride) {
+  float4 a = *reinterpret_cast<const float4*>(x);
+  for (int k = 1; k < parts; ++k) {
+    const float4 b = *reinterpret_cast<const float4*>(x + k * stride);
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+  }
+  return a;
+}
+
+__global__ __launch_bounds__(256) void decode_rope_append_kernel(const float* __restrict__ qkv, int parts, int B,
                                                                  const int32_t* __restrict__ pos, int H, double base,
                                                                  float eps, int max_len, bf16* __restrict__ qhat,
                                                                  bf16* __restrict__ kc, bf16* __restrict__ vc,
@@ -64,17 +78,19 @@ __global__ __launch_bounds__(256) void decode_rope_append_kernel(const bf16* __r
     return;
   }
   const int j = threadIdx.x & 15;
-  const bf16* row = qkv + (int64_t)b * (H + 2) * kHd;
+  const int64_t stride = (int64_t)B * (H + 2) * kHd;
+  const float* row = qkv + (int64_t)b * (H + 2) * kHd;
   const int64_t cache_row = ((int64_t)b * max_len + p) * kHd;
   for (int head = threadIdx.x >> 4; head < H + 2; head += 16) {
-    const bf16* x = row + head * kHd;
-    if (head == H + 1) {  // value: copied as is
-      *reinterpret_cast<uint4*>(vc + cache_row + 8 * j) = *reinterpret_cast<const uint4*>(x + 8 * j);
+    const float* x = row + head * kHd;
+    if (head == H + 1) {  // value: rounded to bf16 as is
+      const float4 v0 = sum_parts4(x + 8 * j, parts, stride), v1 = sum_parts4(x + 8 * j + 4, parts, stride);
+      *reinterpret_cast<uint4*>(vc + cache_row + 8 * j) = make_uint4(
+          pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y), pack_bf16x2(v1.z, v1.w));
       continue;
     }
-    float a[4], c[4];
-    unpack4(*reinterpret_cast<const uint2*>(x + 4 * j), a);
-    unpack4(*reinterpret_cast<const uint2*>(x + 64 + 4 * j), c);
+    const float4 a4 = sum_parts4(x + 4 * j, parts, stride), c4 = sum_parts4(x + 64 + 4 * j, parts, stride);
+    const float a[4] = {a4.x, a4.y, a4.z, a4.w}, c[4] = {c4.x, c4.y, c4.z, c4.w};
     float ya[4], yb[4], ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -315,6 +331,46 @@ __global__ __launch_bounds__(256) void cache_fill_kernel(const bf16* __restrict_
   *reinterpret_cast<uint4*>(dst) = v;
 }
 
+// Decode residual update and norm, one block per token row (d / 4 threads,
+// one float4 each, d <= 2048): x += sum over k of part[k] (k in order: the
+// k-split partial products of the projection that feeds the residual), then
+// y = x / sqrt(mean(x^2) + eps) in bf16.  All loads of a thread are issued
+// before the first add.
+constexpr int kMaxParts = 8;
+
+__global__ __launch_bounds__(512) void residual_rmsnorm_kernel(float* __restrict__ x, const float* __restrict__ part,
+                                                               int parts, int rows, int d, float eps,
+                                                               bf16* __restrict__ y) {
+  __shared__ float red[8];
+  const int row = blockIdx.x, t = threadIdx.x, c = 4 * t;
+  const int64_t off = (int64_t)row * d + c, stride = (int64_t)rows * d;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < d) {
+    float4 pv[kMaxParts];
+#pragma unroll
+    for (int q = 0; q < kMaxParts; ++q)
+      if (q < parts) pv[q] = *reinterpret_cast<const float4*>(part + q * stride + off);
+    a = *reinterpret_cast<const float4*>(x + off);
+#pragma unroll
+    for (int q = 0; q < kMaxParts; ++q)
+      if (q < parts) {
+        a.x += pv[q].x;
+        a.y += pv[q].y;
+        a.z += pv[q].z;
+        a.w += pv[q].w;
+      }
+    *reinterpret_cast<float4*>(x + off) = a;
+  }
+  float ss = wave_sum(a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  ss = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) ss += red[w];
+  const float r = 1.f / sqrtf(ss / (float)d + eps);
+  if (c < d)
+    *reinterpret_cast<uint2*>(y + off) = make_uint2(pack_bf16x2(a.x * r, a.y * r), pack_bf16x2(a.z * r, a.w * r));
+}
+
 // rows_out[b] = x[b T + T - 1] (fp32 rows of width d): the last position of
 // every prompt.
 __global__ __launch_bounds__(256) void last_rows_kernel(const float* __restrict__ x, int B, int T, int d,
@@ -335,6 +391,7 @@ int validate_infer(const nc_config* c, int max_len) {
   NC_REQUIRE((int64_t)c->n_head * kHd == c->d_model, NC_ERR_INVALID_ARG, "infer: n_head * head_dim != d_model");
   NC_REQUIRE(c->n_head <= kMaxHeads, NC_ERR_UNSUPPORTED, "infer: at most %d query heads", kMaxHeads);
   NC_REQUIRE(c->batch <= kMaxSeqs, NC_ERR_UNSUPPORTED, "infer: at most %d sequences", kMaxSeqs);
+  NC_REQUIRE(c->d_model <= 2048, NC_ERR_UNSUPPORTED, "infer: d_model must be at most 2048");
   NC_REQUIRE(c->d_model % 64 == 0 && c->d_ff % 64 == 0 && c->vocab % 32 == 0, NC_ERR_UNSUPPORTED,
              "infer: d_model and d_ff must be multiples of 64, vocab of 32");
   NC_REQUIRE(max_len >= c->seq_len, NC_ERR_INVALID_ARG, "infer: max_len %d is below the prompt length %d", max_len,
@@ -346,14 +403,23 @@ struct InferWs {
   int32_t* flag;
   // decode (one token per sequence)
   float *dx, *drstd;
-  void *da, *dqkv, *dq, *dout, *dm, *da2, *dh;
+  void *da, *dq, *dout, *dm, *da2, *dh;
   float *part_o, *part_ml;
+  float *part_qkv, *part_x;  // k-split partial products of QKV, and of the O / MLP projections
+  int ks_qkv, ks_o, ks_p;
   // prefill (B T tokens)
   float *x, *rstd, *rstd_q, *rstd_k, *lse, *table, *xl;
   void *a, *qkv, *o, *a2, *hl;
   void* gemm_ws;
   size_t gemm_ws_bytes;
 };
+
+// K-split of a decode projection (N outputs, K inputs) over blocks: about
+// 320 blocks of 16 columns, at least 8 k-chunks of 64 per block.
+int decode_split(int64_t N, int64_t K) {
+  const int64_t slabs = N / 16, nch = K / 64;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({cdiv(320, slabs), nch / 8, (int64_t)kMaxParts}));
+}
 
 size_t decode_part_floats(int B, int H, int max_len) { return (size_t)B * cdiv(max_len, kChunk) * H; }
 
@@ -369,9 +435,11 @@ size_t carve_infer(const nc_config* c, int max_len, InferWs* w, void* base) {
   char* p = static_cast<char*>(base);
   auto at = [&](size_t o) -> void* { return p ? p + o : nullptr; };
   const size_t o_flag = take(4);
-  const size_t o_dx = take(B * d * 4), o_dr = take(B * 4), o_da = take(B * d * 2), o_dqkv = take(B * Q * 2),
+  const int ks_qkv = decode_split(Q, d), ks_o = decode_split(d, HD), ks_p = decode_split(d, F);
+  const size_t o_dx = take(B * d * 4), o_dr = take(B * 4), o_da = take(B * d * 2),
                o_dq = take(B * HD * 2), o_do = take(B * HD * 2), o_dm = take(B * d * 2), o_da2 = take(B * F * 2),
-               o_dh = take(B * d * 2);
+               o_dh = take(B * d * 2), o_pq = take((size_t)ks_qkv * B * Q * 4),
+               o_px = take((size_t)std::max(ks_o, ks_p) * B * d * 4);
   const size_t parts = decode_part_floats((int)B, (int)H, max_len);
   const size_t o_po = take(parts * kHd * 4), o_pml = take(parts * 2 * 4);
   const size_t o_x = take(M * d * 4), o_r = take(M * 4), o_rq = take(M * H * 4), o_rk = take(M * 4),
@@ -385,7 +453,11 @@ size_t carve_infer(const nc_config* c, int max_len, InferWs* w, void* base) {
     w->dx = static_cast<float*>(at(o_dx));
     w->drstd = static_cast<float*>(at(o_dr));
     w->da = at(o_da);
-    w->dqkv = at(o_dqkv);
+    w->part_qkv = static_cast<float*>(at(o_pq));
+    w->part_x = static_cast<float*>(at(o_px));
+    w->ks_qkv = ks_qkv;
+    w->ks_o = ks_o;
+    w->ks_p = ks_p;
     w->dq = at(o_dq);
     w->dout = at(o_do);
     w->dm = at(o_dm);
@@ -550,26 +622,36 @@ int decode_step(const nc_config* c, const nc_params* p, const int32_t* ids, cons
 
   NC_TRY(fill_zero(w.flag, 4, s));
   NC_TRY(embed_fwd(ids, B, p->embed, NC_BF16, V, (int)d, nullptr, w.dx, w.drstd, c->eps, w.flag, s));
+  // Residual norm: x += the partial products of the projection that feeds it,
+  // then the norm (the first layer's input is the embedding output itself).
+  auto residual_norm = [&](int parts, void* out) -> int {
+    residual_rmsnorm_kernel<<<B, (unsigned)align_up((size_t)d / 4, 64), 0, s>>>(w.dx, w.part_x, parts, B, (int)d,
+                                                                               c->eps, static_cast<bf16*>(out));
+    return check_launch("residual_rmsnorm_kernel");
+  };
   for (int l = 0; l < L; ++l) {
-    NC_TRY(rmsnorm_fwd(w.dx, NC_F32, B, (int)d, c->eps, w.da, NC_BF16, w.drstd, s));
-    NC_TRY(gemm(nt(B, Q, d, w.da, W(p->w_qkv, l, Q * d), w.dqkv, NC_BF16), s));
-    decode_rope_append_kernel<<<B, 256, 0, s>>>(static_cast<const bf16*>(w.dqkv), pos, H, (double)c->rope_base,
-                                                c->eps, max_len, static_cast<bf16*>(w.dq), cv.k(l), cv.v(l), w.flag);
+    if (l == 0) NC_TRY(rmsnorm_fwd(w.dx, NC_F32, B, (int)d, c->eps, w.da, NC_BF16, w.drstd, s));
+    else NC_TRY(residual_norm(w.ks_p, w.da));
+    GemmDesc gq = nt(B, Q, d, w.da, W(p->w_qkv, l, Q * d), w.part_qkv, NC_F32);
+    gq.sk_split = w.ks_qkv;
+    NC_TRY(gemm(gq, s));
+    decode_rope_append_kernel<<<B, 256, 0, s>>>(w.part_qkv, w.ks_qkv, B, pos, H, (double)c->rope_base, c->eps,
+                                                max_len, static_cast<bf16*>(w.dq), cv.k(l), cv.v(l), w.flag);
     NC_TRY(check_launch("decode_rope_append_kernel"));
     NC_TRY(mqa_decode_attn(w.dq, cv.k(l), cv.v(l), pos, 1, B, H, kHd, max_len, scale, w.dout, w.part_o, w.part_ml,
                            s));
-    GemmDesc go = nt(B, d, HD, w.dout, W(p->w_o, l, d * HD), w.dx, NC_F32);
-    go.beta = 1.f;
+    GemmDesc go = nt(B, d, HD, w.dout, W(p->w_o, l, d * HD), w.part_x, NC_F32);
+    go.sk_split = w.ks_o;
     NC_TRY(gemm(go, s));
-    NC_TRY(rmsnorm_fwd(w.dx, NC_F32, B, (int)d, c->eps, w.dm, NC_BF16, w.drstd, s));
+    NC_TRY(residual_norm(w.ks_o, w.dm));
     GemmDesc gf = nt(B, F, d, w.dm, W(p->w_fc, l, F * d), w.da2, NC_BF16);
     gf.epi = NC_EPI_RELU2_SQ;
     NC_TRY(gemm(gf, s));
-    GemmDesc gp = nt(B, d, F, w.da2, W(p->w_proj, l, d * F), w.dx, NC_F32);
-    gp.beta = 1.f;
+    GemmDesc gp = nt(B, d, F, w.da2, W(p->w_proj, l, d * F), w.part_x, NC_F32);
+    gp.sk_split = w.ks_p;
     NC_TRY(gemm(gp, s));
   }
-  NC_TRY(rmsnorm_fwd(w.dx, NC_F32, B, (int)d, c->eps, w.dh, NC_BF16, w.drstd, s));
+  NC_TRY(residual_norm(w.ks_p, w.dh));
   GemmDesc gu = nt(B, V, d, w.dh, p->unembed, logits, NC_F32);
   gu.capc = c->softcap;
   return gemm(gu, s);
