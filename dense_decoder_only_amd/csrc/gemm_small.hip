@@ -39,7 +39,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 //    16 x 16 tile at a time, and 256 threads apply the epilogue.
 // A (at most 128 x K bf16) stays in L2 across the blocks that re-read it.
 // ---------------------------------------------------------------------------
-constexpr int SK_WAVES = 16, SK_MMAX = 128, SK_CPW = 4;
+#ifndef NC_SK_CPW
+#define NC_SK_CPW 4
+#endif
+#ifndef NC_SK_WIDE
+#define NC_SK_WIDE 256
+#endif
+constexpr int SK_WAVES = 16, SK_MMAX = 128, SK_CPW = NC_SK_CPW;
 enum { E_SOFTCAP_F32 = 10 };  // small-M only: C (fp32) = c tanh(acc / c)
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -165,7 +171,7 @@ void launch_skinny_w(const SkinnyParams& p, int nmt, hipStream_t s) {
 template <int EPI>
 void launch_skinny(const SkinnyParams& p, int nmt, hipStream_t s) {
   // products with blocks to spare (>= 256 slabs x splits): 8-wave blocks, two per CU
-  if ((p.N / 16) * p.ksplit >= 256) launch_skinny_w<EPI, 8>(p, nmt, s);
+  if ((p.N / 16) * p.ksplit >= NC_SK_WIDE) launch_skinny_w<EPI, 8>(p, nmt, s);
   else launch_skinny_w<EPI, 16>(p, nmt, s);
 }
 

@@ -48,9 +48,9 @@ __device__ __forceinline__ void unpack4(uint2 u, float (&f)[4]) {
 // RoPE + per-head RMS norm of one new token per sequence, at its own
 // position pos[b]; the key and the value (rounded to bf16) are appended to
 // the cache at that position, the query heads go to qhat [B, H, 128].  A 16-lane group per head
-// (lane j owns the pairs (i, i + 64), i = 4 j .. 4 j + 3); the angles are
-// computed in fp64 and rounded to fp32 as for the training table, so a
-// position gets the same rotation in both paths.  A position outside
+// (lane j owns the pairs (i, i + 64), i = 4 j .. 4 j + 3); the 64 angles are
+// computed once per token in fp64 and rounded to fp32 as for the training
+// table, so a position gets the same rotation in both paths.  A position outside
 // [0, max_len) raises the flag and leaves that sequence's outputs unwritten.
 // The projection arrives as `parts` fp32 partial sums [parts][B][(H+2) 128]
 // (k-split small-M GEMM); they are added in order here.
@@ -77,6 +77,13 @@ __global__ __launch_bounds__(256) void decode_rope_append_kernel(const float* __
     if (threadIdx.x == 0 && flag) *flag = 1;
     return;
   }
+  // the 64 rotation angles of this position, once per block (fp64, rounded to fp32)
+  __shared__ float2 cs_sn[kHd / 2];
+  if (threadIdx.x < kHd / 2) {
+    const double th = (double)p * pow(base, -2.0 * (double)threadIdx.x / (double)kHd);
+    cs_sn[threadIdx.x] = make_float2((float)cos(th), (float)sin(th));
+  }
+  __syncthreads();
   const int j = threadIdx.x & 15;
   const int64_t stride = (int64_t)B * (H + 2) * kHd;
   const float* row = qkv + (int64_t)b * (H + 2) * kHd;
@@ -94,8 +101,7 @@ __global__ __launch_bounds__(256) void decode_rope_append_kernel(const float* __
     float ya[4], yb[4], ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const double th = (double)p * pow(base, -2.0 * (double)(4 * j + e) / (double)kHd);
-      const float cs = (float)cos(th), sn = (float)sin(th);
+      const float cs = cs_sn[4 * j + e].x, sn = cs_sn[4 * j + e].y;
       ya[e] = a[e] * cs - c[e] * sn;
       yb[e] = a[e] * sn + c[e] * cs;
       ss += ya[e] * ya[e] + yb[e] * yb[e];
