@@ -87,3 +87,33 @@ def test_adamw_host_validation():
     lib = nc.load()
     rc = lib.nc_adamw_step(None, None, None, None, None, 16, 1, 1e-3, 0.9, 0.95, 1e-8, 0.0, 1.0, None)
     assert rc == nc.NC_ERR_INVALID_ARG and "null" in nc.nc_last_error()
+
+
+def test_inference_size_queries_and_validation():
+    import dataclasses
+    from dense_decoder_only_amd import nc
+    from synthetic import CONFIGS
+    lib = nc.load()
+    small = nc.make_config(dataclasses.replace(CONFIGS["small"], seq_len=16, batch=2))
+    assert nc.nc_kv_cache_bytes(small, 32) == 4 * 2 * 2 * 32 * 128 * 2  # L x (K, V) x B x max_len x 128 x bf16
+    assert nc.nc_infer_workspace_bytes(small, 32) > 0
+    # unsupported or inconsistent configurations report 0 bytes
+    assert nc.nc_kv_cache_bytes(nc.make_config(CONFIGS["tiny"]), 128) == 0      # fp32, head_dim 64
+    assert nc.nc_kv_cache_bytes(small, 8) == 0                                   # max_len < prompt length
+    big_b = nc.make_config(dataclasses.replace(CONFIGS["small"], batch=129))
+    assert nc.nc_infer_workspace_bytes(big_b, 1024) == 0                         # more than 128 sequences
+    # errors are returned on the host, before anything is enqueued
+    p = nc.nc_params(*[None] * 6)
+    rc = lib.nc_prefill(ctypes.byref(small), ctypes.byref(p), None, None, 32, None, None, 0, None)
+    assert rc == nc.NC_ERR_INVALID_ARG and "null parameter" in nc.nc_last_error()
+    tiny = nc.make_config(CONFIGS["tiny"])
+    rc = lib.nc_decode_step(ctypes.byref(tiny), ctypes.byref(p), None, None, None, 128, None, None, 0, None)
+    assert rc == nc.NC_ERR_UNSUPPORTED
+    assert nc.nc_mqa_decode_workspace_bytes(0, 10, 64) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    rc = lib.nc_mqa_decode_attn(fake, fake, fake, fake, 2, 10, 64, 64, 0.1, fake, fake, 1 << 20, None)
+    assert rc == nc.NC_ERR_UNSUPPORTED and "head_dim" in nc.nc_last_error()
+    rc = lib.nc_mqa_decode_attn(fake, fake, fake, fake, 2, 40, 128, 64, 0.1, fake, fake, 1 << 20, None)
+    assert rc == nc.NC_ERR_UNSUPPORTED
+    rc = lib.nc_mqa_decode_attn(fake, fake, fake, fake, 2, 10, 128, 64, 0.1, fake, fake, 16, None)
+    assert rc == nc.NC_ERR_WORKSPACE
