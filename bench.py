@@ -96,7 +96,7 @@ def stored_traffic(summary):
     return float(fields["traffic_bytes_per_launch"])
 
 
-def roofline(name, ms, launches, flops):
+def roofline(name, ms, launches, flops, workload):
     fam = FAMILIES[name]
     achieved = flops / (ms / 1e3) / 1e12
     return {
@@ -109,7 +109,8 @@ def roofline(name, ms, launches, flops):
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": stored_traffic(fam[3]),
+        # the stored counter figures are per launch of the d20 step
+        "traffic": stored_traffic(fam[3]) if workload == "d20" else None,
     }
 
 
@@ -252,7 +253,7 @@ def decode_leg(cfg, torch, nc, params, s, steps=64, max_len=2048):
     att_gbs = kv_bytes_launch / (att_us * 1e-6) / 1e9
     gem_gbs = gem_bytes / (gem_ms * 1e-3) / 1e9
     step_gbs = step_bytes / (ms * 1e-3) / 1e9
-    log(f"[bench] decode d20: {ms:.3f} ms/step ({B / (ms * 1e-3):.0f} tok/s), {step_gbs:.0f} GB/s over "
+    log(f"[bench] decode {cfg.name}: {ms:.3f} ms/step ({B / (ms * 1e-3):.0f} tok/s), {step_gbs:.0f} GB/s over "
         f"{step_bytes / 1e9:.3f} GB; attention {att_us:.1f} us/launch {att_gbs:.0f} GB/s; small-M GEMMs "
         f"{gem_gbs:.0f} GB/s; prefill {prefill_ms:.1f} ms")
     return {
@@ -324,7 +325,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_s = e0.elapsed_time(e1) / 1e3
-    roof = roofline(a.roofline_kernel, *nc.nc_probe_stop())
+    roof = roofline(a.roofline_kernel, *nc.nc_probe_stop(), cfg.name)
     elapsed = max(wall, gpu_s)
     tokens = cfg.tokens * a.steps
     value = tokens / elapsed
