@@ -45,76 +45,6 @@ __device__ __forceinline__ void unpack4(uint2 u, float (&f)[4]) {
   f[3] = __uint_as_float(u.y & 0xffff0000u);
 }
 
-// RoPE + per-head RMS norm of one new token per sequence, at its own
-// position pos[b]; the key and the value (rounded to bf16) are appended to
-// the cache at that position, the query heads go to qhat [B, H, 128].  A 16-lane group per head
-// (lane j owns the pairs (i, i + 64), i = 4 j .. 4 j + 3); the 64 angles are
-// computed once per token in fp64 and rounded to fp32 as for the training
-// table, so a position gets the same rotation in both paths.  A position outside
-// [0, max_len) raises the flag and leaves that sequence's outputs unwritten.
-// The projection arrives as `parts` fp32 partial sums [parts][B][(H+2) 128]
-// (k-split small-M GEMM); they are added in order here.
-__device__ __forceinline__ float4 sum_parts4(const float* x, int parts, int64_t stride) {
-  float4 a = *reinterpret_cast<const float4*>(x);
-  for (int k = 1; k < parts; ++k) {
-    const float4 b = *reinterpret_cast<const float4*>(x + k * stride);
-    a.x += b.x;
-    a.y += b.y;
-    a.z += b.z;
-    a.w += b.w;
-  }
-  return a;
-}
-
-__global__ __launch_bounds__(256) void decode_rope_append_kernel(const float* __restrict__ qkv, int parts, int B,
-                                                                 const int32_t* __restrict__ pos, int H, double base,
-                                                                 float eps, int max_len, bf16* __restrict__ qhat,
-                                                                 bf16* __restrict__ kc, bf16* __restrict__ vc,
-                                                                 int32_t* __restrict__ flag) {
-  const int b = blockIdx.x;
-  const int p = pos[b];
-  if (p < 0 || p >= max_len) {
-    if (threadIdx.x == 0 && flag) *flag = 1;
-    return;
-  }
-  // the 64 rotation angles of this position, once per block (fp64, rounded to fp32)
-  __shared__ float2 cs_sn[kHd / 2];
-  if (threadIdx.x < kHd / 2) {
-    const double th = (double)p * pow(base, -2.0 * (double)threadIdx.x / (double)kHd);
-    cs_sn[threadIdx.x] = make_float2((float)cos(th), (float)sin(th));
-  }
-  __syncthreads();
-  const int j = threadIdx.x & 15;
-  const int64_t stride = (int64_t)B * (H + 2) * kHd;
-  const float* row = qkv + (int64_t)b * (H + 2) * kHd;
-  const int64_t cache_row = ((int64_t)b * max_len + p) * kHd;
-  for (int head = threadIdx.x >> 4; head < H + 2; head += 16) {
-    const float* x = row + head * kHd;
-    if (head == H + 1) {  // value: rounded to bf16 as is
-      const float4 v0 = sum_parts4(x + 8 * j, parts, stride), v1 = sum_parts4(x + 8 * j + 4, parts, stride);
-      *reinterpret_cast<uint4*>(vc + cache_row + 8 * j) = make_uint4(
-          pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y), pack_bf16x2(v1.z, v1.w));
-      continue;
-    }
-    const float4 a4 = sum_parts4(x + 4 * j, parts, stride), c4 = sum_parts4(x + 64 + 4 * j, parts, stride);
-    const float a[4] = {a4.x, a4.y, a4.z, a4.w}, c[4] = {c4.x, c4.y, c4.z, c4.w};
-    float ya[4], yb[4], ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float cs = cs_sn[4 * j + e].x, sn = cs_sn[4 * j + e].y;
-      ya[e] = a[e] * cs - c[e] * sn;
-      yb[e] = a[e] * sn + c[e] * cs;
-      ss += ya[e] * ya[e] + yb[e] * yb[e];
-    }
-    const float r = 1.f / sqrtf(sum16(ss) / (float)kHd + eps);
-    bf16* dst = head < H ? qhat + ((int64_t)b * H + head) * kHd : kc + cache_row;
-    *reinterpret_cast<uint2*>(dst + 4 * j) =
-        make_uint2(pack_bf16x2(ya[0] * r, ya[1] * r), pack_bf16x2(ya[2] * r, ya[3] * r));
-    *reinterpret_cast<uint2*>(dst + 64 + 4 * j) =
-        make_uint2(pack_bf16x2(yb[0] * r, yb[1] * r), pack_bf16x2(yb[2] * r, yb[3] * r));
-  }
-}
-
 __device__ __forceinline__ int seq_len_of(const int32_t* lens, int b, int len_add, int max_len) {
   const int n = lens[b] + len_add;
   return n < 0 ? 0 : (n > max_len ? max_len : n);
@@ -165,17 +95,41 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8_t a, bf16x8_t b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(64) void decode_attn_split_kernel(const bf16* __restrict__ q,
-                                                               const bf16* __restrict__ kc,
-                                                               const bf16* __restrict__ vc,
+// With ROPE the kernel also does the new token's RoPE + QK norm and cache
+// append (one launch less per layer): `lens` are then the positions (len_add
+// = 1), the projection arrives as fp32 partial sums [parts][B][(H+2) 128],
+// every block rotates and normalises the query heads itself (each lane holds
+// both members of its RoPE pairs: dims 16 ks + 8 h + e and that + 64), and the
+// block whose chunk holds the position computes the key and value, writes them
+// to the cache and into its LDS tiles.
+struct RopeIn {
+  const float* qkv;
+  int parts, B;
+  double base;
+  float eps;
+  int32_t* flag;
+};
+
+template <bool ROPE>
+__global__ __launch_bounds__(64) void decode_attn_split_kernel(const bf16* __restrict__ q, bf16* __restrict__ kc,
+                                                               bf16* __restrict__ vc,
                                                                const int32_t* __restrict__ lens, int len_add, int H,
                                                                int max_len, float scale_log2,
                                                                float* __restrict__ part_o,
-                                                               float* __restrict__ part_ml) {
+                                                               float* __restrict__ part_ml, RopeIn ri) {
   __shared__ __attribute__((aligned(16))) bf16 Ks[kChunk * kHd];
   __shared__ __attribute__((aligned(16))) bf16 Vs[kChunk * kHd];
+  __shared__ float2 cs_sn[kHd / 2];
   const int chunk = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int nch = gridDim.x;
+  int pnew = 0;
+  if constexpr (ROPE) {
+    pnew = lens[b];
+    if (pnew < 0 || pnew >= max_len) {  // outputs of this sequence stay undefined
+      if (chunk == 0 && lane == 0 && ri.flag) *ri.flag = 1;
+      return;
+    }
+  }
   const int len = seq_len_of(lens, b, len_add, max_len);
   const int t0 = chunk * kChunk;
   if (t0 >= len) return;
@@ -195,15 +149,95 @@ __global__ __launch_bounds__(64) void decode_attn_split_kernel(const bf16* __res
   // the query of head lane mod 32, dims 16 ks + 8 h .. + 7 (zero past H)
   const int hcol = lane & 31, h = lane >> 5;
   bf16x8_t qreg[kHd / 16];
+  if constexpr (!ROPE) {
 #pragma unroll
-  for (int ks = 0; ks < kHd / 16; ++ks)
-    qreg[ks] = hcol < H ? *reinterpret_cast<const bf16x8_t*>(q + ((int64_t)b * H + hcol) * kHd + 16 * ks + 8 * h)
-                        : bf16x8_t{};
+    for (int ks = 0; ks < kHd / 16; ++ks)
+      qreg[ks] = hcol < H ? *reinterpret_cast<const bf16x8_t*>(q + ((int64_t)b * H + hcol) * kHd + 16 * ks + 8 * h)
+                          : bf16x8_t{};
+  }
+  float cs = 0.f, sn = 0.f;
+  if constexpr (ROPE) {  // angle of pair `lane` at this position (fp64, rounded to fp32)
+    const double th = (double)pnew * pow(ri.base, -2.0 * (double)lane / (double)kHd);
+    cs = (float)cos(th);
+    sn = (float)sin(th);
+    cs_sn[lane] = make_float2(cs, sn);
+  }
 #pragma unroll
   for (int g = 0; g < kChunk / 4; ++g) {
     const int row = 4 * g + rsub;
     *reinterpret_cast<uint4*>(Ks + toff(row, cp)) = kl[g];
     *reinterpret_cast<uint4*>(Vs + toff(row, cp)) = vl[g];
+  }
+  if constexpr (ROPE) {
+    const int64_t stride = (int64_t)ri.B * (H + 2) * kHd;
+    const float* qkvrow = ri.qkv + (int64_t)b * (H + 2) * kHd;
+    if (pnew >= t0 && pnew < t0 + kChunk) {
+      // the new position's key (rotated, normalised) and value: lane owns dims lane, lane + 64
+      const float* kr = qkvrow + H * kHd;
+      float ka = 0.f, kb = 0.f, va = 0.f, vb = 0.f;
+      for (int k = 0; k < ri.parts; ++k) {
+        ka += kr[k * stride + lane];
+        kb += kr[k * stride + lane + 64];
+        va += kr[k * stride + kHd + lane];
+        vb += kr[k * stride + kHd + lane + 64];
+      }
+      const float ya = ka * cs - kb * sn, yb = ka * sn + kb * cs;
+      const float r = 1.f / sqrtf(wave_sum(ya * ya + yb * yb) / (float)kHd + ri.eps);
+      const bf16 k0 = f2bf(ya * r), k1 = f2bf(yb * r), v0 = f2bf(va), v1 = f2bf(vb);
+      const int row = pnew - t0;
+      Ks[toff(row, lane >> 3) + (lane & 7)] = k0;
+      Ks[toff(row, (lane + 64) >> 3) + (lane & 7)] = k1;
+      Vs[toff(row, lane >> 3) + (lane & 7)] = v0;
+      Vs[toff(row, (lane + 64) >> 3) + (lane & 7)] = v1;
+      const int64_t crow = seq + (int64_t)pnew * kHd;
+      kc[crow + lane] = k0;
+      kc[crow + lane + 64] = k1;
+      vc[crow + lane] = v0;
+      vc[crow + lane + 64] = v1;
+    }
+    __syncthreads();  // the angle table
+    if (hcol < H) {
+      const float* qr = qkvrow + hcol * kHd + 8 * h;
+      float qv[kHd / 16][8];
+#pragma unroll
+      for (int ks = 0; ks < kHd / 16; ++ks) {
+        const float4 a0 = *reinterpret_cast<const float4*>(qr + 16 * ks);
+        const float4 a1 = *reinterpret_cast<const float4*>(qr + 16 * ks + 4);
+        qv[ks][0] = a0.x; qv[ks][1] = a0.y; qv[ks][2] = a0.z; qv[ks][3] = a0.w;
+        qv[ks][4] = a1.x; qv[ks][5] = a1.y; qv[ks][6] = a1.z; qv[ks][7] = a1.w;
+      }
+      for (int k = 1; k < ri.parts; ++k) {
+#pragma unroll
+        for (int ks = 0; ks < kHd / 16; ++ks) {
+          const float4 a0 = *reinterpret_cast<const float4*>(qr + k * stride + 16 * ks);
+          const float4 a1 = *reinterpret_cast<const float4*>(qr + k * stride + 16 * ks + 4);
+          qv[ks][0] += a0.x; qv[ks][1] += a0.y; qv[ks][2] += a0.z; qv[ks][3] += a0.w;
+          qv[ks][4] += a1.x; qv[ks][5] += a1.y; qv[ks][6] += a1.z; qv[ks][7] += a1.w;
+        }
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kHd / 32; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 t = cs_sn[16 * ks + 8 * h + e];
+          const float a = qv[ks][e], c = qv[ks + 4][e];
+          const float ya = a * t.x - c * t.y, yb = a * t.y + c * t.x;
+          qv[ks][e] = ya;
+          qv[ks + 4][e] = yb;
+          ss += ya * ya + yb * yb;
+        }
+      ss += __shfl_xor(ss, 32, 64);  // the other half of the head's dims
+      const float r = 1.f / sqrtf(ss / (float)kHd + ri.eps);
+#pragma unroll
+      for (int ks = 0; ks < kHd / 16; ++ks)
+        qreg[ks] = __builtin_bit_cast(
+            bf16x8_t, make_uint4(pack_bf16x2(qv[ks][0] * r, qv[ks][1] * r), pack_bf16x2(qv[ks][2] * r, qv[ks][3] * r),
+                                 pack_bf16x2(qv[ks][4] * r, qv[ks][5] * r), pack_bf16x2(qv[ks][6] * r, qv[ks][7] * r)));
+    } else {  // lanes l and l ^ 32 share a head, so the shuffle above stays within active lanes
+#pragma unroll
+      for (int ks = 0; ks < kHd / 16; ++ks) qreg[ks] = bf16x8_t{};
+    }
   }
   __syncthreads();
   f32x16 s[2];
@@ -409,7 +443,7 @@ struct InferWs {
   int32_t* flag;
   // decode (one token per sequence)
   float *dx, *drstd;
-  void *da, *dq, *dout, *dm, *da2, *dh;
+  void *da, *dout, *dm, *da2, *dh;
   float *part_o, *part_ml;
   float *part_qkv, *part_x;  // k-split partial products of QKV, and of the O / MLP projections
   int ks_qkv, ks_o, ks_p;
@@ -443,7 +477,7 @@ size_t carve_infer(const nc_config* c, int max_len, InferWs* w, void* base) {
   const size_t o_flag = take(4);
   const int ks_qkv = decode_split(Q, d), ks_o = decode_split(d, HD), ks_p = decode_split(d, F);
   const size_t o_dx = take(B * d * 4), o_dr = take(B * 4), o_da = take(B * d * 2),
-               o_dq = take(B * HD * 2), o_do = take(B * HD * 2), o_dm = take(B * d * 2), o_da2 = take(B * F * 2),
+               o_do = take(B * HD * 2), o_dm = take(B * d * 2), o_da2 = take(B * F * 2),
                o_dh = take(B * d * 2), o_pq = take((size_t)ks_qkv * B * Q * 4),
                o_px = take((size_t)std::max(ks_o, ks_p) * B * d * 4);
   const size_t parts = decode_part_floats((int)B, (int)H, max_len);
@@ -464,7 +498,6 @@ size_t carve_infer(const nc_config* c, int max_len, InferWs* w, void* base) {
     w->ks_qkv = ks_qkv;
     w->ks_o = ks_o;
     w->ks_p = ks_p;
-    w->dq = at(o_dq);
     w->dout = at(o_do);
     w->dm = at(o_dm);
     w->da2 = at(o_da2);
@@ -528,9 +561,15 @@ size_t mqa_decode_workspace_bytes(int B, int H, int max_len) {
   return align_up(parts * kHd * 4, 256) + parts * 2 * 4;
 }
 
+// rope == nullptr: q holds the queries, `lens` + len_add the lengths.
+// rope != nullptr: the queries, keys and values come as projection partial
+// sums (RopeIn) and are rotated and normalised here; `lens` are the new
+// positions, each of whose key and value is written to the cache.
 int mqa_decode_attn(const void* q, const void* kc, const void* vc, const int32_t* lens, int len_add, int B, int H,
-                    int hd, int max_len, float scale, void* o, float* part_o, float* part_ml, hipStream_t s) {
-  NC_REQUIRE(q && kc && vc && lens && o && part_o && part_ml, NC_ERR_INVALID_ARG, "decode_attn: null pointer");
+                    int hd, int max_len, float scale, void* o, float* part_o, float* part_ml, hipStream_t s,
+                    const RopeIn* rope = nullptr) {
+  NC_REQUIRE((q || rope) && kc && vc && lens && o && part_o && part_ml, NC_ERR_INVALID_ARG,
+             "decode_attn: null pointer");
   NC_REQUIRE(B > 0 && H > 0 && max_len > 0, NC_ERR_INVALID_ARG, "decode_attn: bad shape");
   NC_REQUIRE(hd == kHd, NC_ERR_UNSUPPORTED, "decode_attn: head_dim must be 128");
   NC_REQUIRE(H <= kMaxHeads, NC_ERR_UNSUPPORTED, "decode_attn: at most %d query heads", kMaxHeads);
@@ -539,10 +578,16 @@ int mqa_decode_attn(const void* q, const void* kc, const void* vc, const int32_t
   NC_REQUIRE(nch < 65536 && B < 65536, NC_ERR_UNSUPPORTED, "decode_attn: grid too large");
   const double bytes = (double)B * max_len * kHd * 2 * 2 + 2.0 * 2 * B * H * kHd;  // cache capacity, q and o
   probe_begin(NC_PROBE_DECODE_ATTN, s);
-  decode_attn_split_kernel<<<dim3(nch, B), 64, 0, s>>>(static_cast<const bf16*>(q), static_cast<const bf16*>(kc),
-                                                       static_cast<const bf16*>(vc), lens, len_add, H, max_len,
-                                                       scale * kLog2e, part_o, part_ml);
-  decode_attn_combine_kernel<<<dim3(H, B), kHd, 0, s>>>(part_o, part_ml, lens, len_add, H, max_len, nch,
+  if (rope)  // lens are the new positions; the cache receives their keys and values
+    decode_attn_split_kernel<true><<<dim3(nch, B), 64, 0, s>>>(
+        nullptr, static_cast<bf16*>(const_cast<void*>(kc)), static_cast<bf16*>(const_cast<void*>(vc)), lens, 1, H,
+        max_len, scale * kLog2e, part_o, part_ml, *rope);
+  else
+    decode_attn_split_kernel<false><<<dim3(nch, B), 64, 0, s>>>(
+        static_cast<const bf16*>(q), static_cast<bf16*>(const_cast<void*>(kc)),
+        static_cast<bf16*>(const_cast<void*>(vc)), lens, len_add, H, max_len, scale * kLog2e, part_o, part_ml,
+        RopeIn{});
+  decode_attn_combine_kernel<<<dim3(H, B), kHd, 0, s>>>(part_o, part_ml, lens, rope ? 1 : len_add, H, max_len, nch,
                                                         static_cast<bf16*>(o));
   probe_end(NC_PROBE_DECODE_ATTN, s, bytes);
   return check_launch("decode_attn kernels");
@@ -641,11 +686,9 @@ int decode_step(const nc_config* c, const nc_params* p, const int32_t* ids, cons
     GemmDesc gq = nt(B, Q, d, w.da, W(p->w_qkv, l, Q * d), w.part_qkv, NC_F32);
     gq.sk_split = w.ks_qkv;
     NC_TRY(gemm(gq, s));
-    decode_rope_append_kernel<<<B, 256, 0, s>>>(w.part_qkv, w.ks_qkv, B, pos, H, (double)c->rope_base, c->eps,
-                                                max_len, static_cast<bf16*>(w.dq), cv.k(l), cv.v(l), w.flag);
-    NC_TRY(check_launch("decode_rope_append_kernel"));
-    NC_TRY(mqa_decode_attn(w.dq, cv.k(l), cv.v(l), pos, 1, B, H, kHd, max_len, scale, w.dout, w.part_o, w.part_ml,
-                           s));
+    const RopeIn ri{w.part_qkv, w.ks_qkv, B, (double)c->rope_base, c->eps, w.flag};
+    NC_TRY(mqa_decode_attn(nullptr, cv.k(l), cv.v(l), pos, 1, B, H, kHd, max_len, scale, w.dout, w.part_o,
+                           w.part_ml, s, &ri));
     GemmDesc go = nt(B, d, HD, w.dout, W(p->w_o, l, d * HD), w.part_x, NC_F32);
     go.sk_split = w.ks_o;
     NC_TRY(gemm(go, s));
