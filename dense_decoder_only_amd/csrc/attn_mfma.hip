@@ -29,6 +29,14 @@
 // chunks are XOR-swizzled by ((r & 3) << 2) | ((r >> 2) & 3) so that both the
 // row reads and the transposed reads spread over the banks.
 //
+// Static stages.  The two stages of each staged operand are separate LDS
+// objects and the tile loops are unrolled by two, so that every DMA and every
+// read names its stage at compile time.  The compiler then knows that the
+// reads of the current stage do not alias the DMA in flight into the other;
+// with one array indexed at run time it must assume they may, and makes the
+// reads wait for that DMA to land, which serialises the prefetch with the
+// products.
+//
 // Kernels: forward (online softmax, writes O and the log-sum-exp), dQ (also
 // writes D = rowsum(dO * O)), dK/dV (key blocks of 128 positions, the query
 // range split into chunks so that early key blocks do not serialize, partials
@@ -46,6 +54,9 @@ constexpr int KT = 64;    // keys per tile
 constexpr int KB = 128;   // keys per dK/dV block (4 waves x 32)
 constexpr int QT = 64;    // query rows per dK/dV tile
 constexpr int QCH = 5120; // query rows per dK/dV split
+#ifndef NC_DKV_PF
+#define NC_DKV_PF 4       // dK/dV: fragment pairs in the S / dP read ring
+#endif
 constexpr int TILE = 64 * HD;  // elements of one [64][128] tile
 constexpr int QTILE = QT * HD; // elements of one dK/dV query tile
 constexpr float LOG2E = 1.4426950408889634f;
@@ -123,8 +134,11 @@ __device__ __forceinline__ uint32_t wd(const uint4& q, int w) {
 // ------------------------------------------------------------------ forward --
 // grid (B, ceil(R / QB)); heavy (late) row blocks first.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnMfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2 * TILE];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2 * TILE];
+  // one LDS object per stage; see the note on static stages above
+  __shared__ __attribute__((aligned(16))) bf16 Ks0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Ks1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Vs0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Vs1[TILE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
   const int H = a.H, T = a.T;
   const int R = T * H;
@@ -148,12 +162,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tmin = r0 / H;
   const int tmax = min(T - 1, (min(r0 + QB, R) - 1) / H);
   const int ntiles = tmax / KT + 1;
-  auto stage = [&](int j, int buf) {
+  auto stage = [&](int j, bf16* Kd, bf16* Vd) {
     const int kv0 = j * KT;
-    dma_tile(Ks + buf * TILE, w, lane,
-             [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + H * HD; });
-    dma_tile(Vs + buf * TILE, w, lane,
-             [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + (H + 1) * HD; });
+    dma_tile(Kd, w, lane, [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + H * HD; });
+    dma_tile(Vd, w, lane, [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + (H + 1) * HD; });
   };
 
   f32x16 o[4];
@@ -161,15 +173,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int i = 0; i < 4; ++i) o[i] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
 
-  stage(0, 0);
+  stage(0, Ks0, Vs0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int cur = j & 1;
+  // key tile j in (K, V); tile j + 1 is DMA'd into (Kn, Vn)
+  auto kv_tile = [&](const int j, const bf16* K, const bf16* V, bf16* Kn, bf16* Vn) {
     const int kv0 = j * KT;
-    if (j + 1 < ntiles) stage(j + 1, cur ^ 1);
-    const bf16* K = Ks + cur * TILE;
-    const bf16* V = Vs + cur * TILE;
+    if (j + 1 < ntiles) stage(j + 1, Kn, Vn);
 
     f32x16 s[2];
 #pragma unroll
@@ -236,7 +246,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    kv_tile(j, Ks0, Vs0, Ks1, Vs1);
+    kv_tile(j + 1, Ks1, Vs1, Ks0, Vs0);
   }
+  if (j < ntiles) kv_tile(j, Ks0, Vs0, Ks1, Vs1);
 
   if (valid) {
     const float inv = 1.f / l_run;
@@ -390,8 +406,11 @@ __device__ __forceinline__ int nsplit_of(int kb, int H, int R) { return (R - qbe
 // (64 VGPRs) beside the dK/dV accumulators (128); forcing two waves per SIMD
 // spills them (measured slower).
 __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 Qs[2 * QTILE];
-  __shared__ __attribute__((aligned(16))) bf16 Ds[2 * QTILE];
+  // one LDS object per stage; see the note on static stages above
+  __shared__ __attribute__((aligned(16))) bf16 Qs0[QTILE];
+  __shared__ __attribute__((aligned(16))) bf16 Qs1[QTILE];
+  __shared__ __attribute__((aligned(16))) bf16 Ds0[QTILE];
+  __shared__ __attribute__((aligned(16))) bf16 Ds1[QTILE];
   __shared__ float lse_s[2][QT], D_s[2][QT];
   __shared__ int tpos_s[2][QT];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
@@ -419,14 +438,14 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
   const int qs0 = qbeg_of(kb, H) + sp * QCH;
   const int qs1 = min(R, qs0 + QCH);
   const int nq = (qs1 - qs0 + QT - 1) / QT;
-  auto stage = [&](int i, int buf) {
+  auto stage = [&](int i, bf16* Qd, bf16* Gd) {
     const int q0 = qs0 + i * QT;
-    dma_tile<QT>(Qs + buf * QTILE, w, lane, [&](int row) {
+    dma_tile<QT>(Qd, w, lane, [&](int row) {
       const int r = min(q0 + row, R - 1);
       const int t = div_h(r, a.hmagic);
       return base + (int64_t)t * a.S + (r - t * H) * HD;
     });
-    dma_tile<QT>(Ds + buf * QTILE, w, lane, [&](int row) { return dbase + (int64_t)min(q0 + row, R - 1) * HD; });
+    dma_tile<QT>(Gd, w, lane, [&](int row) { return dbase + (int64_t)min(q0 + row, R - 1) * HD; });
   };
   // per-row statistics of a query tile, loaded by threads 0..63 into registers
   float n_lse = 0.f, n_D = 0.f;
@@ -435,7 +454,7 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
     const int r = qs0 + i * QT + tid;
     if (tid < QT) {
       if (r < R) {
-        n_lse = a.lse[(int64_t)b * R + r] * LOG2E;
+        n_lse = a.lse[(int64_t)b * R + r];  // scaled by log2(e) in put_stats
         n_D = a.Dbuf[(int64_t)b * R + r];
         n_t = div_h(r, a.hmagic);
       } else {
@@ -447,7 +466,9 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
   };
   auto put_stats = [&](int buf) {
     if (tid < QT) {
-      lse_s[buf][tid] = n_lse;
+      // scaled here, at the end of the tile's work, so that the wait for the
+      // load is not placed ahead of the tile's products
+      lse_s[buf][tid] = n_lse * LOG2E;
       D_s[buf][tid] = n_D;
       tpos_s[buf][tid] = n_t;
     }
@@ -459,19 +480,18 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
     dv[i] = zero16();
   }
 
-  stage(0, 0);
+  stage(0, Qs0, Ds0);
   fetch_stats(0);
   put_stats(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int i = 0; i < nq; ++i) {
-    const int cur = i & 1;
+  // query tile i in (Q, G) with statistics in slot cur; tile i + 1 is DMA'd
+  // into (Qn, Gn)
+  auto q_tile = [&](const int i, const int cur, const bf16* Q, const bf16* G, bf16* Qn, bf16* Gn) {
     if (i + 1 < nq) {
-      stage(i + 1, cur ^ 1);
+      stage(i + 1, Qn, Gn);
       fetch_stats(i + 1);
     }
-    const bf16* Q = Qs + cur * QTILE;
-    const bf16* G = Ds + cur * QTILE;
 
     // S = Q K^T and dP = dO V^T: rows q (one 32-row tile), column = key.
     constexpr int NQT = QT / 32;
@@ -480,10 +500,31 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
     for (int qt = 0; qt < NQT; ++qt) {
       s[qt] = zero16();
       dp[qt] = zero16();
+    }
+    {
+      // The Q and dO fragments of step j = 8 qt + ks are read PF - 1 steps
+      // ahead of their MFMAs (a ring of PF fragment pairs): with one wave per
+      // SIMD nothing else would cover the LDS latency.
+      constexpr int NSTEP = NQT * 8, PF = NC_DKV_PF;
+      bf16x8_t fq[PF], fd[PF];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s[qt] = mfma(frag_row(Q, qt * 32 + lc, 2 * ks + h), kreg[ks], s[qt]);
-        dp[qt] = mfma(frag_row(G, qt * 32 + lc, 2 * ks + h), vreg[ks], dp[qt]);
+      for (int j = 0; j < PF - 1; ++j) {
+        fq[j] = frag_row(Q, (j >> 3) * 32 + lc, 2 * (j & 7) + h);
+        fd[j] = frag_row(G, (j >> 3) * 32 + lc, 2 * (j & 7) + h);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 0);
+#pragma unroll
+      for (int j = 0; j < NSTEP; ++j) {
+        if (j + PF - 1 < NSTEP) {
+          const int jn = j + PF - 1;
+          fq[jn % PF] = frag_row(Q, (jn >> 3) * 32 + lc, 2 * (jn & 7) + h);
+          fd[jn % PF] = frag_row(G, (jn >> 3) * 32 + lc, 2 * (jn & 7) + h);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        const int qt = j >> 3, ks = j & 7;
+        s[qt] = mfma(fq[j % PF], kreg[ks], s[qt]);
+        dp[qt] = mfma(fd[j % PF], vreg[ks], dp[qt]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
     }
     // Keys of this block after the earliest query position of the tile need
@@ -525,7 +566,13 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
     if (i + 1 < nq) put_stats(cur ^ 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  int i = 0;
+  for (; i + 1 < nq; i += 2) {
+    q_tile(i, 0, Qs0, Ds0, Qs1, Ds1);
+    q_tile(i + 1, 1, Qs1, Ds1, Qs0, Ds0);
   }
+  if (i < nq) q_tile(i, 0, Qs0, Ds0, Qs1, Ds1);
 
   // partial [slot][2][KB keys][HD]: lane holds hd = ht*32 + 8 q4 + 4 h + e for key (w*32 + lc)
   float* pk = a.part + ((((int64_t)b * a.nkb + kb) * smax + sp) * 2) * (KB * HD) + (w * 32 + lc) * HD;

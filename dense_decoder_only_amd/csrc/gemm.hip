@@ -871,9 +871,16 @@ constexpr int pipe_nreads() { return TN ? 12 : 6; }
 
 template <int EPI, bool TN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pipe_kernel(MfmaParams p) {
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * BM * BK];
-  bf16* const As = lds;
-  bf16* const Bs = lds + 2 * BM * BK;
+  // The two stages of each operand are separate LDS objects and the k loop
+  // below is unrolled by two, so every DMA and fragment read names its stage
+  // at compile time.  The compiler then knows that the reads of one stage do
+  // not alias the DMA in flight into the other; with a single array indexed
+  // at run time it has to assume they may, and makes the transposed reads
+  // (ds_read_b64_tr_b16) wait for that DMA to land.
+  __shared__ __attribute__((aligned(16))) bf16 sA0[BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16 sA1[BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16 sB0[BN * BK];
+  __shared__ __attribute__((aligned(16))) bf16 sB1[BN * BK];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -924,19 +931,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #else
 #define PIPE_STAGE(k0, abuf, bbuf) pipe_stage<TN>(p, m0, n0, k0, abuf, bbuf, wave, lane)
 #endif
-  PIPE_STAGE(kbeg, As, Bs);
-  PIPE_STAGE(nk > 1 ? kbeg + BK : kbeg, As + BM * BK, Bs + BN * BK);
+  PIPE_STAGE(kbeg, sA0, sB0);
+  PIPE_STAGE(nk > 1 ? kbeg + BK : kbeg, sA1, sB1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   constexpr int NR = pipe_nreads<TN>();
   bf16x8_t fa[2][4], fb[2][2];
-  pipe_frags<TN>(As, Bs, 0, wm, wn, lane, fa[0], fb[0]);
+  pipe_frags<TN>(sA0, sB0, 0, wm, wn, lane, fa[0], fb[0]);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bf16* a_c = As + cur * (BM * BK);
-    const bf16* b_c = Bs + cur * (BN * BK);
+  // k-tile kt: its operands are in stage (a_c, b_c); tile kt + 1 is in the
+  // other stage (a_o, b_o), and tile kt + 2 is DMA'd into (a_c, b_c) once
+  // the block is past its last reads.
+  auto k_tile = [&](const int kt, bf16* a_c, bf16* b_c, const bf16* a_o, const bf16* b_o) {
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
       const int c = ks & 1;
@@ -967,8 +974,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     const int k2 = kt + 2 < nk ? kbeg + (kt + 2) * BK : klast;
-    PIPE_STAGE(k2, As + cur * (BM * BK), Bs + cur * (BN * BK));
-    pipe_frags<TN>(As + (cur ^ 1) * (BM * BK), Bs + (cur ^ 1) * (BN * BK), 0, wm, wn, lane, fa[0], fb[0]);
+    PIPE_STAGE(k2, a_c, b_c);
+    pipe_frags<TN>(a_o, b_o, 0, wm, wn, lane, fa[0], fb[0]);
 #pragma unroll
     for (int q = NC_GEMM_PIPE_PRE; q < 8; ++q)
       acc[q >> 1][q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][q & 1], fa[1][q >> 1], acc[q >> 1][q & 1], 0, 0, 0);
@@ -978,12 +985,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x010, 4, 0);
     sched_mfma_ds<0, POST - 2, NR>();
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    k_tile(kt, sA0, sB0, sA1, sB1);
+    k_tile(kt + 1, sA1, sB1, sA0, sB0);
   }
+  if (kt < nk) k_tile(kt, sA0, sB0, sA1, sB1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  // epilogue staging: 32 x SROW floats per wave, three waves per 32 KB stage
   constexpr int SROW = 68;
-  float* stage = reinterpret_cast<float*>(lds) + wave * (32 * SROW);
+  static_assert(3 * 32 * SROW * 4 <= BM * BK * 2, "epilogue staging does not fit a stage");
+  float* stage = reinterpret_cast<float*>(wave < 3 ? sA0 : (wave < 6 ? sA1 : sB0)) + (wave % 3) * (32 * SROW);
   // Epilogue inputs read from memory are loaded ahead of their use so that
   // their latency overlaps the LDS staging: the relu^2 backward's stored
   // activation for the whole sub-tile up front, the accumulated fp32 C one
