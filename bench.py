@@ -60,16 +60,18 @@ def build_device_inputs(cfg, torch, nc):
 FAMILIES = {
     # name: (probe family, kernel symbol in the profiles, what it computes,
     #        committed counter summary giving its HBM bytes per launch)
+    "gemm": ("NC_PROBE_GEMM", "gemm_pipe_kernel<E, TN>",
+             "every GEMM of the step: projections, relu^2 MLP, logits, activation and weight gradients",
+             "gemm_pipe_kernel_d20_traffic.md"),
     "wgrad": ("NC_PROBE_GEMM_WGRAD", "gemm_pipe_kernel<E, true>",
-              "weight-gradient GEMMs dW = dY^T X (K = tokens, split-K partial products)",
-              "gemm_pipe_kernel_tn_d20_traffic.md"),
+              "weight-gradient GEMMs dW = dY^T X (K = tokens, split-K partial products)", None),
     "nt": ("NC_PROBE_GEMM_NT", "gemm_pipe_kernel<E, false>",
            "K-contiguous GEMMs (forward projections and activation gradients)", None),
     "attn_fwd": ("NC_PROBE_ATTN_FWD", "attn_fwd_kernel", "causal MQA attention forward", None),
     "attn_dq": ("NC_PROBE_ATTN_DQ", "attn_dq_kernel", "attention backward, dQ", None),
     "attn_dkv": ("NC_PROBE_ATTN_DKV", "attn_dkv_kernel", "attention backward, dK and dV", None),
 }
-DOMINANT = "wgrad"   # largest share of kernel time in the committed kernel-trace summary
+DOMINANT = "gemm"    # largest share of kernel time in the committed kernel-trace summary
 
 
 def stored_traffic(summary):

@@ -48,10 +48,17 @@ void probe_release() {
 }
 }  // namespace
 
+// Whether launches of `family` are timed while the timer is armed for `armed`.
+bool probe_match(int armed, int family) {
+  if (family == NC_PROBE_OFF) return false;
+  if (armed == family) return true;
+  return armed == NC_PROBE_GEMM && (family == NC_PROBE_GEMM_WGRAD || family == NC_PROBE_GEMM_NT);
+}
+
 void probe_begin(int family, hipStream_t s) {
-  if (g_probe.family.load(std::memory_order_relaxed) != family || family == NC_PROBE_OFF) return;
+  if (!probe_match(g_probe.family.load(std::memory_order_relaxed), family)) return;
   std::lock_guard<std::mutex> lk(g_probe.mu);
-  if (g_probe.family.load() != family) return;
+  if (!probe_match(g_probe.family.load(), family)) return;
   if (2 * (g_probe.used + 1) > (int)g_probe.ev.size()) {
     ++g_probe.dropped;
     return;
@@ -61,9 +68,9 @@ void probe_begin(int family, hipStream_t s) {
 }
 
 void probe_end(int family, hipStream_t s, double flops) {
-  if (g_probe.family.load(std::memory_order_relaxed) != family || family == NC_PROBE_OFF) return;
+  if (!probe_match(g_probe.family.load(std::memory_order_relaxed), family)) return;
   std::lock_guard<std::mutex> lk(g_probe.mu);
-  if (g_probe.family.load() != family || g_probe.open != g_probe.used) return;
+  if (!probe_match(g_probe.family.load(), family) || g_probe.open != g_probe.used) return;
   (void)hipEventRecord(g_probe.ev[2 * g_probe.used + 1], s);
   g_probe.flops += flops;
   ++g_probe.used;
@@ -73,7 +80,7 @@ void probe_end(int family, hipStream_t s, double flops) {
 }  // namespace nc
 
 extern "C" int nc_probe_start(int family, int max_launches) {
-  NC_REQUIRE(family >= NC_PROBE_OFF && family <= NC_PROBE_DECODE_ATTN, NC_ERR_INVALID_ARG, "probe: unknown family %d",
+  NC_REQUIRE(family >= NC_PROBE_OFF && family <= NC_PROBE_GEMM, NC_ERR_INVALID_ARG, "probe: unknown family %d",
              family);
   NC_REQUIRE(max_launches >= 0 && max_launches <= (1 << 20), NC_ERR_INVALID_ARG, "probe: max_launches %d",
              max_launches);

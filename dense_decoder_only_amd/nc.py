@@ -22,7 +22,7 @@ NC_OK, NC_ERR_INVALID_ARG, NC_ERR_UNSUPPORTED, NC_ERR_WORKSPACE, NC_ERR_HIP, NC_
 NC_F32, NC_BF16 = 0, 1
 NC_EPI_STORE, NC_EPI_RELU2, NC_EPI_RELU2_BWD, NC_EPI_RELU2_SQ, NC_EPI_RELU2_BWD_SQ = 0, 1, 2, 3, 4
 (NC_PROBE_OFF, NC_PROBE_GEMM_WGRAD, NC_PROBE_GEMM_NT, NC_PROBE_ATTN_FWD, NC_PROBE_ATTN_DQ,
- NC_PROBE_ATTN_DKV, NC_PROBE_GEMM_SKINNY, NC_PROBE_DECODE_ATTN) = range(8)
+ NC_PROBE_ATTN_DKV, NC_PROBE_GEMM_SKINNY, NC_PROBE_DECODE_ATTN, NC_PROBE_GEMM) = range(9)
 
 c_int, c_i64, c_f, c_sz, c_p = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 

@@ -144,7 +144,8 @@ typedef enum {
   NC_PROBE_ATTN_DQ = 4,    /* attention backward, dQ kernel                          */
   NC_PROBE_ATTN_DKV = 5,   /* attention backward, dK/dV kernel                       */
   NC_PROBE_GEMM_SKINNY = 6, /* small-M GEMMs (M <= 128, decoding): counts bytes       */
-  NC_PROBE_DECODE_ATTN = 7  /* decode attention over the key/value cache: bytes       */
+  NC_PROBE_DECODE_ATTN = 7, /* decode attention over the key/value cache: bytes       */
+  NC_PROBE_GEMM = 8         /* every matrix-core GEMM launch: families 1 and 2 together */
 } nc_probe_family;
 
 int nc_probe_start(int family, int max_launches);

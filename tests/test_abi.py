@@ -82,6 +82,15 @@ def test_step_workspace_query_and_config_validation():
     assert rc == nc.NC_ERR_INVALID_ARG
 
 
+def test_kernel_timer_rejects_unknown_families():
+    from dense_decoder_only_amd import nc
+    lib = nc.load()
+    for fam in (-1, nc.NC_PROBE_GEMM + 1):
+        assert lib.nc_probe_start(fam, 4) == nc.NC_ERR_INVALID_ARG
+        assert "unknown family" in nc.nc_last_error()
+    assert lib.nc_probe_start(nc.NC_PROBE_GEMM, -1) == nc.NC_ERR_INVALID_ARG
+
+
 def test_adamw_host_validation():
     from dense_decoder_only_amd import nc
     lib = nc.load()

@@ -247,8 +247,10 @@ def _gemm_operands(r, ta, tb, M, N, K, dtype):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("ta,tb", [(0, 1), (0, 0), (1, 0), (1, 1)])
-@pytest.mark.parametrize("M,N,K", [(264, 392, 200), (512, 256, 1024), (8, 8, 8)])
+@pytest.mark.parametrize("M,N,K", [(264, 392, 200), (512, 256, 1024), (8, 8, 8), (320, 264, 1344), (256, 256, 64)])
 def test_gemm_layouts_and_store(dtype, ta, tb, M, N, K):
+    # K = 1344 and 64: an odd number of 64-deep k-tiles (the pipelined kernel
+    # runs its k loop two tiles at a time, one per LDS stage)
     n = nc()
     r = rng(M + N + K + 10 * ta + tb)
     A, Bm, ref = _gemm_operands(r, ta, tb, M, N, K, dtype)
@@ -321,6 +323,31 @@ def test_gemm_split_k_is_deterministic():
     n.nc_gemm_bf16(1, 0, M, N, K, A, M, Bm, N, C3, N)  # no workspace: single pass
     sync()
     assert_close(dev_to_f64(C3), ref, 1e-4, 1e-5, "unsplit gemm")
+
+
+def test_kernel_timer_gemm_families():
+    """The kernel timer brackets exactly the launches of the armed family;
+    NC_PROBE_GEMM takes both matrix-core forms."""
+    n = nc()
+    r = rng(11)
+    M, N, K = 512, 256, 1024
+    A1, B1, _ = _gemm_operands(r, 0, 1, M, N, K, BF16)   # K-contiguous form
+    A2, B2, _ = _gemm_operands(r, 1, 0, M, N, K, BF16)   # weight-gradient form
+    C = torch.empty((M, N), dtype=F32, device=DEV)
+
+    def both():
+        n.nc_gemm_bf16(0, 1, M, N, K, A1, K, B1, K, C, N)
+        n.nc_gemm_bf16(1, 0, M, N, K, A2, M, B2, N, C, N)
+
+    flops = 2.0 * M * N * K
+    for fam, want in ((n.NC_PROBE_GEMM, 2), (n.NC_PROBE_GEMM_NT, 1), (n.NC_PROBE_GEMM_WGRAD, 1),
+                      (n.NC_PROBE_ATTN_FWD, 0)):
+        n.nc_probe_start(fam, 8)
+        both()
+        ms, launches, fl = n.nc_probe_stop()
+        assert launches == want, (fam, launches)
+        assert fl == want * flops
+        assert (ms > 0) == (want > 0)
 
 
 # ------------------------------------------------------ relu^2 MLP block --
