@@ -1,0 +1,147 @@
+// dQ kernel of the matrix-core attention backward (head_dim 128, bf16); the
+// register and LDS layouts are those described at the top of attn_mfma.hip.
+// It sits in a file of its own: at 256 VGPRs and two waves per SIMD it is
+// at the edge of spilling, and its register allocation then does not move
+// with edits to the other attention kernels.
+#include "attn_mfma_dev.h"
+
+namespace nc {
+namespace {
+
+// ----------------------------------------------------------------------- dQ --
+// Also writes D = rowsum(dO * O) for the key-side kernel.
+#ifndef NC_ATTN_DQ_WAVES
+#define NC_ATTN_DQ_WAVES 2  // waves per SIMD the dQ kernel is compiled for
+#endif
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC_ATTN_DQ_WAVES, NC_ATTN_DQ_WAVES))) void attn_dq_kernel(AttnMfmaArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2 * TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2 * TILE];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
+  const int H = a.H, T = a.T;
+  const int R = T * H;
+  const int nrb = (R + QB - 1) / QB;
+  const int rb = nrb - 1 - (int)blockIdx.y;
+  const int b = blockIdx.x;
+  const int r0 = rb * QB;
+  const bf16* base = a.qkv + (int64_t)b * T * a.S;
+
+  const int myr = r0 + w * 32 + lc;
+  const bool valid = myr < R;
+  const int rr = valid ? myr : R - 1;
+  const int tq = rr / H;
+  const int hq = rr - tq * H;
+  bf16x8_t qreg[8], dreg[8];
+  float dpart = 0.f;
+  {
+    const bf16* qp = base + (int64_t)tq * a.S + hq * HD + 8 * h;
+    const bf16* dp = a.dout + ((int64_t)b * R + rr) * HD + 8 * h;
+    const bf16* op = a.o + ((int64_t)b * R + rr) * HD + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qreg[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
+      const uint4 dv = *reinterpret_cast<const uint4*>(dp + ks * 16);
+      const uint4 ov = *reinterpret_cast<const uint4*>(op + ks * 16);
+      dreg[ks] = __builtin_bit_cast(bf16x8_t, dv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = wd(dv, e), y = wd(ov, e);
+        dpart += __uint_as_float(x << 16) * __uint_as_float(y << 16) +
+                 __uint_as_float(x & 0xffff0000u) * __uint_as_float(y & 0xffff0000u);
+      }
+    }
+  }
+  const float D = dpart + __shfl_xor(dpart, 32, 64);
+  const float lse2 = a.lse[(int64_t)b * R + rr] * LOG2E;
+  if (valid && h == 0) a.Dbuf[(int64_t)b * R + myr] = D;
+
+  const int tmin = r0 / H;
+  const int tmax = min(T - 1, (min(r0 + QB, R) - 1) / H);
+  const int ntiles = tmax / KT + 1;
+  auto stage = [&](int j, int buf) {
+    const int kv0 = j * KT;
+    dma_tile(Ks + buf * TILE, w, lane,
+             [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + H * HD; });
+    dma_tile(Vs + buf * TILE, w, lane,
+             [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + (H + 1) * HD; });
+  };
+  f32x16 dq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dq[i] = zero16();
+
+  stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
+    const int kv0 = j * KT;
+    if (j + 1 < ntiles) stage(j + 1, cur ^ 1);
+    const bf16* K = Ks + cur * TILE;
+    const bf16* V = Vs + cur * TILE;
+
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      s[st] = zero16();
+      dp[st] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        s[st] = mfma(frag_row(K, st * 32 + lc, 2 * ks + h), qreg[ks], s[st]);
+        dp[st] = mfma(frag_row(V, st * 32 + lc, 2 * ks + h), dreg[ks], dp[st]);
+      }
+    }
+    if (kv0 + KT - 1 > tmin) {  // the tile crosses some row's diagonal
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kv = kv0 + st * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const float p = kv > tq ? 0.f : fexp2(s[st][r] * a.scale_log2 - lse2);
+          s[st][r] = p * (dp[st][r] - D);
+        }
+    } else {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fexp2(s[st][r] * a.scale_log2 - lse2);
+          s[st][r] = p * (dp[st][r] - D);
+        }
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) {
+        const bf16x8_t pb = pack_p(s[st], jp);
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) dq[ht] = mfma(frag_tr(K, st * 32 + 16 * jp, ht * 32, lane), pb, dq[ht]);
+      }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (valid) {
+    float* out = a.dqkv + ((int64_t)b * T + tq) * (int64_t)(H + 2) * HD + hq * HD;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int hd = ht * 32 + 8 * q4 + 4 * h;
+        *reinterpret_cast<float4*>(out + hd) =
+            make_float4(dq[ht][4 * q4] * a.scale, dq[ht][4 * q4 + 1] * a.scale, dq[ht][4 * q4 + 2] * a.scale,
+                        dq[ht][4 * q4 + 3] * a.scale);
+      }
+  }
+}
+
+}  // namespace
+
+int attn_mfma_dq(const AttnMfmaArgs& a, hipStream_t s) {
+  const int nrb = (a.T * a.H + QB - 1) / QB;
+  const double fl = 2.0 * a.B * a.H * (double)HD * a.T * a.T;
+  probe_begin(NC_PROBE_ATTN_DQ, s);
+  attn_dq_kernel<<<dim3(a.B, nrb), 256, 0, s>>>(a);
+  probe_end(NC_PROBE_ATTN_DQ, s, fl);
+  return check_launch("attn_dq_kernel");
+}
+
+}  // namespace nc

@@ -25,5 +25,7 @@ size_t attn_mfma_bwd_workspace_bytes(int B, int T, int H);
 int attn_mfma_fwd(const void* qkv, int B, int T, int H, float scale, void* o, float* lse, hipStream_t s);
 int attn_mfma_bwd(const void* qkv, const void* o, const void* dout, const float* lse, int B, int T, int H, float scale,
                   float* dqkv, void* ws, hipStream_t s);
+// The dQ launch of attn_mfma_bwd (also writes D = rowsum(dO * O) to a.Dbuf).
+int attn_mfma_dq(const AttnMfmaArgs& a, hipStream_t s);
 
 }  // namespace nc

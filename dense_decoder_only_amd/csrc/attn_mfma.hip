@@ -42,94 +42,11 @@
 // range split into chunks so that early key blocks do not serialize, partials
 // summed in a fixed order by a reduce kernel).  No atomics; results are
 // bitwise reproducible.
-#include "common.h"
-#include "attn_mfma.h"
+
+#include "attn_mfma_dev.h"
 
 namespace nc {
 namespace {
-
-constexpr int HD = 128;
-constexpr int QB = 128;   // query rows per forward / dQ block (4 waves x 32)
-constexpr int KT = 64;    // keys per tile
-constexpr int KB = 128;   // keys per dK/dV block (4 waves x 32)
-constexpr int QT = 64;    // query rows per dK/dV tile
-constexpr int QCH = 5120; // query rows per dK/dV split
-#ifndef NC_DKV_PF
-#define NC_DKV_PF 4       // dK/dV: fragment pairs in the S / dP read ring
-#endif
-constexpr int TILE = 64 * HD;  // elements of one [64][128] tile
-constexpr int QTILE = QT * HD; // elements of one dK/dV query tile
-constexpr float LOG2E = 1.4426950408889634f;
-
-typedef __bf16 bf16x4_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
-
-__device__ __forceinline__ int tswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-// element offset of (row, 8-column chunk c) in a swizzled [rows][128] tile
-__device__ __forceinline__ int toff(int row, int c) { return row * HD + ((c ^ tswz(row)) << 3); }
-
-// Direct global -> LDS staging of a [ROWS][128] tile: ROWS / 4 instructions
-// of 1 KB (4 rows each), ROWS / 16 per wave.  rowp(row) gives the global
-// address of a row.
-template <int ROWS = 64, typename RowPtr>
-__device__ __forceinline__ void dma_tile(bf16* S, int wave, int lane, RowPtr rowp) {
-  const int rsub = lane >> 4, cp = lane & 15;
-#pragma unroll
-  for (int i = 0; i < ROWS / 16; ++i) {
-    const int g = wave * (ROWS / 16) + i;
-    const int row = g * 4 + rsub;
-    const int c = cp ^ tswz(row);
-    __builtin_amdgcn_global_load_lds(rowp(row) + c * 8, (__attribute__((address_space(3))) void*)(S + g * 4 * HD),
-                                     16, 0, 0);
-  }
-}
-
-// MFMA operand: 8 consecutive columns (chunk c) of `row`.
-__device__ __forceinline__ bf16x8_t frag_row(const bf16* S, int row, int c) {
-  return *reinterpret_cast<const bf16x8_t*>(S + toff(row, c));
-}
-
-// MFMA A operand of X^T from a row-major tile X: output rows are the columns
-// col0 .. col0 + 31 of X, k-slots are rows rbase + 8 (e >> 2) + 4 h + (e & 3).
-__device__ __forceinline__ bf16x8_t frag_tr(const bf16* S, int rbase, int col0, int lane) {
-  const int g = lane >> 4, p = lane & 15, h = lane >> 5;
-  const int col = col0 + 16 * (g & 1) + 4 * (p & 3);
-  const int r1 = rbase + 4 * h + (p >> 2);
-  const bf16* a1 = S + toff(r1, col >> 3) + (col & 7);
-  const bf16* a2 = S + toff(r1 + 8, col >> 3) + (col & 7);
-  const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)a1);
-  const bf16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)a2);
-  const uint2 u = __builtin_bit_cast(uint2, x), v = __builtin_bit_cast(uint2, y);
-  return __builtin_bit_cast(bf16x8_t, make_uint4(u.x, u.y, v.x, v.y));
-}
-
-// Registers r = 8 jp .. 8 jp + 7 of a score tile, rounded to bf16, as the
-// B operand of the next product.
-__device__ __forceinline__ bf16x8_t pack_p(const f32x16& p, int jp) {
-  const int b = jp * 8;
-  return __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16x2(p[b + 0], p[b + 1]), pack_bf16x2(p[b + 2], p[b + 3]),
-                                                 pack_bf16x2(p[b + 4], p[b + 5]), pack_bf16x2(p[b + 6], p[b + 7])));
-}
-
-// 2^x by the hardware v_exp_f32 (results below 2^-126 flush to zero, which
-// is immaterial for probabilities that are summed with ones of order 1).
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ int div_h(int r, uint32_t hmagic) { return (int)__umulhi((uint32_t)r, hmagic); }
-
-__device__ __forceinline__ f32x16 mfma(bf16x8_t a, bf16x8_t b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x16 zero16() {
-  f32x16 z;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) z[i] = 0.f;
-  return z;
-}
-
-__device__ __forceinline__ uint32_t wd(const uint4& q, int w) {
-  return w == 0 ? q.x : (w == 1 ? q.y : (w == 2 ? q.z : q.w));
-}
 
 // ------------------------------------------------------------------ forward --
 // grid (B, ceil(R / QB)); heavy (late) row blocks first.
@@ -267,131 +184,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                        pack_bf16x2(o[ht][4 * q4 + 2] * inv, o[ht][4 * q4 + 3] * inv));
       }
     if (h == 0) a.lse_out[(int64_t)b * R + myr] = (m_run + log2f(l_run)) * (1.f / LOG2E);
-  }
-}
-
-// ----------------------------------------------------------------------- dQ --
-// Also writes D = rowsum(dO * O) for the key-side kernel.
-#ifndef NC_ATTN_DQ_WAVES
-#define NC_ATTN_DQ_WAVES 2  // waves per SIMD the dQ kernel is compiled for
-#endif
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC_ATTN_DQ_WAVES, NC_ATTN_DQ_WAVES))) void attn_dq_kernel(AttnMfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2 * TILE];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2 * TILE];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
-  const int H = a.H, T = a.T;
-  const int R = T * H;
-  const int nrb = (R + QB - 1) / QB;
-  const int rb = nrb - 1 - (int)blockIdx.y;
-  const int b = blockIdx.x;
-  const int r0 = rb * QB;
-  const bf16* base = a.qkv + (int64_t)b * T * a.S;
-
-  const int myr = r0 + w * 32 + lc;
-  const bool valid = myr < R;
-  const int rr = valid ? myr : R - 1;
-  const int tq = rr / H;
-  const int hq = rr - tq * H;
-  bf16x8_t qreg[8], dreg[8];
-  float dpart = 0.f;
-  {
-    const bf16* qp = base + (int64_t)tq * a.S + hq * HD + 8 * h;
-    const bf16* dp = a.dout + ((int64_t)b * R + rr) * HD + 8 * h;
-    const bf16* op = a.o + ((int64_t)b * R + rr) * HD + 8 * h;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      qreg[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
-      const uint4 dv = *reinterpret_cast<const uint4*>(dp + ks * 16);
-      const uint4 ov = *reinterpret_cast<const uint4*>(op + ks * 16);
-      dreg[ks] = __builtin_bit_cast(bf16x8_t, dv);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t x = wd(dv, e), y = wd(ov, e);
-        dpart += __uint_as_float(x << 16) * __uint_as_float(y << 16) +
-                 __uint_as_float(x & 0xffff0000u) * __uint_as_float(y & 0xffff0000u);
-      }
-    }
-  }
-  const float D = dpart + __shfl_xor(dpart, 32, 64);
-  const float lse2 = a.lse[(int64_t)b * R + rr] * LOG2E;
-  if (valid && h == 0) a.Dbuf[(int64_t)b * R + myr] = D;
-
-  const int tmin = r0 / H;
-  const int tmax = min(T - 1, (min(r0 + QB, R) - 1) / H);
-  const int ntiles = tmax / KT + 1;
-  auto stage = [&](int j, int buf) {
-    const int kv0 = j * KT;
-    dma_tile(Ks + buf * TILE, w, lane,
-             [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + H * HD; });
-    dma_tile(Vs + buf * TILE, w, lane,
-             [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + (H + 1) * HD; });
-  };
-  f32x16 dq[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dq[i] = zero16();
-
-  stage(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int cur = j & 1;
-    const int kv0 = j * KT;
-    if (j + 1 < ntiles) stage(j + 1, cur ^ 1);
-    const bf16* K = Ks + cur * TILE;
-    const bf16* V = Vs + cur * TILE;
-
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      s[st] = zero16();
-      dp[st] = zero16();
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s[st] = mfma(frag_row(K, st * 32 + lc, 2 * ks + h), qreg[ks], s[st]);
-        dp[st] = mfma(frag_row(V, st * 32 + lc, 2 * ks + h), dreg[ks], dp[st]);
-      }
-    }
-    if (kv0 + KT - 1 > tmin) {  // the tile crosses some row's diagonal
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kv = kv0 + st * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          const float p = kv > tq ? 0.f : fexp2(s[st][r] * a.scale_log2 - lse2);
-          s[st][r] = p * (dp[st][r] - D);
-        }
-    } else {
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fexp2(s[st][r] * a.scale_log2 - lse2);
-          s[st][r] = p * (dp[st][r] - D);
-        }
-    }
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int jp = 0; jp < 2; ++jp) {
-        const bf16x8_t pb = pack_p(s[st], jp);
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht) dq[ht] = mfma(frag_tr(K, st * 32 + 16 * jp, ht * 32, lane), pb, dq[ht]);
-      }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-
-  if (valid) {
-    float* out = a.dqkv + ((int64_t)b * T + tq) * (int64_t)(H + 2) * HD + hq * HD;
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int hd = ht * 32 + 8 * q4 + 4 * h;
-        *reinterpret_cast<float4*>(out + hd) =
-            make_float4(dq[ht][4 * q4] * a.scale, dq[ht][4 * q4 + 1] * a.scale, dq[ht][4 * q4 + 2] * a.scale,
-                        dq[ht][4 * q4 + 3] * a.scale);
-      }
   }
 }
 
@@ -664,12 +456,8 @@ int attn_mfma_bwd(const void* qkv, const void* o, const void* dout, const float*
   a.nkb = (T + KB - 1) / KB;
   a.smax = attn_mfma_smax(T, H);
   a.hmagic = (uint32_t)((((uint64_t)1 << 32) + H - 1) / H);
-  const int nrb = (T * H + QB - 1) / QB;
   const double fl = 2.0 * B * H * (double)HD * T * T;
-  probe_begin(NC_PROBE_ATTN_DQ, s);
-  attn_dq_kernel<<<dim3(B, nrb), 256, 0, s>>>(a);
-  probe_end(NC_PROBE_ATTN_DQ, s, fl);
-  NC_TRY(check_launch("attn_dq_kernel"));
+  NC_TRY(attn_mfma_dq(a, s));
   probe_begin(NC_PROBE_ATTN_DKV, s);
   attn_dkv_kernel<<<dim3(B, a.nkb * a.smax), 256, 0, s>>>(a);
   probe_end(NC_PROBE_ATTN_DKV, s, fl);
