@@ -80,10 +80,9 @@ __device__ __forceinline__ float softcap_of(float z, float c, float inv_c) {
   return copysignf(c * (1.f - t) * __builtin_amdgcn_rcpf(1.f + t), x);
 }
 
-// Logit-gradient epilogue on four consecutive columns of one row.
-__device__ __forceinline__ void xent_bwd4(const MfmaParams& p, float4 v, int row, int col) {
-  const float L = p.xlse[row] * kLog2e;
-  const int y = p.xtgt[row] - p.xv0;
+// Logit-gradient epilogue on four consecutive columns of one row; y is the
+// row's target column (relative to xv0), L its log-sum-exp times log2(e).
+__device__ __forceinline__ void xent_bwd4(const MfmaParams& p, float4 v, int row, int col, int y, float L) {
   const float zz[4] = {v.x, v.y, v.z, v.w};
   float g[4];
 #pragma unroll
@@ -98,10 +97,10 @@ __device__ __forceinline__ void xent_bwd4(const MfmaParams& p, float4 v, int row
 }
 
 // Forward cross-entropy epilogue: a 16-lane group holds one row's 64 columns
-// (4 per lane); every lane of the group must call this (it shuffles).
-__device__ __forceinline__ void xent_fwd4(const MfmaParams& p, float4 v, int row, int col, int gcol64) {
+// (4 per lane); every lane of the group must call this (it shuffles).  y is
+// the row's target column relative to xv0 (-1 for rows past M).
+__device__ __forceinline__ void xent_fwd4(const MfmaParams& p, float4 v, int row, int col, int gcol64, int y) {
   const bool ok = row < p.M;
-  const int y = ok ? p.xtgt[row] - p.xv0 : -1;
   const float zz[4] = {v.x, v.y, v.z, v.w};
   float s = 0.f;
   float zq[4] = {0.f, 0.f, 0.f, 0.f};
@@ -269,9 +268,8 @@ __device__ __forceinline__ void epilogue4(const MfmaParams& p, float4 v, int row
     const float r3 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.y >> 16)));
     *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + off) =
         make_uint2(pack_bf16x2(v.x * 2.f * r0, v.y * 2.f * r1), pack_bf16x2(v.z * 2.f * r2, v.w * 2.f * r3));
-  } else if constexpr (EPI == E_XENT_BWD) {
-    xent_bwd4(p, v, row, col);
   } else {  // E_PARTIAL: [split][M][N] fp32
+    static_assert(EPI == E_PARTIAL, "the cross-entropy epilogues are the pipelined kernel's own");
     *reinterpret_cast<float4*>(static_cast<float*>(p.C) + (int64_t)blockIdx.z * p.M * p.N +
                                (int64_t)row * p.N + col) = v;
   }
@@ -881,6 +879,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) bf16 sA1[BM * BK];
   __shared__ __attribute__((aligned(16))) bf16 sB0[BN * BK];
   __shared__ __attribute__((aligned(16))) bf16 sB1[BN * BK];
+  // cross-entropy epilogues: the block's row targets (and log-sum-exps),
+  // fetched before the k loop so that their latency is hidden by it
+  constexpr bool XENT = EPI == E_XENT_FWD || EPI == E_XENT_BWD;
+  __shared__ int32_t s_xt[XENT ? BM : 1];
+  __shared__ float s_xl[EPI == E_XENT_BWD ? BM : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -915,6 +918,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   kend = kend < p.K ? kend : p.K;
   const int nk = (kend - kbeg) / BK;
   const int klast = kbeg + (nk - 1) * BK;
+  if constexpr (XENT) {
+    if (tid < BM) {
+      const int r = m0 + tid;
+      s_xt[tid] = r < p.M ? p.xtgt[r] - p.xv0 : -1;
+      if constexpr (EPI == E_XENT_BWD) s_xl[tid] = r < p.M ? p.xlse[r] * kLog2e : 0.f;
+    }
+  }
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -1056,10 +1066,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float4 v = *reinterpret_cast<const float4*>(stage + row * SROW + c4);
       const int grow = m0 + wm * 128 + i * 32 + row, gcol = n0 + wn * 64 + c4;
       if constexpr (EPI == E_XENT_FWD) {
-        xent_fwd4(p, v, grow, gcol, n0 + wn * 64);
+        xent_fwd4(p, v, grow, gcol, n0 + wn * 64, s_xt[grow - m0]);
       } else if (grow < p.M && gcol < p.N) {
         const int64_t off = (int64_t)grow * p.ldc + gcol;
-        if constexpr (EPI == E_RELU2_BWD_SQ) {
+        if constexpr (EPI == E_XENT_BWD) {
+          xent_bwd4(p, v, grow, gcol, s_xt[grow - m0], s_xl[grow - m0]);
+        } else if constexpr (EPI == E_RELU2_BWD_SQ) {
           const uint2 q = pa[i][it];
           const float r0 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.x & 0xffffu)));
           const float r1 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.x >> 16)));
