@@ -69,7 +69,10 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(const TG* __restri
   if (row >= rows) return;
   const TG* gr = g + row * d;
   const TY* yr = y + row * d;
-  float4 gv[CV], yv[CV];
+  float* dr = dx + row * d;
+  // the accumulated dx is loaded with g and y, ahead of the row reduction,
+  // so that its latency is not paid a second time after it
+  float4 gv[CV], yv[CV], pv[CV];
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < CV; ++k) {
@@ -77,22 +80,21 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(const TG* __restri
     if (c < d) {
       gv[k] = load4(gr + c);
       yv[k] = load4(yr + c);
-      s += dot4(gv[k], yv[k]);
+      pv[k] = accumulate ? load4(dr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
-  const float mean = wave_sum(s) / (float)d;
+#pragma unroll
+  for (int k = 0; k < CV; ++k)
+    if (lane * 4 + k * 256 < d) s += dot4(gv[k], yv[k]);
   const float r = rstd[row];
-  float* dr = dx + row * d;
+  const float mean = wave_sum(s) / (float)d;
 #pragma unroll
   for (int k = 0; k < CV; ++k) {
     const int c = lane * 4 + k * 256;
     if (c < d) {
       float4 o = make_float4(r * (gv[k].x - yv[k].x * mean), r * (gv[k].y - yv[k].y * mean),
                              r * (gv[k].z - yv[k].z * mean), r * (gv[k].w - yv[k].w * mean));
-      if (accumulate) {
-        const float4 p = load4(dr + c);
-        o = make_float4(o.x + p.x, o.y + p.y, o.z + p.z, o.w + p.w);
-      }
+      if (accumulate) o = make_float4(o.x + pv[k].x, o.y + pv[k].y, o.z + pv[k].z, o.w + pv[k].w);
       store4(dr + c, o);
       if (dx_bf16) store4(dx_bf16 + row * d + c, o);
     }

@@ -182,36 +182,55 @@ __global__ __launch_bounds__(256) void xent_bwd_rows_kernel(const float* __restr
 }
 
 // dz from the stored logits, in place: q = round(z'/c * 32767) (int16) ->
-// dz = dloss (exp(z' - lse) - [v == y]) (1 - (z'/c)^2) (bf16), 8 per thread.
-// One chunk covering the whole vocabulary (column = vocabulary id).
+// dz = dloss (exp(z' - lse) - [v == y]) (1 - (z'/c)^2) (bf16).  One chunk
+// covering the whole vocabulary (column = vocabulary id).  A block streams
+// rows (its row's log-sum-exp and target read once), each thread 8
+// consecutive columns per 16-byte access with DZ_UNROLL accesses in flight;
+// the logits are read once and dz written once, so both go around the caches.
+constexpr int DZ_UNROLL = 4;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t dz_pair(uint32_t w, int col, int y, float L2, float c2, float inv, float dloss) {
+  float g2[2];
+#pragma unroll
+  for (int hlf = 0; hlf < 2; ++hlf) {
+    const int16_t qi = (int16_t)(hlf ? (w >> 16) : (w & 0xffffu));
+    const float th = (float)qi * inv;  // z' / c
+    const float pr = __builtin_amdgcn_exp2f(c2 * th - L2);  // exp(z' - lse) by the hardware exp2
+    g2[hlf] = dloss * (pr - (col + hlf == y ? 1.f : 0.f)) * (1.f - th * th);
+  }
+  return pack_bf16x2(g2[0], g2[1]);
+}
+
 __global__ __launch_bounds__(256) void xent_dz_stored_kernel(uint16_t* __restrict__ buf, int64_t M, int N, float c,
                                                              const int32_t* __restrict__ tgt,
                                                              const float* __restrict__ lse, float dloss) {
-  const int64_t total8 = M * N / 8;
   const float inv = 1.f / 32767.f;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total8; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e0 = i * 8;
-    const int64_t row = e0 / N;
-    const int col = (int)(e0 - row * N);
+  const float c2 = c * 1.4426950408889634f;
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
     const float L2 = lse[row] * 1.4426950408889634f;
-    const float c2 = c * 1.4426950408889634f;
     const int y = tgt[row];
-    uint4 q = *reinterpret_cast<const uint4*>(buf + e0);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    uint32_t o[4];
+    u32x4_t* rb = reinterpret_cast<u32x4_t*>(buf + row * N);
+    const int n16 = N >> 3;  // 16-byte groups in the row
+    for (int i0 = threadIdx.x; i0 < n16; i0 += 256 * DZ_UNROLL) {
+      u32x4_t q[DZ_UNROLL];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float g2[2];
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        const int16_t qi = (int16_t)(hlf ? (w[k] >> 16) : (w[k] & 0xffffu));
-        const float th = (float)qi * inv;  // z' / c
-        const float pr = __builtin_amdgcn_exp2f(c2 * th - L2);  // exp(z' - lse) by the hardware exp2
-        g2[hlf] = dloss * (pr - (col + 2 * k + hlf == y ? 1.f : 0.f)) * (1.f - th * th);
+      for (int u = 0; u < DZ_UNROLL; ++u) {
+        const int i = i0 + u * 256;
+        q[u] = i < n16 ? __builtin_nontemporal_load(rb + i) : u32x4_t{0u, 0u, 0u, 0u};
       }
-      o[k] = pack_bf16x2(g2[0], g2[1]);
+#pragma unroll
+      for (int u = 0; u < DZ_UNROLL; ++u) {
+        const int i = i0 + u * 256;
+        if (i < n16) {
+          const int col = i * 8;
+          const uint32_t w0 = q[u].x, w1 = q[u].y, w2 = q[u].z, w3 = q[u].w;
+          const u32x4_t o = {dz_pair(w0, col, y, L2, c2, inv, dloss), dz_pair(w1, col + 2, y, L2, c2, inv, dloss),
+                             dz_pair(w2, col + 4, y, L2, c2, inv, dloss), dz_pair(w3, col + 6, y, L2, c2, inv, dloss)};
+          __builtin_nontemporal_store(o, rb + i);
+        }
+      }
     }
-    *reinterpret_cast<uint4*>(buf + e0) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -322,8 +341,7 @@ int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
     g.dtype = dtype;
     if (fused && from_stored) {
       NC_REQUIRE(nch == 1, NC_ERR_INVALID_ARG, "softcap_xent_bwd: stored logits need a one-chunk vocabulary");
-      const int64_t total8 = (int64_t)M * n / 8;
-      xent_dz_stored_kernel<<<(unsigned)std::min<int64_t>(cdiv(total8, 256), 65536), 256, 0, s>>>(
+      xent_dz_stored_kernel<<<(unsigned)std::min<int64_t>(M, 1 << 30), 256, 0, s>>>(
           static_cast<uint16_t*>(w.dz), M, n, softcap, tgt, lse, dloss);
       NC_TRY(check_launch("xent_dz_stored_kernel"));
     } else if (fused) {
