@@ -174,6 +174,51 @@ def test_prefill_then_decode_small():
         _check_logits(dev_to_f64(logits), np.stack(rows), f"decode step {j}")
 
 
+def test_decode_steps_replay_from_a_graph():
+    """Three decode steps captured once into a HIP graph (the library records
+    kernels only, no memset nodes) replay to the eager logits bit for bit,
+    with eager prefills and synchronizations between the replays."""
+    n = _nc()
+    T0, B, max_len, steps = 24, 2, 32, 3
+    cfg = dataclasses.replace(CONFIGS["small"], seq_len=T0, batch=B)
+    inp = make_inputs(CONFIGS["small"])
+    params = _device_params(inp)
+    prompts = torch.from_numpy(make_tokens(cfg, seed=21)[:, :T0]).to(DEV)
+    extra = make_tokens(cfg, seed=22)[:, :steps]
+    ccfg = n.make_config(cfg)
+    kv = torch.empty(n.nc_kv_cache_bytes(ccfg, max_len), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(n.nc_infer_workspace_bytes(ccfg, max_len), dtype=torch.uint8, device=DEV)
+    logits = torch.empty(B, cfg.vocab, device=DEV)
+    pos = [torch.full((B,), T0 + j, dtype=torch.int32, device=DEV) for j in range(steps)]
+    ids = [torch.from_numpy(np.ascontiguousarray(extra[:, j])).to(DEV) for j in range(steps)]
+    out = torch.empty(steps, B, cfg.vocab, device=DEV)
+
+    def decode():  # library launches only: each step writes its own logits rows
+        st = torch.cuda.current_stream()
+        for j in range(steps):
+            n.nc_decode_step(ccfg, params, ids[j], pos[j], kv, max_len, out[j], ws, stream=st)
+
+    n.nc_prefill(ccfg, params, prompts, kv, max_len, logits, ws)
+    decode()
+    torch.cuda.synchronize()
+    assert n.nc_sync_status(ws) == n.NC_OK
+    ref = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        decode()
+    torch.cuda.synchronize()
+    for r in range(3):
+        n.nc_prefill(ccfg, params, prompts, kv, max_len, logits, ws)
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert n.nc_sync_status(ws) == n.NC_OK
+        assert torch.equal(out, ref), f"replay {r} differs from the eager steps"
+
+
 def test_decode_flags_bad_position_and_id():
     n = _nc()
     cfg = dataclasses.replace(CONFIGS["small"], seq_len=8, batch=2)
