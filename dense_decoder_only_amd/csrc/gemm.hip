@@ -4,26 +4,29 @@
 // MLP uses relu^2).
 //
 // bf16 path (gfx950 matrix cores): C[M,N] = sum_k A'[m,k] B'[k,n] with fp32
-// accumulation in v_mfma_f32_32x32x16_bf16.
-//   * Block tile 256 x 256 x 64, 256 threads = 4 waves in a 2 x 2 grid, each
-//     wave owning a 128 x 128 sub-tile = 4 x 4 MFMA tiles (256 accumulators
-//     per lane, held in AGPRs).
-//   * Both operands are staged into LDS as [256 rows][64 k] bf16 tiles with
-//     the 16-byte chunk index XOR-swizzled by (row & 7), so the MFMA fragment
-//     reads (one 16-byte ds_read per fragment) and the staging writes are
-//     free of bank conflicts.  Two LDS buffers (128 KB) let the global loads
-//     of tile k+1 overlap the MFMAs of tile k with one barrier per k-tile.
-//   * K-contiguous operands are copied 16 bytes at a time.  M/N-contiguous
-//     operands (the transposed forms used by the backward) are read as 8x8
-//     bf16 blocks (eight 16-byte loads along m), transposed in registers and
-//     written as eight 16-byte LDS rows.
-//   * Epilogues are fused: bf16 or fp32 store, fp32 accumulate (residual
-//     add / gradient accumulation), relu^2 forward (u and relu(u)^2) and
-//     relu^2 backward (acc * 2 relu(u)); they are staged through LDS so that
-//     global stores are 16-byte and row-contiguous.
-//   * Tall-K problems with few output tiles (the weight gradients, K = B*T)
-//     split K over blockIdx.z into fp32 partials reduced in a fixed order, so
-//     results are bitwise reproducible.
+// accumulation in v_mfma_f32_32x32x16_bf16.  Three kernels:
+//   * gemm_pipe_kernel: every full-tile product of the step, in two forms
+//     (both operands K-contiguous, "NT"; both with K as rows, the weight
+//     gradients, "TN").  Block tile 256 x 256 x 64, 512 threads = 8 waves in
+//     a 2 x 4 grid of 128 x 64 wave tiles (two waves per SIMD).  Tiles go
+//     global -> LDS by buffer_load ... lds in two stages that are separate
+//     LDS objects (so the compiler does not make fragment reads wait for the
+//     DMA into the other stage), with a rotated k loop that issues the next
+//     DMA right after the barrier inside each k-tile's last k-step.  The NT
+//     form reads fragments as swizzled 16-byte rows, the TN form with
+//     ds_read_b64_tr_b16 straight from the tile as stored.
+//   * gemm_mfma8_kernel: the TN form when a k-tile is ragged (register
+//     transpose of 8 x 8 blocks instead of transposed LDS reads).
+//   * gemm_mfma_kernel: 4 waves of 128 x 128, single-buffered register
+//     staging or direct DMA; the remaining layouts (NN, TT, or K not a
+//     multiple of 64).
+// Epilogues are fused and staged through LDS so that global stores are
+// 16-byte and row-contiguous: bf16 or fp32 store, fp32 accumulate (residual
+// add / gradient accumulation), relu^2 forward, relu^2 backward from the
+// stored relu(u)^2, split-K partial products, and the softcap cross-entropy
+// terms of the logit product.  Tall-K problems with few output tiles (the
+// weight gradients, K = B*T) split K into fp32 partials reduced in a fixed
+// order, so results are bitwise reproducible.
 #include "common.h"
 #include "gemm.h"
 #include "ops.h"
