@@ -870,6 +870,12 @@ __device__ __forceinline__ void sched_mfma_ds() {
 template <bool TN>
 constexpr int pipe_nreads() { return TN ? 12 : 6; }
 
+// s_waitcnt immediate (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8) for vmcnt <= 8 with the other two counters left alone: a
+// stage is 8 DMA instructions per wave (4 for A, 4 for B) in every staging
+// form below (pipe_stage_buf, stage_direct8, stage_tn).
+constexpr int kWaitFirstStage = 8 | (7 << 4) | (15 << 8);
+
 template <int EPI, bool TN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pipe_kernel(MfmaParams p) {
   // The two stages of each operand are separate LDS objects and the k loop
@@ -946,8 +952,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #endif
   PIPE_STAGE(kbeg, sA0, sB0);
   PIPE_STAGE(nk > 1 ? kbeg + BK : kbeg, sA1, sB1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // Only the first stage has to have landed here (vmcnt <= the 8 DMAs of the
+  // second stage per wave, expcnt and lgkmcnt not waited on): the second
+  // one is waited for at the barrier inside the first k-tile.  A plain
+  // s_barrier, not __syncthreads: the latter's release fence would wait for
+  // every outstanding load, the second stage's DMA included.  The empty asm
+  // keeps the compiler from moving the first fragment reads above it.
+  __builtin_amdgcn_s_waitcnt(kWaitFirstStage);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 
   constexpr int NR = pipe_nreads<TN>();
   bf16x8_t fa[2][4], fb[2][2];
