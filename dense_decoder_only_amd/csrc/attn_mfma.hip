@@ -230,14 +230,46 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
   const int qs0 = qbeg_of(kb, H) + sp * QCH;
   const int qs1 = min(R, qs0 + QCH);
   const int nq = (qs1 - qs0 + QT - 1) / QT;
+  // Staging of the query tiles, through buffer resources.  Row r = t H + h of
+  // the folded query view sits at element t S + h HD of the sequence: not a
+  // fixed stride apart, so each lane keeps, for each of its DMA rows, that
+  // row's offset and head and advances both by one tile (QT rows: QT / H
+  // positions and QT % H heads, with a carry) per staged tile, in place of a
+  // division by H per row.  Rows past the end (offsets at or past T S) read
+  // row R - 1.  dO rows are HD apart.
+  const int S = (int)a.S;
+  const int dtq = QT / H, dhq = QT - dtq * H;
+  const int qinc = dtq * S + dhq * HD, qend = T * S, qlast = (T - 1) * S + (H - 1) * HD;
+  int qoff[QT / 16], qhd[QT / 16], dchk[QT / 16];
+#pragma unroll
+  for (int k = 0; k < QT / 16; ++k) {
+    const int row = (w * (QT / 16) + k) * 4 + (lane >> 4);
+    const int c8 = ((lane & 15) ^ tswz(row)) << 3;
+    const int r = qs0 + row, t = div_h(r, a.hmagic);
+    qhd[k] = r - t * H;
+    qoff[k] = t * S + qhd[k] * HD + c8;
+    dchk[k] = c8;
+  }
+  const __amdgpu_buffer_rsrc_t qrs = row_rsrc(base);
   auto stage = [&](int i, bf16* Qd, bf16* Gd) {
     const int q0 = qs0 + i * QT;
-    dma_tile<QT>(Qd, w, lane, [&](int row) {
-      const int r = min(q0 + row, R - 1);
-      const int t = div_h(r, a.hmagic);
-      return base + (int64_t)t * a.S + (r - t * H) * HD;
-    });
-    dma_tile<QT>(Gd, w, lane, [&](int row) { return dbase + (int64_t)min(q0 + row, R - 1) * HD; });
+    const __amdgpu_buffer_rsrc_t drs = row_rsrc(dbase + (int64_t)q0 * HD);
+#pragma unroll
+    for (int k = 0; k < QT / 16; ++k) {
+      const int g = w * (QT / 16) + k;
+      const int row = g * 4 + (lane >> 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (__attribute__((address_space(3))) void*)(Qd + g * 4 * HD), 16,
+                                               (uint32_t)(qoff[k] < qend ? qoff[k] : qlast + dchk[k]) * 2, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)(Gd + g * 4 * HD), 16,
+                                               (uint32_t)(min(row, R - 1 - q0) * HD + dchk[k]) * 2, 0, 0, 0);
+      // advance this row to the next tile
+      qhd[k] += dhq;
+      qoff[k] += qinc;
+      if (qhd[k] >= H) {
+        qhd[k] -= H;
+        qoff[k] += S - H * HD;
+      }
+    }
   };
   // per-row statistics of a query tile, loaded by threads 0..63 into registers
   float n_lse = 0.f, n_D = 0.f;
@@ -439,6 +471,9 @@ int attn_mfma_fwd(const void* qkv, int B, int T, int H, float scale, void* o, fl
 int attn_mfma_bwd(const void* qkv, const void* o, const void* dout, const float* lse, int B, int T, int H, float scale,
                   float* dqkv, void* ws, hipStream_t s) {
   NC_REQUIRE((uint64_t)T * H * H < ((uint64_t)1 << 32), NC_ERR_UNSUPPORTED, "attention: T * H^2 must be < 2^32");
+  // the dK/dV staging addresses a sequence's q/k/v rows with 32-bit byte offsets
+  NC_REQUIRE((int64_t)T * (H + 2) * HD * 2 < ((int64_t)1 << 31), NC_ERR_UNSUPPORTED,
+             "attention: a sequence of T rows of (H + 2) * 128 bf16 must be < 2 GiB");
   AttnMfmaArgs a{};
   a.qkv = static_cast<const bf16*>(qkv);
   a.o = static_cast<const bf16*>(o);

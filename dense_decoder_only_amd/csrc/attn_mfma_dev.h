@@ -44,6 +44,12 @@ __device__ __forceinline__ void dma_tile(bf16* S, int wave, int lane, RowPtr row
   }
 }
 
+// Buffer resource whose base is `base` (no range limit below 2^31 bytes):
+// the staging loops give per-lane 32-bit byte offsets from it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const bf16* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
 // MFMA operand: 8 consecutive columns (chunk c) of `row`.
 __device__ __forceinline__ bf16x8_t frag_row(const bf16* S, int row, int c) {
   return *reinterpret_cast<const bf16x8_t*>(S + toff(row, c));
