@@ -57,12 +57,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC_ATTN_DQ_
   const int tmin = r0 / H;
   const int tmax = min(T - 1, (min(r0 + QB, R) - 1) / H);
   const int ntiles = tmax / KT + 1;
+  // K/V rows are S apart: buffer resources at the sequence's K and V columns
+  // and 32-bit byte offsets (rows past the end read row T - 1)
+  const __amdgpu_buffer_rsrc_t krs = row_rsrc(base + H * HD), vrs = row_rsrc(base + (H + 1) * HD);
   auto stage = [&](int j, int buf) {
     const int kv0 = j * KT;
-    dma_tile(Ks + buf * TILE, w, lane,
-             [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + H * HD; });
-    dma_tile(Vs + buf * TILE, w, lane,
-             [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + (H + 1) * HD; });
+#pragma unroll
+    for (int k = 0; k < KT / 16; ++k) {
+      const int g = w * (KT / 16) + k;
+      const int row = g * 4 + (lane >> 4);
+      const uint32_t off = (uint32_t)(min(kv0 + row, T - 1) * (int)a.S + (((lane & 15) ^ tswz(row)) << 3)) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(Ks + buf * TILE + g * 4 * HD),
+                                               16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(Vs + buf * TILE + g * 4 * HD),
+                                               16, off, 0, 0, 0);
+    }
   };
   f32x16 dq[4];
 #pragma unroll

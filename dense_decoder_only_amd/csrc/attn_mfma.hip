@@ -79,10 +79,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tmin = r0 / H;
   const int tmax = min(T - 1, (min(r0 + QB, R) - 1) / H);
   const int ntiles = tmax / KT + 1;
+  // K/V rows are S apart: buffer resources at the sequence's K and V columns
+  // and 32-bit byte offsets (rows past the end read row T - 1)
+  const __amdgpu_buffer_rsrc_t krs = row_rsrc(base + H * HD), vrs = row_rsrc(base + (H + 1) * HD);
   auto stage = [&](int j, bf16* Kd, bf16* Vd) {
     const int kv0 = j * KT;
-    dma_tile(Kd, w, lane, [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + H * HD; });
-    dma_tile(Vd, w, lane, [&](int row) { return base + (int64_t)min(kv0 + row, T - 1) * a.S + (H + 1) * HD; });
+#pragma unroll
+    for (int k = 0; k < KT / 16; ++k) {
+      const int g = w * (KT / 16) + k;
+      const int row = g * 4 + (lane >> 4);
+      const uint32_t off = (uint32_t)(min(kv0 + row, T - 1) * (int)a.S + (((lane & 15) ^ tswz(row)) << 3)) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(Kd + g * 4 * HD), 16, off,
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(Vd + g * 4 * HD), 16, off,
+                                               0, 0, 0);
+    }
   };
 
   f32x16 o[4];
@@ -449,6 +460,9 @@ size_t attn_mfma_bwd_workspace_bytes(int B, int T, int H) {
 
 int attn_mfma_fwd(const void* qkv, int B, int T, int H, float scale, void* o, float* lse, hipStream_t s) {
   NC_REQUIRE((uint64_t)T * H * H < ((uint64_t)1 << 32), NC_ERR_UNSUPPORTED, "attention: T * H^2 must be < 2^32");
+  // the K/V staging addresses a sequence's rows with 32-bit byte offsets
+  NC_REQUIRE((int64_t)T * (H + 2) * HD * 2 < ((int64_t)1 << 31), NC_ERR_UNSUPPORTED,
+             "attention: a sequence of T rows of (H + 2) * 128 bf16 must be < 2 GiB");
   AttnMfmaArgs a{};
   a.qkv = static_cast<const bf16*>(qkv);
   a.o_out = static_cast<bf16*>(o);
