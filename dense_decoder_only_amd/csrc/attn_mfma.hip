@@ -110,11 +110,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (j + 1 < ntiles) stage(j + 1, Kn, Vn);
 
     f32x16 s[2];
+    s[0] = zero16();
+    s[1] = zero16();
+    {
+      // K fragments of step j = 8 st + ks read PF - 1 steps ahead (a ring);
+      // the two 32-key halves alternate so that back-to-back MFMAs are independent
+      constexpr int PF = NC_FWD_PF;
+      bf16x8_t fk[PF];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      s[st] = zero16();
+      for (int j = 0; j < PF - 1; ++j) fk[j] = frag_row(K, (j & 1) * 32 + lc, 2 * (j >> 1) + h);
+      __builtin_amdgcn_sched_group_barrier(0x100, PF - 1, 0);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s[st] = mfma(frag_row(K, st * 32 + lc, 2 * ks + h), qreg[ks], s[st]);
+      for (int j = 0; j < 16; ++j) {
+        if (j + PF - 1 < 16) {
+          const int jn = j + PF - 1;
+          fk[jn % PF] = frag_row(K, (jn & 1) * 32 + lc, 2 * (jn >> 1) + h);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        s[j & 1] = mfma(fk[j % PF], qreg[j >> 1], s[j & 1]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
     }
     float mt = -INFINITY;
     if (kv0 + KT - 1 > tmin) {  // the tile crosses some row's diagonal
@@ -164,14 +179,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     ls += __shfl_xor(ls, 32, 64);
     l_run += ls;
+    {
+      // O^T += V^T P^T, step j = 4 (2 st + jp) + ht, the V^T fragments read
+      // PF - 1 steps ahead (a ring)
+      constexpr int PF = NC_FWD_PF;
+      bf16x8_t fv[PF];
+      auto v_read = [&](int j) { fv[j % PF] = frag_tr(V, (j >> 3) * 32 + 16 * ((j >> 2) & 1), (j & 3) * 32, lane); };
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int j = 0; j < PF - 1; ++j) v_read(j);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 0);
+      bf16x8_t pb = {};
 #pragma unroll
-      for (int jp = 0; jp < 2; ++jp) {
-        const bf16x8_t pb = pack_p(s[st], jp);
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht) o[ht] = mfma(frag_tr(V, st * 32 + 16 * jp, ht * 32, lane), pb, o[ht]);
+      for (int j = 0; j < 16; ++j) {
+        if (j + PF - 1 < 16) {
+          v_read(j + PF - 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        if ((j & 3) == 0) pb = pack_p(s[j >> 3], (j >> 2) & 1);
+        o[j & 3] = mfma(fv[j % PF], pb, o[j & 3]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };

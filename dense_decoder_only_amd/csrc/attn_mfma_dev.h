@@ -15,6 +15,9 @@ constexpr int KT = 64;    // keys per tile
 constexpr int KB = 128;   // keys per dK/dV block (4 waves x 32)
 constexpr int QT = 64;    // query rows per dK/dV tile
 constexpr int QCH = 5120; // query rows per dK/dV split
+#ifndef NC_FWD_PF
+#define NC_FWD_PF 3       // forward: K fragments in the score read ring
+#endif
 #ifndef NC_DKV_PF
 #define NC_DKV_PF 4       // dK/dV: fragment pairs in the S / dP read ring
 #endif
