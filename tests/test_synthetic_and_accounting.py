@@ -1,5 +1,7 @@
 """Seeded inputs and FLOP/parameter accounting (CPU)."""
+import json
 import math
+import os
 
 import numpy as np
 
@@ -7,11 +9,21 @@ from dense_decoder_only_amd import accounting as acc
 from synthetic import CONFIGS, bf16_bits_to_f32, make_tokens, to_bf16_bits, zipf_ids
 
 
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _scale():
+    with open(os.path.join(GOLDEN, "d20_scale.json")) as f:
+        return json.load(f)
+
+
 def test_param_counts():
     d20 = CONFIGS["d20"]
     assert acc.total_params(d20) == 502_005_760
-    # with full K/V heads the d20 count is the pages' "about 560M"
-    assert acc.total_params(d20, kv_heads=d20.n_head) == 560_988_160
+    # with full K/V heads the d20 count is the page's approximate d20 size
+    full = acc.total_params(d20, kv_heads=d20.n_head)
+    assert full == 560_988_160
+    assert abs(full - _scale()["d20_params_approx"]) / _scale()["d20_params_approx"] < 0.005
     assert acc.total_params(CONFIGS["tiny"]) == 491_520
     assert acc.total_params(CONFIGS["d26"]) == 949_092_352
 
@@ -20,8 +32,12 @@ def test_flops_convention_matches_pages():
     d20 = CONFIGS["d20"]
     assert acc.matmul_params(d20) == 418_119_680
     assert acc.flops_per_token(d20) == 6 * 418_119_680 + 6 * 20 * 10 * 128 * 2048
-    # 6 N D with the pages' 560M params and 11.2B tokens is about 4e19 FLOPs
-    assert abs(6 * 560e6 * 11.2e9 - 4e19) / 4e19 < 0.07
+    # the page's token budget is 20 tokens per parameter, and 6 N D over it is
+    # its approximate total compute
+    g = _scale()
+    assert abs(g["d20_tokens"] - g["tokens_per_param"] * g["d20_params_approx"]) < 1e6
+    full = acc.total_params(d20, kv_heads=d20.n_head)
+    assert abs(6 * full * g["d20_tokens"] - g["d20_total_flops_approx"]) / g["d20_total_flops_approx"] < 0.07
 
 
 def test_zipf_marginals():
