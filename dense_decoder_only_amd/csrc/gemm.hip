@@ -99,33 +99,50 @@ __device__ __forceinline__ void xent_bwd4(const MfmaParams& p, float4 v, int row
       make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
 }
 
-// Forward cross-entropy epilogue: a 16-lane group holds one row's 64 columns
-// (4 per lane); every lane of the group must call this (it shuffles).  y is
-// the row's target column relative to xv0 (-1 for rows past M).
+// Sum over the 16 lanes of a DPP row (the lanes l with the same l / 16); every
+// lane of the row gets the total.  Rotations by 8 and 4 within the row, then
+// the two quad exchanges.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float s) {
+  s += dpp_f<0x128>(s);  // row_ror:8
+  s += dpp_f<0x124>(s);  // row_ror:4
+  s += dpp_f<0x4e>(s);   // quad_perm [2,3,0,1]
+  s += dpp_f<0xb1>(s);   // quad_perm [1,0,3,2]
+  return s;
+}
+
+// Forward cross-entropy epilogue: a 16-lane group (one DPP row) holds one
+// row's 64 columns (4 per lane); every lane of the group must call this.  y is
+// the row's target column relative to xv0 (-1 for rows past M).  With
+// th = tanh(z / c) = sign(z) (1 - t) / (1 + t), t = e^{-2|z|/c}, the capped
+// logit is c th, exp(c th - c) = 2^{(th - 1) c log2(e)}, and the stored code
+// is round(32767 th).
 __device__ __forceinline__ void xent_fwd4(const MfmaParams& p, float4 v, int row, int col, int gcol64, int y) {
   const bool ok = row < p.M;
+  const bool in = col < p.N;  // N is a multiple of 8: the 4 columns are all in range or none is
   const float zz[4] = {v.x, v.y, v.z, v.w};
+  const float ka = -2.f * kLog2e * p.xinv_c, cl = p.xc * kLog2e;
+  float th[4];
   float s = 0.f;
-  float zq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    if (col + e < p.N) {
-      const float zc = softcap_of(zz[e], p.xc, p.xinv_c);
-      s += __builtin_amdgcn_exp2f((zc - p.xc) * kLog2e);
-      if (ok && col + e == y) p.xztgt[row] = zc;
-      zq[e] = zc * p.xinv_c * 32767.f;
-    }
+    const float t = __builtin_amdgcn_exp2f(ka * fabsf(zz[e]));
+    th[e] = copysignf((1.f - t) * __builtin_amdgcn_rcpf(1.f + t), zz[e]);
+    s += __builtin_amdgcn_exp2f(fmaf(th[e], cl, -cl));
   }
-  if (p.C && ok && col < p.N) {  // N is a multiple of 8: the 4 columns are all in range
-    const int q0 = __float2int_rn(zq[0]), q1 = __float2int_rn(zq[1]);
-    const int q2 = __float2int_rn(zq[2]), q3 = __float2int_rn(zq[3]);
+  if (!in) s = 0.f;
+  const unsigned d = (unsigned)(y - col);
+  if (ok && in && d < 4u) p.xztgt[row] = p.xc * (d == 0 ? th[0] : d == 1 ? th[1] : d == 2 ? th[2] : th[3]);
+  if (p.C && ok && in) {
+    const int q0 = __float2int_rn(th[0] * 32767.f), q1 = __float2int_rn(th[1] * 32767.f);
+    const int q2 = __float2int_rn(th[2] * 32767.f), q3 = __float2int_rn(th[3] * 32767.f);
     *reinterpret_cast<uint2*>(static_cast<int16_t*>(p.C) + (int64_t)row * p.ldc + col) =
         make_uint2((uint32_t)(q0 & 0xffff) | ((uint32_t)q1 << 16), (uint32_t)(q2 & 0xffff) | ((uint32_t)q3 << 16));
   }
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);
-  s += __shfl_xor(s, 4, 64);
-  s += __shfl_xor(s, 8, 64);
+  s = row16_sum(s);
   if (ok && (threadIdx.x & 15) == 0 && gcol64 < p.N)
     p.xpart[(int64_t)((p.xv0 + gcol64) >> 6) * p.M + row] = s;
 }
