@@ -1466,12 +1466,43 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
   }
 }
 
+// 2-byte elements with R and C multiples of 8 and 16-byte aligned matrices:
+// every global access moves 8 elements (16 bytes).  Thread t handles the
+// 8-element pieces t and t + 256 of the tile: on the way in, piece id is
+// row id / 8 of the tile, columns 8 (id % 8) ..; on the way out, output row
+// id / 8 (a tile column), output columns 8 (id % 8) .. (eight tile rows).
+__global__ __launch_bounds__(256) void transpose_b16x8_kernel(const uint16_t* __restrict__ src, int64_t R, int64_t C,
+                                                              uint16_t* __restrict__ dst) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // rows 144 bytes apart
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int id = t + 256 * k, rr = id >> 3, ch = (id & 7) * 8;
+    if (r0 + rr < R && c0 + ch < C)  // C % 8 == 0: the piece is whole
+      *reinterpret_cast<uint4*>(&tile[rr][ch]) = *reinterpret_cast<const uint4*>(src + (r0 + rr) * C + c0 + ch);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int id = t + 256 * k, cc = id >> 3, ch = (id & 7) * 8;
+    if (c0 + cc < C && r0 + ch < R) {  // R % 8 == 0: the piece is whole
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[ch + 2 * e][cc] | ((uint32_t)tile[ch + 2 * e + 1][cc] << 16);
+      *reinterpret_cast<uint4*>(dst + (c0 + cc) * R + r0 + ch) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 }  // namespace
 
 int transpose(const void* src, int64_t R, int64_t C, int elem_bytes, void* dst, hipStream_t s) {
   NC_REQUIRE(src && dst && R > 0 && C > 0, NC_ERR_INVALID_ARG, "transpose: bad arguments");
   dim3 grid((unsigned)cdiv(C, 64), (unsigned)cdiv(R, 64));
-  if (elem_bytes == 2)
+  if (elem_bytes == 2 && R % 8 == 0 && C % 8 == 0 && aligned16(src) && aligned16(dst))
+    transpose_b16x8_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), R, C, static_cast<uint16_t*>(dst));
+  else if (elem_bytes == 2)
     transpose_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), R, C, static_cast<uint16_t*>(dst));
   else
     transpose_kernel<uint32_t><<<grid, 256, 0, s>>>(static_cast<const uint32_t*>(src), R, C, static_cast<uint32_t*>(dst));
