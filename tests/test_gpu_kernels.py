@@ -393,10 +393,11 @@ def test_relu2_mlp_fwd_bwd(dtype):
 # ------------------------------------------------- softcap cross entropy --
 
 # bf16 with d a multiple of 64 takes the fused epilogue path; d = 200 the
-# chunked fp32-logit path.
+# chunked fp32-logit path.  V = 1000 ends in a partial 64-column group and a
+# partial 64-row tile of the transposed U.
 @pytest.mark.parametrize("dtype,M,d,V,ustd", [(F32, 512, 256, 8192, 1.0), (BF16, 512, 256, 8192, 1.0),
                                               (BF16, 8192, 128, 40960, 1.0), (BF16, 264, 128, 1024, 20.0),
-                                              (BF16, 512, 200, 4096, 1.0)])
+                                              (BF16, 512, 200, 4096, 1.0), (BF16, 264, 128, 1000, 1.0)])
 def test_softcap_xent_fwd_bwd(dtype, M, d, V, ustd):
     n = nc()
     r = rng(M + V)
