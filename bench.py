@@ -291,7 +291,7 @@ def main():
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", a.gpus))
     if a.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for {a.gpus}).",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for {a.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
   NC_OK = 0,
   NC_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer      */
-  NC_ERR_UNSUPPORTED = 2, /* a shape or dtype this build does not implement  */
+  NC_ERR_UNSUPPORTED = 2, /* a shape or dtype the library does not implement */
   NC_ERR_WORKSPACE = 3,   /* ws too small for this call                      */
   NC_ERR_HIP = 4,         /* a HIP runtime call failed                       */
   NC_ERR_DEVICE_FLAG = 5  /* a kernel raised the device flag (bad token id)  */
