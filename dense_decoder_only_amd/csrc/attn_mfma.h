@@ -18,6 +18,7 @@ struct AttnMfmaArgs {
   int64_t S;           // qkv row stride in elements
   float scale, scale_log2;
   int nkb, smax;
+  int qch;             // query rows per dK/dV split (a multiple of 64)
   uint32_t hmagic;     // ceil(2^32 / H): r / H == umulhi(r, hmagic) for r < 2^32 / H^2
 };
 

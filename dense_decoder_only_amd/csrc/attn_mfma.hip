@@ -228,10 +228,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // -------------------------------------------------------------------- dK/dV --
 __device__ __forceinline__ int qbeg_of(int kb, int H) { return ((kb * KB * H) / QT) * QT; }
-__device__ __forceinline__ int nsplit_of(int kb, int H, int R) { return (R - qbeg_of(kb, H) + QCH - 1) / QCH; }
+__device__ __forceinline__ int nsplit_of(int kb, int H, int R, int qch) { return (R - qbeg_of(kb, H) + qch - 1) / qch; }
 
 // grid (B, nkb * SMAX): block (kb, s) handles key rows kb*128 .. +127 against
-// query rows [qbeg + s*QCH, min(R, qbeg + (s+1)*QCH)).  Writes partial dK^T,
+// query rows [qbeg + s*qch, min(R, qbeg + (s+1)*qch)).  Writes partial dK^T,
 // dV^T sums (unscaled) to part[(b * nkb + kb) * SMAX + s].
 // One wave per SIMD: K and V of the wave's 32 keys live in registers
 // (64 VGPRs) beside the dK/dV accumulators (128); forcing two waves per SIMD
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
   const int smax = a.smax;
   const int kb = blockIdx.y / smax, sp = blockIdx.y - (blockIdx.y / smax) * smax;
   const int b = blockIdx.x;
-  if (sp >= nsplit_of(kb, H, R)) return;
+  if (sp >= nsplit_of(kb, H, R, a.qch)) return;
   const bf16* base = a.qkv + (int64_t)b * T * a.S;
   const bf16* dbase = a.dout + (int64_t)b * R * HD;
   const int u0 = kb * KB;
@@ -266,8 +266,8 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
     }
   }
 
-  const int qs0 = qbeg_of(kb, H) + sp * QCH;
-  const int qs1 = min(R, qs0 + QCH);
+  const int qs0 = qbeg_of(kb, H) + sp * a.qch;
+  const int qs1 = min(R, qs0 + a.qch);
   const int nq = (qs1 - qs0 + QT - 1) / QT;
   // Staging of the query tiles, through buffer resources.  Row r = t H + h of
   // the folded query view sits at element t S + h HD of the sequence: not a
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
 __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(AttnMfmaArgs a) {
   const int H = a.H, T = a.T, R = T * H;
   const int kb = blockIdx.x, b = blockIdx.y;
-  const int ns = nsplit_of(kb, H, R);
+  const int ns = nsplit_of(kb, H, R, a.qch);
   const float* p0 = a.part + (((int64_t)b * a.nkb + kb) * a.smax * 2) * (KB * HD);
   for (int e = threadIdx.x * 4; e < KB * HD; e += 256 * 4) {
     const int key = e / HD, hd = e - key * HD;
@@ -477,12 +477,29 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(AttnMfmaArgs a) {
 
 }  // namespace
 
-int attn_mfma_smax(int T, int H) { return (T * H + QCH - 1) / QCH; }
+// Query rows per dK/dV split.  Splitting adds partial sums to write and
+// reduce and re-stages K and V, so a key block keeps its whole query range
+// when the B x nkb key blocks alone make DKV_BLOCKS; otherwise the range is
+// split so that the longest one (key block 0) gives about that many, and never
+// below QCH_MIN rows.
+int attn_mfma_qch(int B, int T, int H) {
+  const int R = T * H, nkb = (T + KB - 1) / KB;
+  const int64_t blocks = (int64_t)B * nkb;
+  const int64_t splits = blocks >= DKV_BLOCKS ? 1 : (DKV_BLOCKS + blocks - 1) / blocks;
+  int64_t qch = (R + splits - 1) / splits;
+  qch = (qch + QT - 1) / QT * QT;
+  return (int)std::max<int64_t>(qch, QCH_MIN);
+}
+
+int attn_mfma_smax(int B, int T, int H) {
+  const int q = attn_mfma_qch(B, T, H);
+  return (T * H + q - 1) / q;
+}
 
 size_t attn_mfma_bwd_workspace_bytes(int B, int T, int H) {
   const int nkb = (T + KB - 1) / KB;
   const size_t dbuf = align_up((size_t)B * T * H * sizeof(float), 256);
-  const size_t part = (size_t)B * nkb * attn_mfma_smax(T, H) * 2 * KB * HD * sizeof(float);
+  const size_t part = (size_t)B * nkb * attn_mfma_smax(B, T, H) * 2 * KB * HD * sizeof(float);
   return dbuf + align_up(part, 256);
 }
 
@@ -531,7 +548,8 @@ int attn_mfma_bwd(const void* qkv, const void* o, const void* dout, const float*
   a.Dbuf = static_cast<float*>(ws);
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)B * T * H * sizeof(float), 256));
   a.nkb = (T + KB - 1) / KB;
-  a.smax = attn_mfma_smax(T, H);
+  a.qch = attn_mfma_qch(B, T, H);
+  a.smax = attn_mfma_smax(B, T, H);
   a.hmagic = (uint32_t)((((uint64_t)1 << 32) + H - 1) / H);
   const double fl = 2.0 * B * H * (double)HD * T * T;
   NC_TRY(attn_mfma_dq(a, s));
