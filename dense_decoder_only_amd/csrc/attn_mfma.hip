@@ -480,15 +480,11 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(AttnMfmaArgs a) {
 // Query rows per dK/dV split.  Splitting adds partial sums to write and
 // reduce and re-stages K and V, so a key block keeps its whole query range
 // when the B x nkb key blocks alone make DKV_BLOCKS; otherwise the range is
-// split so that the longest one (key block 0) gives about that many, and never
-// below QCH_MIN rows.
+// cut into chunks of QCH_MIN rows.
 int attn_mfma_qch(int B, int T, int H) {
   const int R = T * H, nkb = (T + KB - 1) / KB;
-  const int64_t blocks = (int64_t)B * nkb;
-  const int64_t splits = blocks >= DKV_BLOCKS ? 1 : (DKV_BLOCKS + blocks - 1) / blocks;
-  int64_t qch = (R + splits - 1) / splits;
-  qch = (qch + QT - 1) / QT * QT;
-  return (int)std::max<int64_t>(qch, QCH_MIN);
+  if ((int64_t)B * nkb < DKV_BLOCKS) return QCH_MIN;
+  return std::max((R + QT - 1) / QT * QT, QCH_MIN);
 }
 
 int attn_mfma_smax(int B, int T, int H) {

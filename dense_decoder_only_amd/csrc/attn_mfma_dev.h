@@ -14,7 +14,7 @@ constexpr int QB = 128;   // query rows per forward / dQ block (4 waves x 32)
 constexpr int KT = 64;    // keys per tile
 constexpr int KB = 128;   // keys per dK/dV block (4 waves x 32)
 constexpr int QT = 64;    // query rows per dK/dV tile
-constexpr int QCH_MIN = 5120;   // fewest query rows per dK/dV split
+constexpr int QCH_MIN = 5120;   // query rows per dK/dV split when the key blocks alone are too few
 constexpr int DKV_BLOCKS = 512; // dK/dV blocks aimed at: two rounds of one block per CU
 #ifndef NC_FWD_PF
 #define NC_FWD_PF 3       // forward: K fragments in the score read ring
