@@ -32,9 +32,11 @@ size_t xent_workspace_bytes(int64_t M, int d, int V);
 // fused path covers the vocabulary in one chunk; xent_bwd with from_stored
 // then forms dz from them instead of recomputing the logit product (same ws,
 // untouched in between).  Returns whether they were stored via *stored.
+// Targets outside [0, V) set *flag to 1 (flag = nullptr: the first int32 of
+// ws, cleared first); such rows have no target logit and count no bytes.
 int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* token_bytes, int64_t M, int d,
              int V, float softcap, float* lse, float* loss_tok, float* loss, float* bpb, void* ws, size_t ws_bytes,
-             hipStream_t s, bool store_logits = false, bool* stored = nullptr);
+             hipStream_t s, bool store_logits = false, bool* stored = nullptr, int32_t* flag = nullptr);
 int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* lse, int64_t M, int d, int V,
              float softcap, float dloss, float* dh, int dh_acc, float* dU, int dU_acc, void* ws, size_t ws_bytes,
              hipStream_t s, bool from_stored = false);

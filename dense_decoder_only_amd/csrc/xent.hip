@@ -52,6 +52,7 @@ int fused_cols(int64_t M, int V) {
 bool use_fused(int dtype, int d) { return dtype == NC_BF16 && d % 64 == 0; }
 
 struct XentWs {
+  int32_t* flag;   // device flag of the public entry points (first int32 of ws)
   float* zbuf;     // [M, Vc] fp32 logit chunk (chunked path)
   void* dz;        // [M, Vc] dtype (backward)
   float* partial;  // [nparts, M]
@@ -71,6 +72,7 @@ size_t carve(int64_t M, int d, int V, bool fused, XentWs* w, void* base) {
     off += align_up(bytes, 256);
     return o;
   };
+  const size_t o_f = take(4);
   const size_t o_z = take(fused ? 0 : (size_t)M * Vc * 4);
   const size_t o_dz = take((size_t)M * Vc * (fused ? 2 : 4));
   const size_t o_p = take((size_t)nparts * M * 4);
@@ -81,6 +83,7 @@ size_t carve(int64_t M, int d, int V, bool fused, XentWs* w, void* base) {
   const size_t o_ut = take((size_t)V * d * 2);
   if (w) {
     char* b = static_cast<char*>(base);
+    w->flag = reinterpret_cast<int32_t*>(b + o_f);
     w->zbuf = reinterpret_cast<float*>(b + o_z);
     w->dz = b + o_dz;
     w->partial = reinterpret_cast<float*>(b + o_p);
@@ -91,6 +94,17 @@ size_t carve(int64_t M, int d, int V, bool fused, XentWs* w, void* base) {
     w->ut = b + o_ut;
   }
   return off;
+}
+
+// Before the logit product: z' at the target starts at 0 for every row, so a
+// row whose target lies outside [0, V) (which no column matches) reads a
+// defined value; such rows raise the device flag.
+__global__ void xent_prep_kernel(const int32_t* __restrict__ tgt, int64_t M, int V, float* __restrict__ ztgt,
+                                 int32_t* __restrict__ flag) {
+  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < M; r += (int64_t)gridDim.x * blockDim.x) {
+    ztgt[r] = 0.f;
+    if ((uint32_t)tgt[r] >= (uint32_t)V) *flag = 1;
+  }
 }
 
 // One wavefront per row of the chunk: partial sum of exp(z' - c) and, when
@@ -133,7 +147,7 @@ __global__ void xent_finish_kernel(const float* __restrict__ partial, int nch, i
 
 // Single block: fixed-order sums of the per-token losses and target bytes.
 __global__ __launch_bounds__(1024) void xent_reduce_kernel(const float* __restrict__ ltok, int64_t M,
-                                                           const int32_t* __restrict__ tgt,
+                                                           const int32_t* __restrict__ tgt, int V,
                                                            const float* __restrict__ token_bytes,
                                                            float default_bytes, float* loss, float* bpb) {
   __shared__ double sl[1024];
@@ -141,7 +155,9 @@ __global__ __launch_bounds__(1024) void xent_reduce_kernel(const float* __restri
   double a = 0.0, b = 0.0;
   for (int64_t i = threadIdx.x; i < M; i += 1024) {
     a += (double)ltok[i];
-    b += token_bytes ? (double)token_bytes[tgt[i]] : (double)default_bytes;
+    // a target outside [0, V) (flagged by xent_prep_kernel) counts no bytes
+    const uint32_t y = (uint32_t)tgt[i];
+    b += token_bytes ? (y < (uint32_t)V ? (double)token_bytes[y] : 0.0) : (double)default_bytes;
   }
   sl[threadIdx.x] = a;
   sb[threadIdx.x] = b;
@@ -251,7 +267,7 @@ size_t xent_workspace_bytes(int64_t M, int d, int V) {
 
 int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* token_bytes, int64_t M, int d,
              int V, float softcap, float* lse, float* loss_tok, float* loss, float* bpb, void* ws, size_t ws_bytes,
-             hipStream_t s, bool store_logits, bool* stored) {
+             hipStream_t s, bool store_logits, bool* stored, int32_t* flag) {
   if (stored) *stored = false;
   NC_TRY(validate(h, U, dtype, tgt, M, d, V));
   NC_REQUIRE(lse && loss && bpb, NC_ERR_INVALID_ARG, "softcap_xent_fwd: null output");
@@ -264,6 +280,12 @@ int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
   const int Vc = fused ? fused_cols(M, V) : chunk_cols(M, V);
   const int nch = (int)cdiv(V, Vc);
   const size_t esz = dtype == NC_BF16 ? 2 : 4;
+  if (!flag) {  // public entry point: the flag lives in ws and starts clear
+    flag = w.flag;
+    NC_TRY(fill_zero(flag, 4, s));
+  }
+  xent_prep_kernel<<<(unsigned)std::min<int64_t>(cdiv(M, 256), 1024), 256, 0, s>>>(tgt, M, V, w.ztgt, flag);
+  NC_TRY(check_launch("xent_prep_kernel"));
   for (int k = 0; k < nch; ++k) {
     const int v0 = k * Vc;
     const int n = std::min(Vc, V - v0);
@@ -305,7 +327,7 @@ int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
   xent_finish_kernel<<<(unsigned)std::min<int64_t>(cdiv(M, 256), 4096), 256, 0, s>>>(w.partial, nparts, M, softcap,
                                                                                        w.ztgt, lse, w.ltok, loss_tok);
   NC_TRY(check_launch("xent_finish_kernel"));
-  xent_reduce_kernel<<<1, 1024, 0, s>>>(w.ltok, M, tgt, token_bytes, 4.8f, loss, bpb);
+  xent_reduce_kernel<<<1, 1024, 0, s>>>(w.ltok, M, tgt, V, token_bytes, 4.8f, loss, bpb);
   return check_launch("xent_reduce_kernel");
 }
 

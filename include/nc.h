@@ -372,7 +372,11 @@ int nc_relu2_mlp_bwd(const void* g_lp, const void* m, const void* u, const void*
  *   loss_tok [M] fp32 (may be NULL): lse - z'[t, tgt[t]].
  *   loss, bpb: fp32 device scalars (mean loss; sum / (ln 2 * sum bytes)).
  *   token_bytes [V] fp32 or NULL (4.8 per id).
- *   ws: nc_softcap_xent_workspace_bytes(M, d, V) bytes. */
+ *   ws: nc_softcap_xent_workspace_bytes(M, d, V) bytes, 256-byte aligned.
+ *   Its first int32 is a device flag: nc_softcap_xent_fwd clears it and sets
+ *   it to 1 when a target lies outside [0, V) (nc_sync_status(ws) reads it).
+ *   Such a row takes z'[t, tgt[t]] = 0 and counts no bytes; no memory outside
+ *   the buffers is read.  In the backward such a row has no one-hot term. */
 size_t nc_softcap_xent_workspace_bytes(int64_t M, int d, int V);
 int nc_softcap_xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt,
                         const float* token_bytes, int64_t M, int d, int V, float softcap,
