@@ -8,7 +8,8 @@ every layer forward and backward, softcap cross entropy, all parameter
 gradients) over one batch; inputs and weights are resident in HBM before the
 timed region.  Besides the throughput it reports
   * roofline: the dominant kernel's achieved TFLOP/s against the bf16 matrix
-    peak, timed live with HIP events on the stream it runs on;
+    peak, timed live with HIP events on the stream it runs on, over separate
+    steps after the timed region (the headline steps run without the events);
   * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
     sample of the same workload;
   * optimizer: the AdamW update over every parameter (HBM roofline) and the
@@ -116,16 +117,33 @@ def roofline(name, ms, launches, flops, workload):
     }
 
 
+def host_cpu_and_blas():
+    """(CPU model name, numpy's BLAS library and version, BLAS threads)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = "unknown", os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '?')}"
+            threads = max(i.get("num_threads", 1) for i in info)
+    except Exception:
+        pass
+    return model, blas, int(threads)
+
+
 def cpu_baseline(cfg, inp, budget_tokens=None):
     """The fp64 oracle, untouched, on a bounded sample: forward+backward of the
     first `n` tokens of sequence 0 with the full model."""
     import oracle
-    from dense_decoder_only_amd import accounting
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    cpu, blas, cores = host_cpu_and_blas()
     n = budget_tokens or cfg.seq_len
     p = oracle.to_f64_params(inp["weights"])
     ids = inp["ids"][:1, :n]
@@ -139,7 +157,10 @@ def cpu_baseline(cfg, inp, budget_tokens=None):
         "cores": int(cores),
         "kind": "oracle",
         "sample": f"fp64 numpy oracle, forward+backward of the first {n} tokens of one sequence, "
-                  f"full {cfg.name} model ({cfg.n_layer} layers, vocab {cfg.vocab}); {dt:.1f} s",
+                  f"full {cfg.name} model ({cfg.n_layer} layers, vocab {cfg.vocab}); {dt:.1f} s "
+                  f"on {cpu}, BLAS {blas} with {cores} threads",
+        "cpu": cpu,
+        "blas": blas,
     }
 
 
@@ -228,8 +249,8 @@ def decode_leg(cfg, torch, nc, params, s, steps=64, max_len=2048):
     ids = [toks[:, T0 + j].contiguous() for j in range(steps)]
 
     def run(family=None):
-        if family is not None:
-            nc.nc_probe_start(getattr(nc, family), 512 * steps)
+        if family is not None:  # room for every launch of the decode steps (5 per layer at most)
+            nc.nc_probe_start(getattr(nc, family), (5 * L + 8) * steps)
         e0.record(s)
         for j in range(steps):
             nc.nc_decode_step(ccfg, params, ids[j], pos[j], kv, max_len, logits, ws, stream=s)
@@ -284,6 +305,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None)
     ap.add_argument("--roofline-kernel", default=DOMINANT, choices=sorted(FAMILIES))
+    ap.add_argument("--roofline-steps", type=int, default=5,
+                    help="steps run after the timed region with the kernel timer armed (0: none)")
     ap.add_argument("--no-decode", action="store_true", help="skip the prefill / decode timings")
     ap.add_argument("--no-optimizer", action="store_true", help="skip the AdamW and full-iteration timings")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -316,8 +339,7 @@ def main():
     if nc.nc_sync_status(ws) != nc.NC_OK:
         raise RuntimeError("device flag raised during warmup")
     torch.cuda.synchronize()
-    fam = FAMILIES[a.roofline_kernel]
-    nc.nc_probe_start(getattr(nc, fam[0]), 512 * a.steps)
+    # headline: the timed steps run with the kernel timer disarmed
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(s)
@@ -327,7 +349,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_s = e0.elapsed_time(e1) / 1e3
+    # roofline of the dominant kernel: separate steps with the kernel timer armed
+    fam = FAMILIES[a.roofline_kernel]
+    rsteps = max(a.roofline_steps, 1)
+    nc.nc_probe_start(getattr(nc, fam[0]), 512 * rsteps)
+    for _ in range(rsteps):
+        step()
+    torch.cuda.synchronize()
     roof = roofline(a.roofline_kernel, *nc.nc_probe_stop(), cfg.name)
+    roof["steps"] = rsteps
     elapsed = max(wall, gpu_s)
     tokens = cfg.tokens * a.steps
     value = tokens / elapsed
@@ -377,7 +407,8 @@ def main():
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
-        "roofline_kernel": {k: roof[k] for k in ("kernel", "launches", "avg_launch_us", "flops_per_launch")},
+        "roofline_kernel": {k: roof[k] for k in ("kernel", "launches", "avg_launch_us", "flops_per_launch",
+                                                  "steps")},
         "cpu_baseline": base,
         "optimizer": opt,
         "decode": dec,
