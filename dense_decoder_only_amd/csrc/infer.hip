@@ -22,6 +22,7 @@
 #include "ops.h"
 
 #include <cmath>
+#include <mutex>
 
 namespace nc {
 namespace {
@@ -726,6 +727,36 @@ extern "C" int nc_decode_step(const nc_config* cfg, const nc_params* params, con
                          static_cast<hipStream_t>(stream));
 }
 
+// Scratch of nc_mqa_decode_attn_noalloc: the chunk partials (fp32 outputs,
+// then (max, sum) pairs) of one decode-attention call, in the layout of the
+// workspace nc_mqa_decode_attn takes.  Every GPU the library runs on holds its
+// own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, never device memory: the device address is looked up once per
+// device with hipGetSymbolAddress and only that address reaches a kernel.
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64] = {};  // per device: the address of that device's `scratch`
+
+// The current device's scratch address (looked up on its first use there).
+int decode_scratch(void** out) {
+  int dev = 0;
+  NC_CHECK_HIP(hipGetDevice(&dev));
+  NC_REQUIRE(dev >= 0 && dev < 64, NC_ERR_UNSUPPORTED, "decode_attn_noalloc: device index %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    NC_CHECK_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    NC_REQUIRE(p != nullptr, NC_ERR_HIP, "decode_attn_noalloc: no device address for the scratch array");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return NC_OK;
+}
+}  // namespace
+
 extern "C" size_t nc_mqa_decode_workspace_bytes(int B, int H, int max_len) {
   return nc::mqa_decode_workspace_bytes(B, H, max_len);
 }
@@ -737,6 +768,23 @@ extern "C" int nc_mqa_decode_attn(const void* q, const void* k_cache, const void
   NC_REQUIRE(ws && need > 0, NC_ERR_INVALID_ARG, "decode_attn: null workspace or bad shape");
   NC_REQUIRE(ws_bytes >= need, NC_ERR_WORKSPACE, "decode_attn: workspace too small (%zu < %zu)", ws_bytes, need);
   NC_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255u) == 0, NC_ERR_INVALID_ARG, "decode_attn: ws must be 256-byte aligned");
+  const size_t parts = (size_t)B * nc::cdiv(max_len, 64) * H;
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + nc::align_up(parts * 128 * 4, 256));
+  return nc::mqa_decode_attn(q, k_cache, v_cache, lens, 0, B, H, hd, max_len, scale, o, part_o, part_ml,
+                             static_cast<hipStream_t>(stream));
+}
+
+extern "C" int nc_mqa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* lens, int B, int H, int hd, int max_len, float scale,
+                                          void* o, void* stream) {
+  const size_t need = nc::mqa_decode_workspace_bytes(B, H, max_len);
+  NC_REQUIRE(need > 0, NC_ERR_INVALID_ARG, "decode_attn_noalloc: bad shape");
+  NC_REQUIRE(need <= kDecodeScratchBytes, NC_ERR_WORKSPACE,
+             "decode_attn_noalloc: B=%d, H=%d, max_len=%d needs %zu bytes of scratch, more than its %zu", B, H,
+             max_len, need, kDecodeScratchBytes);
+  void* ws = nullptr;
+  NC_TRY(decode_scratch(&ws));
   const size_t parts = (size_t)B * nc::cdiv(max_len, 64) * H;
   float* part_o = static_cast<float*>(ws);
   float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + nc::align_up(parts * 128 * 4, 256));

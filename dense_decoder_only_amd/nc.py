@@ -84,6 +84,7 @@ _SIGS = {
                                c_sz, c_p]),
     "nc_mqa_decode_workspace_bytes": (c_sz, [c_int, c_int, c_int]),
     "nc_mqa_decode_attn": (c_int, [c_p, c_p, c_p, c_p, c_int, c_int, c_int, c_int, c_f, c_p, c_p, c_sz, c_p]),
+    "nc_mqa_decode_attn_noalloc": (c_int, [c_p, c_p, c_p, c_p, c_int, c_int, c_int, c_int, c_f, c_p, c_p]),
     "nc_softcap_xent_workspace_bytes": (c_sz, [c_i64, c_int, c_int]),
     "nc_softcap_xent_fwd": (c_int, [c_p, c_p, c_int, c_p, c_p, c_i64, c_int, c_int, c_f, c_p, c_p, c_p, c_p, c_p,
                                     c_sz, c_p]),
@@ -330,3 +331,8 @@ def nc_mqa_decode_workspace_bytes(B: int, H: int, max_len: int) -> int:
 def nc_mqa_decode_attn(q, k_cache, v_cache, lens, B, H, hd, max_len, scale, o, ws, stream=None) -> None:
     _check(load().nc_mqa_decode_attn(_p(q), _p(k_cache), _p(v_cache), _p(lens), B, H, hd, max_len, scale, _p(o),
                                      _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def nc_mqa_decode_attn_noalloc(q, k_cache, v_cache, lens, B, H, hd, max_len, scale, o, stream=None) -> None:
+    _check(load().nc_mqa_decode_attn_noalloc(_p(q), _p(k_cache), _p(v_cache), _p(lens), B, H, hd, max_len, scale,
+                                             _p(o), _stream(stream)))

@@ -232,6 +232,25 @@ int nc_mqa_decode_attn(const void* q, const void* k_cache, const void* v_cache, 
                        int H, int hd, int max_len, float scale, void* o, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* nc_mqa_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc.  Same arguments (minus ws), same kernels,
+ * same results.  The chunk partials go to a scratch array of 16 MiB that the
+ * library holds in device memory of every GPU it runs on until the process
+ * ends; the call allocates nothing.
+ *   Limit: nc_mqa_decode_workspace_bytes(B, H, max_len) <= 16 MiB (e.g. 32
+ *   sequences x 10 heads x 2048 positions needs 5.3 MB); larger shapes return
+ *   NC_ERR_WORKSPACE.  Nothing in the scratch needs clearing between calls.
+ *   All calls on one GPU share its scratch: calls that overlap in time on
+ *   that GPU (different streams, or threads) race and must be serialized by
+ *   the caller; calls on one stream are ordered by it.
+ *   The first call on each device looks up the scratch's device address
+ *   (hipGetSymbolAddress); make it outside graph capture.
+ * Errors: as nc_mqa_decode_attn, with NC_ERR_WORKSPACE for shapes beyond the
+ * limit. */
+int nc_mqa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* lens,
+                               int B, int H, int hd, int max_len, float scale, void* o, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Token-embedding gather and the norm that follows it [NEWS: untied
  * embedding; a norm after the token embedding; RMSNorm without parameters].
