@@ -233,18 +233,40 @@ __device__ __forceinline__ int nsplit_of(int kb, int H, int R, int qch) { return
 // grid (B, nkb * SMAX): block (kb, s) handles key rows kb*128 .. +127 against
 // query rows [qbeg + s*qch, min(R, qbeg + (s+1)*qch)).  Writes partial dK^T,
 // dV^T sums (unscaled) to part[(b * nkb + kb) * SMAX + s].
-// One wave per SIMD: K and V of the wave's 32 keys live in registers
-// (64 VGPRs) beside the dK/dV accumulators (128); forcing two waves per SIMD
-// spills them (measured slower).
-__global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
+//
+// Two roles per 32 keys, one wave each, the pair sharing a SIMD (waves w and
+// w + 4 of a block run on SIMD w):
+//   role P (waves 0-3): S = Q K^T, P = exp(S scale - lse) with the causal
+//     mask, P handed to the partner through LDS in fp32, dV^T += dO^T P;
+//   role G (waves 4-7): dP = dO V^T, then dS = P (dP - D) with the
+//     partner's P, dK^T += Q^T dS.
+// A query tile runs in two halves separated by a block barrier:
+//   [P: S products, softmax, P to LDS | G: dP products]
+//   [P: dV products                   | G: P from LDS, dS, dK products].
+// Each wave holds one key-side operand (K or V of its 32 keys, 32 VGPRs) and
+// one accumulator set (64), so two waves fit per SIMD, and the softmax VALU
+// work of one overlaps the other's matrix-core products.
+__device__ __forceinline__ void lds_barrier() {
+  // this wave's LDS writes have landed; outstanding DMA (vmcnt) is not waited for
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_dkv_kernel(AttnMfmaArgs a) {
   // one LDS object per stage; see the note on static stages above
   __shared__ __attribute__((aligned(16))) bf16 Qs0[QTILE];
   __shared__ __attribute__((aligned(16))) bf16 Qs1[QTILE];
   __shared__ __attribute__((aligned(16))) bf16 Ds0[QTILE];
   __shared__ __attribute__((aligned(16))) bf16 Ds1[QTILE];
-  __shared__ float lse_s[2][QT], D_s[2][QT];
-  __shared__ int tpos_s[2][QT];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
+  // P of the current tile: [key wave][8 float4 of a lane][64 lanes]
+  __shared__ __attribute__((aligned(16))) float4 Pex[4 * 8 * 64];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][QT];
+  __shared__ __attribute__((aligned(16))) float D_s[2][QT];
+  __shared__ __attribute__((aligned(16))) int tpos_s[2][QT];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, h = lane >> 5, lc = lane & 31;
+  const bool role_p = wv < 4;  // wave-uniform
+  const int w = wv & 3;
   const int H = a.H, T = a.T;
   const int R = T * H;
   const int smax = a.smax;
@@ -256,33 +278,33 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
   const int u0 = kb * KB;
   const int myu = u0 + w * 32 + lc;  // this lane's key position (column)
   const int uu = min(myu, T - 1);
-  bf16x8_t kreg[8], vreg[8];
+  // role P: the lane's key row; role G: its value row
+  bf16x8_t kv[8];
   {
-    const bf16* kp = base + (int64_t)uu * a.S + H * HD + 8 * h;
+    const bf16* kp = base + (int64_t)uu * a.S + (role_p ? H : H + 1) * HD + 8 * h;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      kreg[ks] = *reinterpret_cast<const bf16x8_t*>(kp + ks * 16);
-      vreg[ks] = *reinterpret_cast<const bf16x8_t*>(kp + HD + ks * 16);
-    }
+    for (int ks = 0; ks < 8; ++ks) kv[ks] = *reinterpret_cast<const bf16x8_t*>(kp + ks * 16);
   }
 
   const int qs0 = qbeg_of(kb, H) + sp * a.qch;
   const int qs1 = min(R, qs0 + a.qch);
   const int nq = (qs1 - qs0 + QT - 1) / QT;
-  // Staging of the query tiles, through buffer resources.  Row r = t H + h of
-  // the folded query view sits at element t S + h HD of the sequence: not a
-  // fixed stride apart, so each lane keeps, for each of its DMA rows, that
-  // row's offset and head and advances both by one tile (QT rows: QT / H
-  // positions and QT % H heads, with a carry) per staged tile, in place of a
-  // division by H per row.  Rows past the end (offsets at or past T S) read
-  // row R - 1.  dO rows are HD apart.
+  // Staging of the query tiles, through buffer resources, NST instructions
+  // (4 rows each) per wave and operand.  Row r = t H + h of the folded query
+  // view sits at element t S + h HD of the sequence: not a fixed stride
+  // apart, so each lane keeps, for each of its DMA rows, that row's offset
+  // and head and advances both by one tile (QT rows: QT / H positions and
+  // QT % H heads, with a carry) per staged tile, in place of a division by H
+  // per row.  Rows past the end (offsets at or past T S) read row R - 1.  dO
+  // rows are HD apart.
+  constexpr int NST = QT / 32;
   const int S = (int)a.S;
   const int dtq = QT / H, dhq = QT - dtq * H;
   const int qinc = dtq * S + dhq * HD, qend = T * S, qlast = (T - 1) * S + (H - 1) * HD;
-  int qoff[QT / 16], qhd[QT / 16], dchk[QT / 16];
+  int qoff[NST], qhd[NST], dchk[NST];
 #pragma unroll
-  for (int k = 0; k < QT / 16; ++k) {
-    const int row = (w * (QT / 16) + k) * 4 + (lane >> 4);
+  for (int k = 0; k < NST; ++k) {
+    const int row = (wv * NST + k) * 4 + (lane >> 4);
     const int c8 = ((lane & 15) ^ tswz(row)) << 3;
     const int r = qs0 + row, t = div_h(r, a.hmagic);
     qhd[k] = r - t * H;
@@ -294,8 +316,8 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
     const int q0 = qs0 + i * QT;
     const __amdgpu_buffer_rsrc_t drs = row_rsrc(dbase + (int64_t)q0 * HD);
 #pragma unroll
-    for (int k = 0; k < QT / 16; ++k) {
-      const int g = w * (QT / 16) + k;
+    for (int k = 0; k < NST; ++k) {
+      const int g = wv * NST + k;
       const int row = g * 4 + (lane >> 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (__attribute__((address_space(3))) void*)(Qd + g * 4 * HD), 16,
                                                (uint32_t)(qoff[k] < qend ? qoff[k] : qlast + dchk[k]) * 2, 0, 0, 0);
@@ -336,18 +358,63 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
       tpos_s[buf][tid] = n_t;
     }
   };
-  f32x16 dk[4], dv[4];
+  f32x16 acc[4];  // role P: dV^T, role G: dK^T (rows hd, column = this lane's key)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    dk[i] = zero16();
-    dv[i] = zero16();
-  }
+  for (int i = 0; i < 4; ++i) acc[i] = zero16();
 
   stage(0, Qs0, Ds0);
   fetch_stats(0);
   put_stats(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  constexpr int NQT = QT / 32;
+  // x[qt] (+)= X K^T (role P, X = Q) or X V^T (role G, X = dO): rows are the
+  // tile's queries, the column is this lane's key.  The X fragments of step
+  // j = 8 qt + ks are read PF - 1 steps ahead of their products (a ring).
+  uint32_t rof[8], tof[8];
+  frag_offsets(lane, rof, tof);
+  auto key_products = [&](const bf16* X, f32x16 (&x)[NQT]) {
+    constexpr int NSTEP = NQT * 8, PF = NC_DKV_PF;
+    bf16x8_t fx[PF];
+#pragma unroll
+    for (int j = 0; j < PF - 1; ++j) fx[j] = frag_at(X + (j >> 3) * 32 * HD, rof[j & 7]);
+    __builtin_amdgcn_sched_group_barrier(0x100, PF - 1, 0);
+#pragma unroll
+    for (int j = 0; j < NSTEP; ++j) {
+      if (j + PF - 1 < NSTEP) {
+        const int jn = j + PF - 1;
+        fx[jn % PF] = frag_at(X + (jn >> 3) * 32 * HD, rof[jn & 7]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      x[j >> 3] = mfma(fx[j % PF], kv[j & 7], x[j >> 3]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  };
+  // acc^T += Y^T x: A = Y^T read transposed from the tile, B = x in bf16.
+  // Step j = 8 qt + 4 jp + ht; its A fragment is read PF - 1 steps ahead (a
+  // ring), which also bounds how many reads the compiler hoists.
+  auto hd_products = [&](const bf16* Y, const f32x16 (&x)[NQT]) {
+    constexpr int NSTEP = NQT * 8, PF = NC_DKV_PF;
+    bf16x8_t fy[PF];
+    auto y_read = [&](int j) {
+      const bf16* Yr = Y + ((j >> 3) * 32 + 16 * ((j >> 2) & 1)) * HD;
+      fy[j % PF] = frag_tr_at(Yr, tof[2 * (j & 3)], tof[2 * (j & 3) + 1]);
+    };
+#pragma unroll
+    for (int j = 0; j < PF - 1; ++j) y_read(j);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 0);
+    bf16x8_t xb = {};
+#pragma unroll
+    for (int j = 0; j < NSTEP; ++j) {
+      if (j + PF - 1 < NSTEP) {
+        y_read(j + PF - 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      if ((j & 3) == 0) xb = pack_p(x[j >> 3], (j >> 2) & 1);
+      acc[j & 3] = mfma(fy[j % PF], xb, acc[j & 3]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  };
   // query tile i in (Q, G) with statistics in slot cur; tile i + 1 is DMA'd
   // into (Qn, Gn)
   auto q_tile = [&](const int i, const int cur, const bf16* Q, const bf16* G, bf16* Qn, bf16* Gn) {
@@ -355,77 +422,75 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
       stage(i + 1, Qn, Gn);
       fetch_stats(i + 1);
     }
-
-    // S = Q K^T and dP = dO V^T: rows q (one 32-row tile), column = key.
-    constexpr int NQT = QT / 32;
-    f32x16 s[NQT], dp[NQT];
+    f32x16 x[NQT];
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-      s[qt] = zero16();
-      dp[qt] = zero16();
-    }
-    {
-      // The Q and dO fragments of step j = 8 qt + ks are read PF - 1 steps
-      // ahead of their MFMAs (a ring of PF fragment pairs): with one wave per
-      // SIMD nothing else would cover the LDS latency.
-      constexpr int NSTEP = NQT * 8, PF = NC_DKV_PF;
-      bf16x8_t fq[PF], fd[PF];
+    for (int qt = 0; qt < NQT; ++qt) x[qt] = zero16();
+    // The lane offsets pass through an empty asm once per tile, so that the
+    // compiler does not hoist a register per (array, offset) pair out of the
+    // tile loop (dozens of live registers); every read is then one of these
+    // registers plus an immediate.
+    asm volatile("" : "+v"(rof[0]), "+v"(rof[1]), "+v"(rof[2]), "+v"(rof[3]), "+v"(rof[4]), "+v"(rof[5]),
+                 "+v"(rof[6]), "+v"(rof[7]));
+    asm volatile("" : "+v"(tof[0]), "+v"(tof[1]), "+v"(tof[2]), "+v"(tof[3]), "+v"(tof[4]), "+v"(tof[5]),
+                 "+v"(tof[6]), "+v"(tof[7]));
+    if (role_p) {
+      key_products(Q, x);
+      // P = 2^(S scale log2(e) - lse log2(e)); keys after a row's position
+      // get 2^-inf = 0.  Keys of this block after the earliest query position
+      // of the tile need the mask; other tiles skip it (a uniform branch).
+      if (u0 + KB - 1 > div_h(qs0 + i * QT, a.hmagic)) {
 #pragma unroll
-      for (int j = 0; j < PF - 1; ++j) {
-        fq[j] = frag_row(Q, (j >> 3) * 32 + lc, 2 * (j & 7) + h);
-        fd[j] = frag_row(G, (j >> 3) * 32 + lc, 2 * (j & 7) + h);
+        for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int q0 = qt * 32 + 8 * g4 + 4 * h;
+            const float4 L = *reinterpret_cast<const float4*>(&lse_s[cur][q0]);
+            const int4 tp = *reinterpret_cast<const int4*>(&tpos_s[cur][q0]);
+            const float Lv[4] = {L.x, L.y, L.z, L.w};
+            const int tv[4] = {tp.x, tp.y, tp.z, tp.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float y = fmaf(x[qt][4 * g4 + e], a.scale_log2, -Lv[e]);
+              x[qt][4 * g4 + e] = fexp2(myu > tv[e] ? -INFINITY : y);
+            }
+            Pex[(w * 8 + qt * 4 + g4) * 64 + lane] =
+                make_float4(x[qt][4 * g4], x[qt][4 * g4 + 1], x[qt][4 * g4 + 2], x[qt][4 * g4 + 3]);
+          }
+      } else {
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int q0 = qt * 32 + 8 * g4 + 4 * h;
+            const float4 L = *reinterpret_cast<const float4*>(&lse_s[cur][q0]);
+            const float Lv[4] = {L.x, L.y, L.z, L.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[qt][4 * g4 + e] = fexp2(fmaf(x[qt][4 * g4 + e], a.scale_log2, -Lv[e]));
+            Pex[(w * 8 + qt * 4 + g4) * 64 + lane] =
+                make_float4(x[qt][4 * g4], x[qt][4 * g4 + 1], x[qt][4 * g4 + 2], x[qt][4 * g4 + 3]);
+          }
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 0);
-#pragma unroll
-      for (int j = 0; j < NSTEP; ++j) {
-        if (j + PF - 1 < NSTEP) {
-          const int jn = j + PF - 1;
-          fq[jn % PF] = frag_row(Q, (jn >> 3) * 32 + lc, 2 * (jn & 7) + h);
-          fd[jn % PF] = frag_row(G, (jn >> 3) * 32 + lc, 2 * (jn & 7) + h);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        const int qt = j >> 3, ks = j & 7;
-        s[qt] = mfma(fq[j % PF], kreg[ks], s[qt]);
-        dp[qt] = mfma(fd[j % PF], vreg[ks], dp[qt]);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      }
-    }
-    // Keys of this block after the earliest query position of the tile need
-    // the causal mask; other tiles skip it (a uniform branch).
-    if (u0 + KB - 1 > div_h(qs0 + i * QT, a.hmagic)) {
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = qt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          const float p = myu > tpos_s[cur][qi] ? 0.f : fexp2(s[qt][r] * a.scale_log2 - lse_s[cur][qi]);
-          s[qt][r] = p;
-          dp[qt][r] = p * (dp[qt][r] - D_s[cur][qi]);
-        }
     } else {
+      key_products(G, x);
+    }
+    lds_barrier();  // P of this tile is in Pex
+    if (role_p) {
+      hd_products(G, x);  // dV^T += dO^T P
+    } else {
+      // dS = P (dP - D)
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = qt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          const float p = fexp2(s[qt][r] * a.scale_log2 - lse_s[cur][qi]);
-          s[qt][r] = p;
-          dp[qt][r] = p * (dp[qt][r] - D_s[cur][qi]);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 P4 = Pex[(w * 8 + qt * 4 + g4) * 64 + lane];
+          const float4 D4 = *reinterpret_cast<const float4*>(&D_s[cur][qt * 32 + 8 * g4 + 4 * h]);
+          x[qt][4 * g4] = P4.x * (x[qt][4 * g4] - D4.x);
+          x[qt][4 * g4 + 1] = P4.y * (x[qt][4 * g4 + 1] - D4.y);
+          x[qt][4 * g4 + 2] = P4.z * (x[qt][4 * g4 + 2] - D4.z);
+          x[qt][4 * g4 + 3] = P4.w * (x[qt][4 * g4 + 3] - D4.w);
         }
+      hd_products(Q, x);  // dK^T += Q^T dS
     }
-    // dV^T += dO^T P ; dK^T += Q^T dS
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-      for (int jp = 0; jp < 2; ++jp) {
-        const bf16x8_t pb = pack_p(s[qt], jp);
-        const bf16x8_t db = pack_p(dp[qt], jp);
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
-          dv[ht] = mfma(frag_tr(G, qt * 32 + 16 * jp, ht * 32, lane), pb, dv[ht]);
-          dk[ht] = mfma(frag_tr(Q, qt * 32 + 16 * jp, ht * 32, lane), db, dk[ht]);
-        }
-      }
     if (i + 1 < nq) put_stats(cur ^ 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -437,18 +502,15 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnMfmaArgs a) {
   }
   if (i < nq) q_tile(i, 0, Qs0, Ds0, Qs1, Ds1);
 
-  // partial [slot][2][KB keys][HD]: lane holds hd = ht*32 + 8 q4 + 4 h + e for key (w*32 + lc)
-  float* pk = a.part + ((((int64_t)b * a.nkb + kb) * smax + sp) * 2) * (KB * HD) + (w * 32 + lc) * HD;
-  float* pv = pk + KB * HD;
+  // partial [slot][2][KB keys][HD] (dK, then dV): lane holds hd = ht*32 + 8 q4 + 4 h + e for key (w*32 + lc)
+  float* pk = a.part + ((((int64_t)b * a.nkb + kb) * smax + sp) * 2 + (role_p ? 1 : 0)) * (KB * HD) + (w * 32 + lc) * HD;
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int hd = ht * 32 + 8 * q4 + 4 * h;
       *reinterpret_cast<float4*>(pk + hd) =
-          make_float4(dk[ht][4 * q4], dk[ht][4 * q4 + 1], dk[ht][4 * q4 + 2], dk[ht][4 * q4 + 3]);
-      *reinterpret_cast<float4*>(pv + hd) =
-          make_float4(dv[ht][4 * q4], dv[ht][4 * q4 + 1], dv[ht][4 * q4 + 2], dv[ht][4 * q4 + 3]);
+          make_float4(acc[ht][4 * q4], acc[ht][4 * q4 + 1], acc[ht][4 * q4 + 2], acc[ht][4 * q4 + 3]);
     }
 }
 
@@ -550,7 +612,7 @@ int attn_mfma_bwd(const void* qkv, const void* o, const void* dout, const float*
   const double fl = 2.0 * B * H * (double)HD * T * T;
   NC_TRY(attn_mfma_dq(a, s));
   probe_begin(NC_PROBE_ATTN_DKV, s);
-  attn_dkv_kernel<<<dim3(B, a.nkb * a.smax), 256, 0, s>>>(a);
+  attn_dkv_kernel<<<dim3(B, a.nkb * a.smax), 512, 0, s>>>(a);
   probe_end(NC_PROBE_ATTN_DKV, s, fl);
   NC_TRY(check_launch("attn_dkv_kernel"));
   attn_dkv_reduce_kernel<<<dim3(a.nkb, B), 256, 0, s>>>(a);

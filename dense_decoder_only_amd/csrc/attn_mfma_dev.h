@@ -73,6 +73,36 @@ __device__ __forceinline__ bf16x8_t frag_tr(const bf16* S, int rbase, int col0, 
   return __builtin_bit_cast(bf16x8_t, make_uint4(u.x, u.y, v.x, v.y));
 }
 
+// The same two reads from precomputed per-lane byte offsets (the address of
+// every fragment of a tile is then a register plus an immediate).
+__device__ __forceinline__ bf16x8_t frag_at(const bf16* S, uint32_t off) {
+  return *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const char*>(S) + off);
+}
+__device__ __forceinline__ bf16x8_t frag_tr_at(const bf16* S, uint32_t o1, uint32_t o2) {
+  const char* b = reinterpret_cast<const char*>(S);
+  const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(b + o1));
+  const bf16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(b + o2));
+  const uint2 u = __builtin_bit_cast(uint2, x), v = __builtin_bit_cast(uint2, y);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(u.x, u.y, v.x, v.y));
+}
+// Per-lane byte offsets inside a swizzled [rows][128] tile:
+//   row fragment (row 32 q + lc, chunk 2 ks + h):  rof[ks] + 8192 q;
+//   transposed fragment (output rows = columns 32 ht .. 32 ht + 31, k-slots
+//   from rows 16 m + 4 h + ...): tof[2 ht], tof[2 ht + 1], plus 4096 m.
+// Adding a multiple of 16 rows leaves the swizzle unchanged.
+__device__ __forceinline__ void frag_offsets(int lane, uint32_t (&rof)[8], uint32_t (&tof)[8]) {
+  const int lc = lane & 31, h = lane >> 5, g = lane >> 4, p = lane & 15;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) rof[ks] = (uint32_t)(toff(lc, 2 * ks + h) * 2);
+  const int r1 = 4 * h + (p >> 2);
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const int col = ht * 32 + 16 * (g & 1) + 4 * (p & 3);
+    tof[2 * ht] = (uint32_t)((toff(r1, col >> 3) + (col & 7)) * 2);
+    tof[2 * ht + 1] = (uint32_t)((toff(r1 + 8, col >> 3) + (col & 7)) * 2);
+  }
+}
+
 // Registers r = 8 jp .. 8 jp + 7 of a score tile, rounded to bf16, as the
 // B operand of the next product.
 __device__ __forceinline__ bf16x8_t pack_p(const f32x16& p, int jp) {

@@ -75,6 +75,11 @@ struct MfmaParams {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Orders this wave's LDS accesses around a hand-off between its own lanes: all
+// of its LDS operations so far have completed (lgkmcnt 0) and the compiler
+// moves no memory access across this point.  Global stores stay in flight.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // c tanh(z / c) from one hardware exp2 and reciprocal:
 // tanh|x| = (1 - e^{-2|x|}) / (1 + e^{-2|x|}).
 __device__ __forceinline__ float softcap_of(float z, float c, float inv_c) {
@@ -1092,7 +1097,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<float4*>(stage + (lane & 31) * SROW + j * 32 + 8 * q + 4 * (lane >> 5)) =
             make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-    __syncthreads();
+    // the staging area is this wave's own: only its lanes' LDS writes have to
+    // land before the reads (no block barrier, whose fence would also wait for
+    // the previous slab's global stores)
+    wave_lds_sync();
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int idx = it * 64 + lane;
@@ -1129,7 +1137,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     }
-    __syncthreads();
+    wave_lds_sync();  // this slab's reads of the staging area precede the next slab's writes
   }
 #undef PIPE_STAGE
 }
