@@ -246,6 +246,9 @@ __device__ __forceinline__ int nsplit_of(int kb, int H, int R, int qch) { return
 // Each wave holds one key-side operand (K or V of its 32 keys, 32 VGPRs) and
 // one accumulator set (64), so two waves fit per SIMD, and the softmax VALU
 // work of one overlaps the other's matrix-core products.
+#ifndef NC_DKV_PRIO
+#define NC_DKV_PRIO 1  // wave priorities that order the two roles' work on a SIMD
+#endif
 __device__ __forceinline__ void lds_barrier() {
   // this wave's LDS writes have landed; outstanding DMA (vmcnt) is not waited for
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -434,7 +437,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     asm volatile("" : "+v"(tof[0]), "+v"(tof[1]), "+v"(tof[2]), "+v"(tof[3]), "+v"(tof[4]), "+v"(tof[5]),
                  "+v"(tof[6]), "+v"(tof[7]));
     if (role_p) {
+      // the partner's dP products queue behind these on the SIMD, so that
+      // the softmax below starts early and runs beside them
+      if (NC_DKV_PRIO) __builtin_amdgcn_s_setprio(2);
       key_products(Q, x);
+      if (NC_DKV_PRIO) __builtin_amdgcn_s_setprio(0);
       // P = 2^(S scale log2(e) - lse log2(e)); keys after a row's position
       // get 2^-inf = 0.  Keys of this block after the earliest query position
       // of the tile need the mask; other tiles skip it (a uniform branch).
@@ -477,7 +484,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (role_p) {
       hd_products(G, x);  // dV^T += dO^T P
     } else {
-      // dS = P (dP - D)
+      // dS = P (dP - D); this VALU work goes ahead of the partner's dV
+      // products, which fill the matrix core meanwhile
+      if (NC_DKV_PRIO) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
@@ -489,6 +498,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           x[qt][4 * g4 + 2] = P4.z * (x[qt][4 * g4 + 2] - D4.z);
           x[qt][4 * g4 + 3] = P4.w * (x[qt][4 * g4 + 3] - D4.w);
         }
+      if (NC_DKV_PRIO) __builtin_amdgcn_s_setprio(0);
       hd_products(Q, x);  // dK^T += Q^T dS
     }
     if (i + 1 < nq) put_stats(cur ^ 1);
