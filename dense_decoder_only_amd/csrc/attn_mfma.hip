@@ -104,10 +104,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   stage(0, Ks0, Vs0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  uint32_t rof[8], tof[8];
+  frag_offsets(lane, rof, tof);
   // key tile j in (K, V); tile j + 1 is DMA'd into (Kn, Vn)
   auto kv_tile = [&](const int j, const bf16* K, const bf16* V, bf16* Kn, bf16* Vn) {
     const int kv0 = j * KT;
     if (j + 1 < ntiles) stage(j + 1, Kn, Vn);
+    // The lane offsets pass through an empty asm once per tile, so that the
+    // compiler does not hoist a register per (array, offset) pair out of the
+    // tile loop; every fragment read is one of them plus an immediate.
+    asm volatile("" : "+v"(rof[0]), "+v"(rof[1]), "+v"(rof[2]), "+v"(rof[3]), "+v"(rof[4]), "+v"(rof[5]),
+                 "+v"(rof[6]), "+v"(rof[7]));
+    asm volatile("" : "+v"(tof[0]), "+v"(tof[1]), "+v"(tof[2]), "+v"(tof[3]), "+v"(tof[4]), "+v"(tof[5]),
+                 "+v"(tof[6]), "+v"(tof[7]));
 
     f32x16 s[2];
     s[0] = zero16();
@@ -118,19 +127,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       constexpr int PF = NC_FWD_PF;
       bf16x8_t fk[PF];
 #pragma unroll
-      for (int j = 0; j < PF - 1; ++j) fk[j] = frag_row(K, (j & 1) * 32 + lc, 2 * (j >> 1) + h);
+      for (int j = 0; j < PF - 1; ++j) fk[j] = frag_at(K + (j & 1) * 32 * HD, rof[j >> 1]);
       __builtin_amdgcn_sched_group_barrier(0x100, PF - 1, 0);
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         if (j + PF - 1 < 16) {
           const int jn = j + PF - 1;
-          fk[jn % PF] = frag_row(K, (jn & 1) * 32 + lc, 2 * (jn >> 1) + h);
+          fk[jn % PF] = frag_at(K + (jn & 1) * 32 * HD, rof[jn >> 1]);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         s[j & 1] = mfma(fk[j % PF], qreg[j >> 1], s[j & 1]);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
     }
+    // Row maxima of the raw scores (the scale is positive, so it commutes
+    // with the maximum); the scale is applied inside the exponent below.
     float mt = -INFINITY;
     if (kv0 + KT - 1 > tmin) {  // the tile crosses some row's diagonal
 #pragma unroll
@@ -138,7 +149,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kv = kv0 + st * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          const float x = kv > tq ? -INFINITY : s[st][r] * a.scale_log2;
+          const float x = kv > tq ? -INFINITY : s[st][r];
           s[st][r] = x;
           mt = fmaxf(mt, x);
         }
@@ -146,13 +157,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = s[st][r] * a.scale_log2;
-          s[st][r] = x;
-          mt = fmaxf(mt, x);
-        }
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[st][r]);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * a.scale_log2;
     // Lazy rescaling: the reference maximum only moves when the tile maximum
     // exceeds it by more than 8 (log2 units), so probabilities stay <= 2^8
     // and the rescale of the running sums is skipped (wave-uniformly) on most
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fexp2(s[st][r] - m_run);
+        const float p = fexp2(fmaf(s[st][r], a.scale_log2, -m_run));
         s[st][r] = p;
         ls += p;
       }
@@ -184,7 +191,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // PF - 1 steps ahead (a ring)
       constexpr int PF = NC_FWD_PF;
       bf16x8_t fv[PF];
-      auto v_read = [&](int j) { fv[j % PF] = frag_tr(V, (j >> 3) * 32 + 16 * ((j >> 2) & 1), (j & 3) * 32, lane); };
+      auto v_read = [&](int j) {
+        fv[j % PF] = frag_tr_at(V + ((j >> 3) * 32 + 16 * ((j >> 2) & 1)) * HD, tof[2 * (j & 3)], tof[2 * (j & 3) + 1]);
+      };
 #pragma unroll
       for (int j = 0; j < PF - 1; ++j) v_read(j);
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 0);
