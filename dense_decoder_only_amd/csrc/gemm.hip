@@ -71,6 +71,7 @@ struct MfmaParams {
   // on XCD s mod 8 (gemm_pipe_kernel only; kxcd a multiple of 8)
   int kxcd = 0;
   int xv0;
+  int splits = 1;  // gemm_pipe_kernel: k-splits (work items = tiles x splits)
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -918,21 +919,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
-  int bid = blockIdx.x, split = blockIdx.z;
+  // Persistent blocks: work item f (a tile, or a tile and k-split) runs on
+  // block f mod gridDim.x, items in increasing order, so that a CU goes from
+  // one tile to the next without a new block being dispatched.  Blocks are
+  // dealt round-robin to the 8 XCDs and gridDim.x is a multiple of 8, so
+  // item f still runs on XCD f mod 8.
+  const int nb = p.tiles_m * p.tiles_n;
+  for (int item = blockIdx.x; item < nb * p.splits; item += gridDim.x) {
+  int bid = item, split = 0;
+  float* cpart = static_cast<float*>(p.C);  // E_PARTIAL: this split's [M][N] slice
 #if NC_GEMM_XCD
   if (p.kxcd) {
-    // Split-K: blocks are dealt round-robin to the 8 XCDs, so block id i runs
-    // on XCD i mod 8.  Give every XCD whole k-splits (split s on XCD s mod 8):
-    // an XCD then reads only its own k-ranges of the panels, and its tiles
-    // (in the grouped order below) share those ranges in its L2.
-    const int nb = p.tiles_m * p.tiles_n;
+    // Split-K with a multiple of 8 splits: give every XCD whole k-splits
+    // (split s on XCD s mod 8): an XCD then reads only its own k-ranges of
+    // the panels, and its tiles (in the grouped order below) share those
+    // ranges in its L2.
     const int j = bid >> 3;
     split = (bid & 7) + 8 * (j / nb);
     bid = j % nb;
-    // the partial-product epilogue indexes its slice by blockIdx.z (0 here)
-    p.C = static_cast<float*>(p.C) + (int64_t)split * p.M * p.N;
   } else {
-    const int nb = p.tiles_m * p.tiles_n;
+    split = bid / nb;
+    bid -= split * nb;
     const int per = nb >> 3;
     if (bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
   }
@@ -941,8 +948,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int gm = min(p.tiles_m - first_m, NC_GEMM_GROUP_M);
   const int tm = first_m + (bid % gsize) % gm, tn = (bid % gsize) / gm;
 #else
+  split = bid / nb;
+  bid -= split * nb;
   const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
 #endif
+  if constexpr (EPI == E_PARTIAL) cpart += (int64_t)split * p.M * p.N;
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = split * p.k_per_split;
   int kend = kbeg + p.k_per_split;
@@ -1048,26 +1058,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int SROW = 68;
   static_assert(3 * 32 * SROW * 4 <= BM * BK * 2, "epilogue staging does not fit a stage");
   float* stage = reinterpret_cast<float*>(wave < 3 ? sA0 : (wave < 6 ? sA1 : sB0)) + (wave % 3) * (32 * SROW);
-  // Epilogue inputs read from memory are loaded ahead of their use so that
-  // their latency overlaps the LDS staging: the relu^2 backward's stored
-  // activation for the whole sub-tile up front, the accumulated fp32 C one
-  // 32-row slab ahead.  Element (i, it) of this lane is row
+  // Epilogue inputs read from memory are loaded one 32-row slab ahead of
+  // their use, so that their latency overlaps the LDS staging: the relu^2
+  // backward's stored activation and the accumulated fp32 C.  Element (i, it) of this lane is row
   // m0 + wm 128 + 32 i + (64 it + lane) / 16, columns n0 + wn 64 + 4 (lane % 16) + 0..3.
   constexpr bool PF_AUX = EPI == E_RELU2_BWD || EPI == E_RELU2_BWD_SQ;
   constexpr bool PF_C = EPI == E_ACC_F32;
   const int er0 = m0 + wm * 128 + (lane >> 4), ec = n0 + wn * 64 + (lane & 15) * 4;
-  uint2 pa[PF_AUX ? 4 : 1][8];
+  uint2 pa[2][8];
   float4 pc[2][8];
-  if constexpr (PF_AUX) {
+  auto load_aux = [&](int i, uint2 (&dst)[8]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int grow = er0 + i * 32 + 4 * it;
-        pa[i][it] = grow < p.M && ec < p.N ? *reinterpret_cast<const uint2*>(p.aux + (int64_t)grow * p.ldc + ec)
-                                           : make_uint2(0, 0);
-      }
-  }
+    for (int it = 0; it < 8; ++it) {
+      const int grow = er0 + i * 32 + 4 * it;
+      dst[it] = grow < p.M && ec < p.N ? *reinterpret_cast<const uint2*>(p.aux + (int64_t)grow * p.ldc + ec)
+                                       : make_uint2(0, 0);
+    }
+  };
+  if constexpr (PF_AUX) load_aux(0, pa[0]);
   if constexpr (PF_C) {
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
@@ -1079,6 +1087,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    if constexpr (PF_AUX) {
+      if (i + 1 < 4) load_aux(i + 1, pa[(i + 1) & 1]);
+    }
     if constexpr (PF_C) {
       if (i + 1 < 4) {
 #pragma unroll
@@ -1114,7 +1125,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if constexpr (EPI == E_XENT_BWD) {
           xent_bwd4(p, v, grow, gcol, s_xt[grow - m0], s_xl[grow - m0]);
         } else if constexpr (EPI == E_RELU2_BWD_SQ) {
-          const uint2 q = pa[i][it];
+          const uint2 q = pa[i & 1][it];
           const float r0 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.x & 0xffffu)));
           const float r1 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.x >> 16)));
           const float r2 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.y & 0xffffu)));
@@ -1122,7 +1133,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + off) =
               make_uint2(pack_bf16x2(v.x * 2.f * r0, v.y * 2.f * r1), pack_bf16x2(v.z * 2.f * r2, v.w * 2.f * r3));
         } else if constexpr (EPI == E_RELU2_BWD) {
-          const uint2 u = pa[i][it];
+          const uint2 u = pa[i & 1][it];
           const float u0 = bf2f((bf16)(u.x & 0xffffu)), u1 = bf2f((bf16)(u.x >> 16));
           const float u2 = bf2f((bf16)(u.y & 0xffffu)), u3 = bf2f((bf16)(u.y >> 16));
           *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + off) =
@@ -1132,6 +1143,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const float4 o = pc[i & 1][it];
           *reinterpret_cast<float4*>(static_cast<float*>(p.C) + off) =
               make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+        } else if constexpr (EPI == E_PARTIAL) {
+          *reinterpret_cast<float4*>(cpart + (int64_t)grow * p.N + gcol) = v;
         } else {
           epilogue4<EPI>(p, v, grow, gcol);
         }
@@ -1139,18 +1152,38 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     wave_lds_sync();  // this slab's reads of the staging area precede the next slab's writes
   }
+  // The next item's DMA and target fetch reuse the LDS this epilogue read:
+  // a block barrier after this wave's LDS reads (its global stores may stay
+  // in flight).
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  }
 #undef PIPE_STAGE
+}
+
+// Blocks of the persistent GEMM grid: one per CU (a block's 128 KB of LDS
+// leaves room for no second one), a multiple of 8 so that every XCD gets the
+// same number.
+int persistent_blocks() {
+  static int blocks[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!blocks[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
+    blocks[dev] = cus / 8 * 8;
+  }
+  return blocks[dev];
 }
 
 template <bool TN>
 hipError_t launch_pipe(int epi, const MfmaParams& p0, int splits, hipStream_t s) {
   MfmaParams p = p0;
-  dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
-  p.kxcd = 0;
-  if (NC_GEMM_KXCD && NC_GEMM_XCD && epi == E_PARTIAL && splits > 1 && splits % 8 == 0) {
-    p.kxcd = splits;
-    grid = dim3(p.tiles_m * p.tiles_n * splits, 1, 1);
-  }
+  p.splits = splits;
+  p.kxcd = NC_GEMM_KXCD && NC_GEMM_XCD && epi == E_PARTIAL && splits > 1 && splits % 8 == 0 ? splits : 0;
+  const int items = p.tiles_m * p.tiles_n * splits;
+  dim3 grid(std::min(items, persistent_blocks()), 1, 1);
   switch (epi) {
     case E_STORE_F32: gemm_pipe_kernel<E_STORE_F32, TN><<<grid, 512, 0, s>>>(p); break;
     case E_ACC_F32: gemm_pipe_kernel<E_ACC_F32, TN><<<grid, 512, 0, s>>>(p); break;
