@@ -243,15 +243,24 @@ int mqa_attn_fwd(const void* qkv, int dtype, int B, int T, int H, int hd, float 
   return fwd_simple<bf16>(qkv, B, T, H, hd, scale, o, lse, s);
 }
 
+bool attn_rope_bwd_fusable(int dtype, int hd) { return dtype == NC_BF16 && hd == 128; }
+
 int mqa_attn_bwd(const void* qkv, const void* o, const void* dout, const float* lse, int dtype, int B, int T, int H,
-                 int hd, float scale, float* dqkv, void* ws, size_t ws_bytes, hipStream_t s) {
+                 int hd, float scale, float* dqkv, void* ws, size_t ws_bytes, hipStream_t s, const AttnRopeBwd* fuse) {
   NC_TRY(validate(qkv, dtype, B, T, H, hd));
-  NC_REQUIRE(o && dout && lse && dqkv, NC_ERR_INVALID_ARG, "mqa_attn_bwd: null pointer");
+  if (fuse) {
+    NC_REQUIRE(attn_rope_bwd_fusable(dtype, hd), NC_ERR_UNSUPPORTED, "mqa_attn_bwd: fused RoPE backward needs bf16, hd 128");
+    NC_REQUIRE(fuse->rstd_q && fuse->rstd_k && fuse->table && fuse->dqkv, NC_ERR_INVALID_ARG,
+               "mqa_attn_bwd: null fused-output pointer");
+  } else {
+    NC_REQUIRE(dqkv, NC_ERR_INVALID_ARG, "mqa_attn_bwd: null pointer");
+  }
+  NC_REQUIRE(o && dout && lse, NC_ERR_INVALID_ARG, "mqa_attn_bwd: null pointer");
   NC_REQUIRE(ws && ws_bytes >= mqa_attn_bwd_workspace_bytes(B, T, H), NC_ERR_WORKSPACE,
              "mqa_attn_bwd: workspace too small (%zu < %zu)", ws_bytes, mqa_attn_bwd_workspace_bytes(B, T, H));
   float* Dbuf = static_cast<float*>(ws);
   if (dtype == NC_F32) return bwd_simple<float>(qkv, o, dout, lse, B, T, H, hd, scale, dqkv, Dbuf, s);
-  if (hd == 128) return attn_mfma_bwd(qkv, o, dout, lse, B, T, H, scale, dqkv, ws, s);
+  if (hd == 128) return attn_mfma_bwd(qkv, o, dout, lse, B, T, H, scale, dqkv, ws, s, fuse);
   return bwd_simple<bf16>(qkv, o, dout, lse, B, T, H, hd, scale, dqkv, Dbuf, s);
 }
 

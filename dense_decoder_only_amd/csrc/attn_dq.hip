@@ -128,7 +128,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC_ATTN_DQ_
     __syncthreads();
   }
 
-  if (valid) {
+  if (a.dqkv_lp) {
+    // QK-norm and RoPE backward of the block's 128 query rows, giving the
+    // bf16 gradient w.r.t. the projection output:
+    //   g' = rstd (g - yhat mean(g yhat)), rotated back by -theta over the
+    //   dim pairs (i, i + 64).
+    // The fp32 dQ tile goes through LDS (free after the last tile's barrier)
+    // so that the row-wise pass holds no MFMA accumulators: waves 0-1 use Ks,
+    // 2-3 Vs, 16 KB per wave, 16-byte chunk c of row lc at c ^ lc.
+    float* G = reinterpret_cast<float*>(w < 2 ? Ks : Vs) + (w & 1) * 32 * HD;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c = ht * 8 + 2 * q4 + h;
+        *reinterpret_cast<float4*>(G + lc * HD + ((c ^ lc) << 2)) =
+            make_float4(dq[ht][4 * q4], dq[ht][4 * q4 + 1], dq[ht][4 * q4 + 2], dq[ht][4 * q4 + 3]);
+      }
+    __syncthreads();
+    const int j = tid & 15;  // dims 4 j .. 4 j + 3 and their pair partners + 64
+#pragma unroll 1
+    for (int row = tid >> 4; row < QB; row += 16) {
+      const int qr = r0 + row;
+      if (qr >= R) break;
+      const int tqr = div_h(qr, a.hmagic), hqr = qr - tqr * H;
+      const float* Gr = reinterpret_cast<const float*>((row >> 6) == 0 ? Ks : Vs) + (row & 63) * HD;
+      const int sw = row & 31;
+      const float4 ga4 = *reinterpret_cast<const float4*>(Gr + ((j ^ sw) << 2));
+      const float4 gb4 = *reinterpret_cast<const float4*>(Gr + (((j + 16) ^ sw) << 2));
+      const float ga[4] = {ga4.x * a.scale, ga4.y * a.scale, ga4.z * a.scale, ga4.w * a.scale};
+      const float gb[4] = {gb4.x * a.scale, gb4.y * a.scale, gb4.z * a.scale, gb4.w * a.scale};
+      const int64_t tok = (int64_t)b * T + tqr;
+      const bf16* yr = a.qkv + tok * a.S + hqr * HD + 4 * j;
+      const uint2 ua = *reinterpret_cast<const uint2*>(yr), ub = *reinterpret_cast<const uint2*>(yr + 64);
+      const float ya[4] = {__uint_as_float(ua.x << 16), __uint_as_float(ua.x & 0xffff0000u),
+                           __uint_as_float(ua.y << 16), __uint_as_float(ua.y & 0xffff0000u)};
+      const float yb[4] = {__uint_as_float(ub.x << 16), __uint_as_float(ub.x & 0xffff0000u),
+                           __uint_as_float(ub.y << 16), __uint_as_float(ub.y & 0xffff0000u)};
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot += ga[e] * ya[e] + gb[e] * yb[e];
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 16);
+      const float mean = dot * (1.f / 128.f);
+      const float r = a.rstd_q[(int64_t)b * R + qr];
+      const float4* tb = reinterpret_cast<const float4*>(a.rope_tab + ((int64_t)tqr * 64 + 4 * j) * 2);
+      const float4 cs0 = tb[0], cs1 = tb[1];  // (cos, sin) of pairs 4 j .. 4 j + 3
+      const float cc[4] = {cs0.x, cs0.z, cs1.x, cs1.z}, sn[4] = {cs0.y, cs0.w, cs1.y, cs1.w};
+      float oa[4], ob[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pa = r * (ga[e] - ya[e] * mean), pb = r * (gb[e] - yb[e] * mean);
+        oa[e] = pa * cc[e] + pb * sn[e];  // rotate back by -theta
+        ob[e] = -pa * sn[e] + pb * cc[e];
+      }
+      bf16* out = a.dqkv_lp + tok * (int64_t)(H + 2) * HD + hqr * HD + 4 * j;
+      *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(oa[0], oa[1]), pack_bf16x2(oa[2], oa[3]));
+      *reinterpret_cast<uint2*>(out + 64) = make_uint2(pack_bf16x2(ob[0], ob[1]), pack_bf16x2(ob[2], ob[3]));
+    }
+  } else if (valid) {
     float* out = a.dqkv + ((int64_t)b * T + tq) * (int64_t)(H + 2) * HD + hq * HD;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)

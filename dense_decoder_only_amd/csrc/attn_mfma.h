@@ -1,6 +1,7 @@
 // Matrix-core attention kernels (bf16, head_dim 128); see attn_mfma.hip.
 #pragma once
 #include "common.h"
+#include "ops.h"
 
 namespace nc {
 
@@ -20,12 +21,19 @@ struct AttnMfmaArgs {
   int nkb, smax;
   int qch;             // query rows per dK/dV split (a multiple of 64)
   uint32_t hmagic;     // ceil(2^32 / H): r / H == umulhi(r, hmagic) for r < 2^32 / H^2
+  // Backward with the QK-norm and RoPE backward folded in (dqkv_lp != null):
+  // the dQ and dK/dV-reduce kernels write the gradient w.r.t. the projection
+  // output, bf16 [B*T, (H+2)*128], instead of fp32 dqkv.
+  bf16* dqkv_lp;
+  const float* rstd_q;    // [B*T, H]
+  const float* rstd_k;    // [B*T]
+  const float* rope_tab;  // [T, 64, 2] (cos, sin)
 };
 
 size_t attn_mfma_bwd_workspace_bytes(int B, int T, int H);
 int attn_mfma_fwd(const void* qkv, int B, int T, int H, float scale, void* o, float* lse, hipStream_t s);
 int attn_mfma_bwd(const void* qkv, const void* o, const void* dout, const float* lse, int B, int T, int H, float scale,
-                  float* dqkv, void* ws, hipStream_t s);
+                  float* dqkv, void* ws, hipStream_t s, const AttnRopeBwd* fuse = nullptr);
 // The dQ launch of attn_mfma_bwd (also writes D = rowsum(dO * O) to a.Dbuf).
 int attn_mfma_dq(const AttnMfmaArgs& a, hipStream_t s);
 

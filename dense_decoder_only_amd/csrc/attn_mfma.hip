@@ -550,9 +550,43 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(AttnMfmaArgs a) {
       sk.x += x.x; sk.y += x.y; sk.z += x.z; sk.w += x.w;
       sv.x += y.x; sv.y += y.y; sv.z += y.z; sv.w += y.w;
     }
-    float* row = a.dqkv + ((int64_t)b * T + u) * (int64_t)(H + 2) * HD;
-    *reinterpret_cast<float4*>(row + H * HD + hd) = make_float4(sk.x * a.scale, sk.y * a.scale, sk.z * a.scale, sk.w * a.scale);
-    *reinterpret_cast<float4*>(row + (H + 1) * HD + hd) = sv;
+    const int64_t tok = (int64_t)b * T + u;
+    if (a.dqkv_lp) {
+      // QK-norm and RoPE backward of the key row: the 32 threads of a key row
+      // are 32 consecutive lanes (4 dims each), and the partner of dim hd in
+      // its RoPE pair (hd + 64 or hd - 64) sits 16 lanes away.
+      const float g[4] = {sk.x * a.scale, sk.y * a.scale, sk.z * a.scale, sk.w * a.scale};
+      const uint2 yu = *reinterpret_cast<const uint2*>(a.qkv + tok * a.S + H * HD + hd);
+      const float y[4] = {__uint_as_float(yu.x << 16), __uint_as_float(yu.x & 0xffff0000u),
+                          __uint_as_float(yu.y << 16), __uint_as_float(yu.y & 0xffff0000u)};
+      float dot = g[0] * y[0] + g[1] * y[1] + g[2] * y[2] + g[3] * y[3];
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 32);
+      const float mean = dot * (1.f / 128.f);
+      const float r = a.rstd_k[tok];
+      float pv[4], qv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[e] = r * (g[e] - y[e] * mean);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[e] = __shfl_xor(pv[e], 16, 32);  // the pair partner's value
+      const bool lo = hd < 64;
+      const int i = lo ? hd : hd - 64;
+      const float4 cs0 = *reinterpret_cast<const float4*>(a.rope_tab + (int64_t)u * 128 + 2 * i);
+      const float4 cs1 = *reinterpret_cast<const float4*>(a.rope_tab + (int64_t)u * 128 + 2 * i + 4);
+      const float c[4] = {cs0.x, cs0.z, cs1.x, cs1.z}, sn[4] = {cs0.y, cs0.w, cs1.y, cs1.w};
+      float o4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)  // rotate back by -theta: (a, b) -> (a c + b s, -a s + b c)
+        o4[e] = lo ? pv[e] * c[e] + qv[e] * sn[e] : -qv[e] * sn[e] + pv[e] * c[e];
+      bf16* row = a.dqkv_lp + tok * (int64_t)(H + 2) * HD;
+      *reinterpret_cast<uint2*>(row + H * HD + hd) = make_uint2(pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3]));
+      *reinterpret_cast<uint2*>(row + (H + 1) * HD + hd) = make_uint2(pack_bf16x2(sv.x, sv.y), pack_bf16x2(sv.z, sv.w));
+    } else {
+      float* row = a.dqkv + tok * (int64_t)(H + 2) * HD;
+      *reinterpret_cast<float4*>(row + H * HD + hd) =
+          make_float4(sk.x * a.scale, sk.y * a.scale, sk.z * a.scale, sk.w * a.scale);
+      *reinterpret_cast<float4*>(row + (H + 1) * HD + hd) = sv;
+    }
   }
 }
 
@@ -605,7 +639,7 @@ int attn_mfma_fwd(const void* qkv, int B, int T, int H, float scale, void* o, fl
 }
 
 int attn_mfma_bwd(const void* qkv, const void* o, const void* dout, const float* lse, int B, int T, int H, float scale,
-                  float* dqkv, void* ws, hipStream_t s) {
+                  float* dqkv, void* ws, hipStream_t s, const AttnRopeBwd* fuse) {
   NC_REQUIRE((uint64_t)T * H * H < ((uint64_t)1 << 32), NC_ERR_UNSUPPORTED, "attention: T * H^2 must be < 2^32");
   // the dK/dV staging addresses a sequence's q/k/v rows with 32-bit byte offsets
   NC_REQUIRE((int64_t)T * (H + 2) * HD * 2 < ((int64_t)1 << 31), NC_ERR_UNSUPPORTED,
@@ -628,6 +662,12 @@ int attn_mfma_bwd(const void* qkv, const void* o, const void* dout, const float*
   a.qch = attn_mfma_qch(B, T, H);
   a.smax = attn_mfma_smax(B, T, H);
   a.hmagic = (uint32_t)((((uint64_t)1 << 32) + H - 1) / H);
+  if (fuse) {
+    a.dqkv_lp = static_cast<bf16*>(fuse->dqkv);
+    a.rstd_q = fuse->rstd_q;
+    a.rstd_k = fuse->rstd_k;
+    a.rope_tab = fuse->table;
+  }
   const double fl = 2.0 * B * H * (double)HD * T * T;
   NC_TRY(attn_mfma_dq(a, s));
   probe_begin(NC_PROBE_ATTN_DKV, s);

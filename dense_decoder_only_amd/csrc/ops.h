@@ -21,11 +21,22 @@ int rope_qknorm_fwd(void* qkv, int dtype, int B, int T, int H, int hd, const flo
 int rope_qknorm_bwd(const float* dhat, const void* yhat, const float* rstd_q, const float* rstd_k,
                     const float* table, int dtype, int B, int T, int H, int hd, void* dqkv, hipStream_t s);
 
+// Optional fusion of the QK-norm + RoPE backward into the attention backward
+// (bf16, head_dim 128): the kernels then write dqkv (bf16, the gradient w.r.t.
+// the projection output) instead of the fp32 gradients w.r.t. q-hat, k-hat, v.
+struct AttnRopeBwd {
+  const float* rstd_q;
+  const float* rstd_k;
+  const float* table;
+  void* dqkv;
+};
+bool attn_rope_bwd_fusable(int dtype, int hd);
 size_t mqa_attn_bwd_workspace_bytes(int B, int T, int H);
 int mqa_attn_fwd(const void* qkv, int dtype, int B, int T, int H, int hd, float scale, void* o, float* lse,
                  hipStream_t s);
 int mqa_attn_bwd(const void* qkv, const void* o, const void* dout, const float* lse, int dtype, int B, int T, int H,
-                 int hd, float scale, float* dqkv, void* ws, size_t ws_bytes, hipStream_t s);
+                 int hd, float scale, float* dqkv, void* ws, size_t ws_bytes, hipStream_t s,
+                 const AttnRopeBwd* fuse = nullptr);
 
 size_t xent_workspace_bytes(int64_t M, int d, int V);
 // store_logits: keep the softcapped logits in ws (16-bit fixed point) when the

@@ -374,11 +374,18 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
     NC_TRY(wgrad(mk(1, 0, d, HD, M, gop, d, ly.o, HD, gr->w_o + (size_t)l * d * HD, NC_F32, HD, dt)));
     NC_TRY(mark_read(B_G, gv));
     NC_TRY(gemm(tw ? mk(0, 1, M, HD, d, gop, d, WoT, d, w.dout, dt, HD, dt) : mk(0, 0, M, HD, d, gop, d, Wo, HD, w.dout, dt, HD, dt), s));
-    NC_TRY(mqa_attn_bwd(ly.qkv, ly.o, w.dout, ly.lse, dt, B, T, H, hd, scale, w.dqkv_hat, w.attn_ws,
-                        w.attn_ws_bytes, s));
     void* dqkv = w.dqkv[qv % kRing];
     NC_TRY(reuse(B_DQ, qv));
-    NC_TRY(rope_qknorm_bwd(w.dqkv_hat, ly.qkv, ly.rstd_q, ly.rstd_k, w.table, dt, B, T, H, hd, dqkv, s));
+    if (attn_rope_bwd_fusable(dt, hd)) {
+      // the attention backward also applies the QK-norm and RoPE backward
+      const AttnRopeBwd fuse{ly.rstd_q, ly.rstd_k, w.table, dqkv};
+      NC_TRY(mqa_attn_bwd(ly.qkv, ly.o, w.dout, ly.lse, dt, B, T, H, hd, scale, nullptr, w.attn_ws, w.attn_ws_bytes, s,
+                          &fuse));
+    } else {
+      NC_TRY(mqa_attn_bwd(ly.qkv, ly.o, w.dout, ly.lse, dt, B, T, H, hd, scale, w.dqkv_hat, w.attn_ws,
+                          w.attn_ws_bytes, s));
+      NC_TRY(rope_qknorm_bwd(w.dqkv_hat, ly.qkv, ly.rstd_q, ly.rstd_k, w.table, dt, B, T, H, hd, dqkv, s));
+    }
     NC_TRY(fork());
     NC_TRY(wgrad(mk(1, 0, Q, d, M, dqkv, Q, ly.a, d, gr->w_qkv + (size_t)l * Q * d, NC_F32, d, dt)));
     NC_TRY(mark_read(B_DQ, qv));
