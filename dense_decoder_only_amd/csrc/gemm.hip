@@ -782,32 +782,21 @@ __device__ __forceinline__ bf16x8_t frag_tn(const bf16* S, int ks, int col0, int
 // ds_read_b64_tr_b16).  Same 2 x 4 grid of 128 x 64 wave tiles as above, but
 // the k loop is rotated so the MFMA pipe never waits on a barrier-fresh tile:
 // the block barrier sits inside the last k-step, after its first MFMAs, and
-// right after it the waves issue the DMA of tile kt + 2 (into the buffer just
-// released) and the first fragment reads of tile kt + 1, while the rest of
-// the last k-step's MFMAs run.  Every k-tile must be full.
+// right after it the waves issue the A half of tile kt + 2's DMA (into the
+// buffer just released) and the first fragment reads of tile kt + 1, while
+// the rest of the last k-step's MFMAs run.  The B half follows in the first
+// k-step of tile kt + 1.  Each DMA instruction sits behind its own MFMA:
+// issued as a burst of eight per wave (64 per CU) they queued in the load
+// path and held up the MFMAs behind them (2-3% slower).  Every k-tile must be
+// full.
 // ---------------------------------------------------------------------------
 #ifndef NC_GEMM_PIPE_PRE
 #define NC_GEMM_PIPE_PRE 2  // MFMAs of the last k-step issued before the barrier
 #endif
 
-template <bool TN>
-__device__ __forceinline__ void pipe_stage(const MfmaParams& p, int m0, int n0, int k0, bf16* a_buf, bf16* b_buf,
-                                           int wave, int lane) {
-  if constexpr (TN) {
-    stage_tn(p.A, p.lda, m0, p.M, k0, a_buf, wave, lane);
-    stage_tn(p.B, p.ldb, n0, p.N, k0, b_buf, wave, lane);
-  } else {
-    stage_direct8(p.A, p.lda, m0, p.M, k0, a_buf, wave, lane);
-    stage_direct8(p.B, p.ldb, n0, p.N, k0, b_buf, wave, lane);
-  }
-}
-
-// Buffer-resource form of the same staging: per stage a scalar base (the
-// tile's first row and column) and per lane loop-invariant 32-bit byte
-// offsets, computed once per block.
-#ifndef NC_GEMM_BUFDMA
-#define NC_GEMM_BUFDMA 1
-#endif
+// Staging of the pipelined kernel: per stage a scalar buffer resource at the
+// tile's first row and column and per-lane loop-invariant 32-bit byte
+// offsets, computed once per tile.
 struct StageOff {
   uint32_t a[4], b[4];
 };
@@ -857,6 +846,20 @@ __device__ __forceinline__ void pipe_stage_buf(const MfmaParams& p, int m0, int 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(b_buf + g * step), 16,
                                              o.b[i], 0, 0, 0);
   }
+}
+
+template <bool TN, int OP>
+__device__ __forceinline__ void pipe_stage_one(const MfmaParams& p, int r0, int k0, bf16* buf, int wave,
+                                               const uint32_t (&o)[4]) {
+  const bf16* P = OP == 0 ? p.A : p.B;
+  const int64_t ld = OP == 0 ? p.lda : p.ldb;
+  const bf16* pa = TN ? P + (int64_t)k0 * ld + r0 : P + (int64_t)r0 * ld + k0;
+  const __amdgpu_buffer_rsrc_t ra = tile_rsrc(pa);
+  const int step = TN ? 2 * TROW : 8 * BK;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(buf + (wave * 4 + i) * step), 16,
+                                             o[i], 0, 0, 0);
 }
 
 template <bool TN>
@@ -975,15 +978,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-#if NC_GEMM_BUFDMA
   StageOff so;
   stage_offsets<TN>(p, m0, n0, wave, lane, so);
-#define PIPE_STAGE(k0, abuf, bbuf) pipe_stage_buf<TN>(p, m0, n0, k0, abuf, bbuf, wave, so)
-#else
-#define PIPE_STAGE(k0, abuf, bbuf) pipe_stage<TN>(p, m0, n0, k0, abuf, bbuf, wave, lane)
-#endif
-  PIPE_STAGE(kbeg, sA0, sB0);
-  PIPE_STAGE(nk > 1 ? kbeg + BK : kbeg, sA1, sB1);
+  pipe_stage_buf<TN>(p, m0, n0, kbeg, sA0, sB0, wave, so);
+  pipe_stage_buf<TN>(p, m0, n0, nk > 1 ? kbeg + BK : kbeg, sA1, sB1, wave, so);
   // Only the first stage has to have landed here (vmcnt <= the 8 DMAs of the
   // second stage per wave, expcnt and lgkmcnt not waited on): the second
   // one is waited for at the barrier inside the first k-tile.  A plain
@@ -1001,11 +999,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // k-tile kt: its operands are in stage (a_c, b_c); tile kt + 1 is in the
   // other stage (a_o, b_o), and tile kt + 2 is DMA'd into (a_c, b_c) once
-  // the block is past its last reads.
-  auto k_tile = [&](const int kt, bf16* a_c, bf16* b_c, const bf16* a_o, const bf16* b_o) {
+  // the block is past its last reads: A right after the barrier in tile kt's
+  // last k-step, B in tile kt + 1's first k-step (where this lambda issues B
+  // of tile kt + 1 into b_o, released at the previous tile's barrier).
+  auto k_tile = [&](const int kt, bf16* a_c, bf16* b_c, bf16* a_o, bf16* b_o) {
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
       const int c = ks & 1;
+      if (ks == 0) {  // (tile 1's B repeats the prologue's DMA: same data)
+        const int k1 = kt + 1 < nk ? kbeg + (kt + 1) * BK : klast;
+        pipe_stage_one<TN, 1>(p, n0, k1, b_o, wave, so.b);
+      }
       pipe_frags<TN>(a_c, b_c, ks + 1, wm, wn, lane, fa[c ^ 1], fb[c ^ 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -1013,16 +1017,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][i], acc[i][j], 0, 0, 0);
       // all of the next k-step's reads go out under the first MFMAs
+      if (ks == 0) {
 #pragma unroll
-      for (int g = 0; g < 3; ++g) {
+        for (int g = 0; g < 3; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, NR / 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        }
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, NR / 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      } else {
+#pragma unroll
+        for (int g = 0; g < 3; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, NR / 3, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
     }
-    // last k-step (fragments in set 1): PRE MFMAs, barrier, then the DMA of
-    // tile kt + 2 into the released buffer and tile kt + 1's first fragments
-    // under the remaining MFMAs.
+    // last k-step (fragments in set 1): PRE MFMAs, barrier, then the A DMA
+    // of tile kt + 2 into the released buffer and tile kt + 1's first
+    // fragments under the remaining MFMAs.
 #pragma unroll
     for (int q = 0; q < NC_GEMM_PIPE_PRE; ++q)
       acc[q >> 1][q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][q & 1], fa[1][q >> 1], acc[q >> 1][q & 1], 0, 0, 0);
@@ -1033,17 +1049,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     const int k2 = kt + 2 < nk ? kbeg + (kt + 2) * BK : klast;
-    PIPE_STAGE(k2, a_c, b_c);
+    pipe_stage_one<TN, 0>(p, m0, k2, a_c, wave, so.a);
     pipe_frags<TN>(a_o, b_o, 0, wm, wn, lane, fa[0], fb[0]);
 #pragma unroll
     for (int q = NC_GEMM_PIPE_PRE; q < 8; ++q)
       acc[q >> 1][q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][q & 1], fa[1][q >> 1], acc[q >> 1][q & 1], 0, 0, 0);
     constexpr int POST = 8 - NC_GEMM_PIPE_PRE;
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x010, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x010, 4, 0);
-    sched_mfma_ds<0, POST - 2, NR>();
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    }
+    sched_mfma_ds<0, POST - 4, NR>();
   };
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
@@ -1159,7 +1176,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   }
-#undef PIPE_STAGE
 }
 
 // Blocks of the persistent GEMM grid: one per CU (a block's 128 KB of LDS
