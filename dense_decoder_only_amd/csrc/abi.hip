@@ -3,6 +3,7 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <atomic>
 #include <mutex>
@@ -19,6 +20,22 @@ int set_error(int code, const char* fmt, ...) {
   vsnprintf(g_err, sizeof(g_err), fmt, ap);
   va_end(ap);
   return code;
+}
+
+bool debug_mode() {
+  static const bool on = [] {
+    const char* v = getenv("NC_DEBUG");
+    return v != nullptr && v[0] == '1' && v[1] == '\0';
+  }();
+  return on;
+}
+
+int api_done(int rc, void* stream, const char* name) {
+  if (rc != NC_OK || !debug_mode()) return rc;
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return set_error(NC_ERR_HIP, "%s: %s (found by the NC_DEBUG=1 check)", name, hipGetErrorString(e));
+  return NC_OK;
 }
 
 int check_launch(const char* what) {
@@ -128,6 +145,8 @@ extern "C" const char* nc_last_error(void) { return nc::g_err; }
 
 extern "C" const char* nc_version(void) { return "libnc 0.1.0 (gfx950)"; }
 
+extern "C" int nc_debug_mode(void) { return nc::debug_mode() ? 1 : 0; }
+
 extern "C" int nc_sync_status(const int32_t* flag, void* stream) {
   NC_REQUIRE(flag, NC_ERR_INVALID_ARG, "sync_status: null flag");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -135,5 +154,5 @@ extern "C" int nc_sync_status(const int32_t* flag, void* stream) {
   NC_CHECK_HIP(hipMemcpyAsync(&h, flag, sizeof(h), hipMemcpyDeviceToHost, s));
   NC_CHECK_HIP(hipStreamSynchronize(s));
   if (h != 0) return nc::set_error(NC_ERR_DEVICE_FLAG, "device flag raised: a token id was outside [0, V)");
-  return NC_OK;
+  return nc::api_done(NC_OK, stream, "nc_sync_status");
 }

@@ -268,7 +268,8 @@ int mqa_attn_bwd(const void* qkv, const void* o, const void* dout, const float* 
 
 extern "C" int nc_mqa_attn_fwd(const void* qkv, int dtype, int B, int T, int H, int hd, float scale, void* o,
                                float* lse, void* stream) {
-  return nc::mqa_attn_fwd(qkv, dtype, B, T, H, hd, scale, o, lse, static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::mqa_attn_fwd(qkv, dtype, B, T, H, hd, scale, o, lse, static_cast<hipStream_t>(stream)),
+                      stream, "nc_mqa_attn_fwd");
 }
 
 extern "C" size_t nc_mqa_attn_bwd_workspace_bytes(int B, int T, int H) {
@@ -278,6 +279,6 @@ extern "C" size_t nc_mqa_attn_bwd_workspace_bytes(int B, int T, int H) {
 extern "C" int nc_mqa_attn_bwd(const void* qkv, const void* o, const void* dout, const float* lse, int dtype, int B,
                                int T, int H, int hd, float scale, float* dqkv_hat, void* ws, size_t ws_bytes,
                                void* stream) {
-  return nc::mqa_attn_bwd(qkv, o, dout, lse, dtype, B, T, H, hd, scale, dqkv_hat, ws, ws_bytes,
-                          static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::mqa_attn_bwd(qkv, o, dout, lse, dtype, B, T, H, hd, scale, dqkv_hat, ws, ws_bytes,
+                          static_cast<hipStream_t>(stream)), stream, "nc_mqa_attn_bwd");
 }

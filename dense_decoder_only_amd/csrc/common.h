@@ -63,6 +63,12 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ---------------------------------------------------------------------------
 int set_error(int code, const char* fmt, ...);
 int check_launch(const char* what);
+// Debug mode (environment variable NC_DEBUG=1, read once per process): every
+// entry point that takes a stream synchronizes it before returning and
+// reports any HIP error it finds, so that a failing kernel is named by the
+// call that launched it.  Not for use under stream capture.
+bool debug_mode();
+int api_done(int rc, void* stream, const char* name);
 // Kernel timer hooks (nc_probe_*): cheap no-ops unless `family` is armed.
 void probe_begin(int family, hipStream_t s);
 void probe_end(int family, hipStream_t s, double flops);

@@ -293,5 +293,6 @@ extern "C" size_t nc_embed_bwd_workspace_bytes(int64_t n, int64_t V, int d) {
 
 extern "C" int nc_embed_bwd(const int32_t* ids, int64_t n, const float* de, int d, float* dtable, int64_t V,
                             int accumulate, void* ws, size_t ws_bytes, void* stream) {
-  return nc::embed_bwd(ids, n, de, d, dtable, V, accumulate, ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::embed_bwd(ids, n, de, d, dtable, V, accumulate, ws, ws_bytes, static_cast<hipStream_t>(stream)),
+                      stream, "nc_embed_bwd");
 }

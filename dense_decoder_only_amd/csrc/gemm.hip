@@ -1493,7 +1493,7 @@ extern "C" int nc_gemm_bf16(int transA, int transB, int64_t M, int64_t N, int64_
   g.dtype = dtype;
   g.ws = ws;
   g.ws_bytes = ws_bytes;
-  return nc::gemm(g, static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::gemm(g, static_cast<hipStream_t>(stream)), stream, "nc_gemm_bf16");
 }
 
 // ---------------------------------------------------------------------------

@@ -717,14 +717,15 @@ extern "C" size_t nc_infer_workspace_bytes(const nc_config* cfg, int max_len) {
 
 extern "C" int nc_prefill(const nc_config* cfg, const nc_params* params, const int32_t* ids, void* kv_cache,
                           int max_len, float* logits, void* ws, size_t ws_bytes, void* stream) {
-  return nc::prefill(cfg, params, ids, kv_cache, max_len, logits, ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::prefill(cfg, params, ids, kv_cache, max_len, logits, ws, ws_bytes, static_cast<hipStream_t>(stream)),
+                      stream, "nc_prefill");
 }
 
 extern "C" int nc_decode_step(const nc_config* cfg, const nc_params* params, const int32_t* ids,
                               const int32_t* pos, void* kv_cache, int max_len, float* logits, void* ws,
                               size_t ws_bytes, void* stream) {
-  return nc::decode_step(cfg, params, ids, pos, kv_cache, max_len, logits, ws, ws_bytes,
-                         static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::decode_step(cfg, params, ids, pos, kv_cache, max_len, logits, ws, ws_bytes,
+                         static_cast<hipStream_t>(stream)), stream, "nc_decode_step");
 }
 
 // Scratch of nc_mqa_decode_attn_noalloc: the chunk partials (fp32 outputs,
@@ -771,8 +772,8 @@ extern "C" int nc_mqa_decode_attn(const void* q, const void* k_cache, const void
   const size_t parts = (size_t)B * nc::cdiv(max_len, 64) * H;
   float* part_o = static_cast<float*>(ws);
   float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + nc::align_up(parts * 128 * 4, 256));
-  return nc::mqa_decode_attn(q, k_cache, v_cache, lens, 0, B, H, hd, max_len, scale, o, part_o, part_ml,
-                             static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::mqa_decode_attn(q, k_cache, v_cache, lens, 0, B, H, hd, max_len, scale, o, part_o, part_ml,
+                             static_cast<hipStream_t>(stream)), stream, "nc_mqa_decode_attn");
 }
 
 extern "C" int nc_mqa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
@@ -788,6 +789,6 @@ extern "C" int nc_mqa_decode_attn_noalloc(const void* q, const void* k_cache, co
   const size_t parts = (size_t)B * nc::cdiv(max_len, 64) * H;
   float* part_o = static_cast<float*>(ws);
   float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + nc::align_up(parts * 128 * 4, 256));
-  return nc::mqa_decode_attn(q, k_cache, v_cache, lens, 0, B, H, hd, max_len, scale, o, part_o, part_ml,
-                             static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::mqa_decode_attn(q, k_cache, v_cache, lens, 0, B, H, hd, max_len, scale, o, part_o, part_ml,
+                             static_cast<hipStream_t>(stream)), stream, "nc_mqa_decode_attn_noalloc");
 }

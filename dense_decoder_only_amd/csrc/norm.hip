@@ -268,16 +268,18 @@ int embed_fwd(const int32_t* ids, int64_t n, const void* table, int dtype, int64
 
 extern "C" int nc_rmsnorm_fwd(const void* x, int xdt, int64_t rows, int d, float eps, void* y, int ydt,
                               float* rstd, void* stream) {
-  return nc::rmsnorm_fwd(x, xdt, rows, d, eps, y, ydt, rstd, static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::rmsnorm_fwd(x, xdt, rows, d, eps, y, ydt, rstd, static_cast<hipStream_t>(stream)),
+                      stream, "nc_rmsnorm_fwd");
 }
 
 extern "C" int nc_rmsnorm_bwd(const void* dy, int dydt, const void* y, int ydt, const float* rstd, int64_t rows,
                               int d, float* dx, int accumulate, void* dx_bf16, void* stream) {
-  return nc::rmsnorm_bwd(dy, dydt, y, ydt, rstd, rows, d, dx, accumulate, dx_bf16, static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::rmsnorm_bwd(dy, dydt, y, ydt, rstd, rows, d, dx, accumulate, dx_bf16, static_cast<hipStream_t>(stream)),
+                      stream, "nc_rmsnorm_bwd");
 }
 
 extern "C" int nc_embed_fwd(const int32_t* ids, int64_t n, const void* table, int dtype, int64_t V, int d,
                             void* rows_out, float* x_out, float* rstd, float eps, int32_t* flag, void* stream) {
-  return nc::embed_fwd(ids, n, table, dtype, V, d, rows_out, x_out, rstd, eps, flag,
-                       static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::embed_fwd(ids, n, table, dtype, V, d, rows_out, x_out, rstd, eps, flag,
+                       static_cast<hipStream_t>(stream)), stream, "nc_embed_fwd");
 }

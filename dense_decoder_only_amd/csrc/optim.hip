@@ -122,6 +122,7 @@ int adamw_step(float* P, float* M, float* V, const float* G, void* W, int64_t n,
 extern "C" int nc_adamw_step(float* master, float* m, float* v, const float* grad, void* weights_lp, int64_t n,
                              int t, float lr, float beta1, float beta2, float eps, float weight_decay,
                              float grad_scale, void* stream) {
-  return nc::adamw_step(master, m, v, grad, weights_lp, n, t, lr, beta1, beta2, eps, weight_decay, grad_scale,
-                        static_cast<hipStream_t>(stream));
+
+                       return nc::api_done(nc::adamw_step(master, m, v, grad, weights_lp, n, t, lr, beta1, beta2, eps, weight_decay, grad_scale,
+                        static_cast<hipStream_t>(stream)), stream, "nc_adamw_step");
 }

@@ -255,17 +255,18 @@ int rope_qknorm_bwd(const float* dhat, const void* yhat, const float* rstd_q, co
 }  // namespace nc
 
 extern "C" int nc_rope_table(float* table, int T, int hd, float base, void* stream) {
-  return nc::rope_table(table, T, hd, base, static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::rope_table(table, T, hd, base, static_cast<hipStream_t>(stream)), stream, "nc_rope_table");
 }
 
 extern "C" int nc_rope_qknorm_fwd(void* qkv, int dtype, int B, int T, int H, int hd, const float* table, float eps,
                                   float* rstd_q, float* rstd_k, void* stream) {
-  return nc::rope_qknorm_fwd(qkv, dtype, B, T, H, hd, table, eps, rstd_q, rstd_k, static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::rope_qknorm_fwd(qkv, dtype, B, T, H, hd, table, eps, rstd_q, rstd_k, static_cast<hipStream_t>(stream)),
+                      stream, "nc_rope_qknorm_fwd");
 }
 
 extern "C" int nc_rope_qknorm_bwd(const float* dqkv_hat, const void* qkv_hat, const float* rstd_q,
                                   const float* rstd_k, const float* table, int dtype, int B, int T, int H, int hd,
                                   void* dqkv, void* stream) {
-  return nc::rope_qknorm_bwd(dqkv_hat, qkv_hat, rstd_q, rstd_k, table, dtype, B, T, H, hd, dqkv,
-                             static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::rope_qknorm_bwd(dqkv_hat, qkv_hat, rstd_q, rstd_k, table, dtype, B, T, H, hd, dqkv,
+                             static_cast<hipStream_t>(stream)), stream, "nc_rope_qknorm_bwd");
 }

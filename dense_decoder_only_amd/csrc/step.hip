@@ -443,19 +443,21 @@ extern "C" size_t nc_step_workspace_bytes(const nc_config* cfg) { return nc::ste
 extern "C" int nc_step_fwd_bwd(const nc_config* cfg, const nc_params* params, const nc_grads* grads,
                                const int32_t* ids, const int32_t* targets, const float* token_bytes, void* ws,
                                size_t ws_bytes, float* loss, float* bpb, float* loss_tok, void* stream) {
-  return nc::step_fwd_bwd(cfg, params, grads, ids, targets, token_bytes, ws, ws_bytes, loss, bpb, loss_tok,
-                          static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::step_fwd_bwd(cfg, params, grads, ids, targets, token_bytes, ws, ws_bytes, loss, bpb, loss_tok,
+                          static_cast<hipStream_t>(stream)), stream, "nc_step_fwd_bwd");
 }
 
 extern "C" int nc_relu2_mlp(const void* m, const void* w_fc, const void* w_proj, int dtype, int64_t M, int d, int F,
                             float* x, void* u_out, void* a2_out, void* stream) {
-  return nc::relu2_mlp(m, w_fc, w_proj, dtype, M, d, F, x, u_out, a2_out, static_cast<hipStream_t>(stream));
+  return nc::api_done(nc::relu2_mlp(m, w_fc, w_proj, dtype, M, d, F, x, u_out, a2_out, static_cast<hipStream_t>(stream)),
+                      stream, "nc_relu2_mlp");
 }
 
 extern "C" int nc_relu2_mlp_bwd(const void* g_lp, const void* m, const void* u, const void* a2, const void* w_fc,
                                 const void* w_proj, int dtype, int64_t M, int d, int F, float* dm, float* dw_fc,
                                 float* dw_proj, int accumulate, void* du_buf, void* ws, size_t ws_bytes,
                                 void* stream) {
-  return nc::relu2_mlp_bwd(g_lp, m, u, a2, w_fc, w_proj, dtype, M, d, F, dm, dw_fc, dw_proj, accumulate, du_buf, ws,
-                           ws_bytes, static_cast<hipStream_t>(stream));
+
+                       return nc::api_done(nc::relu2_mlp_bwd(g_lp, m, u, a2, w_fc, w_proj, dtype, M, d, F, dm, dw_fc, dw_proj, accumulate, du_buf, ws,
+                           ws_bytes, static_cast<hipStream_t>(stream)), stream, "nc_relu2_mlp_bwd");
 }

@@ -443,13 +443,15 @@ extern "C" size_t nc_softcap_xent_workspace_bytes(int64_t M, int d, int V) { ret
 extern "C" int nc_softcap_xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt,
                                    const float* token_bytes, int64_t M, int d, int V, float softcap, float* lse,
                                    float* loss_tok, float* loss, float* bpb, void* ws, size_t ws_bytes, void* stream) {
-  return nc::xent_fwd(h, U, dtype, tgt, token_bytes, M, d, V, softcap, lse, loss_tok, loss, bpb, ws, ws_bytes,
-                      static_cast<hipStream_t>(stream));
+
+                       return nc::api_done(nc::xent_fwd(h, U, dtype, tgt, token_bytes, M, d, V, softcap, lse, loss_tok, loss, bpb, ws, ws_bytes,
+                      static_cast<hipStream_t>(stream)), stream, "nc_softcap_xent_fwd");
 }
 
 extern "C" int nc_softcap_xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* lse,
                                    int64_t M, int d, int V, float softcap, float dloss, float* dh, int dh_accumulate,
                                    float* dU, int dU_accumulate, void* ws, size_t ws_bytes, void* stream) {
-  return nc::xent_bwd(h, U, dtype, tgt, lse, M, d, V, softcap, dloss, dh, dh_accumulate, dU, dU_accumulate, ws,
-                      ws_bytes, static_cast<hipStream_t>(stream));
+
+                       return nc::api_done(nc::xent_bwd(h, U, dtype, tgt, lse, M, d, V, softcap, dloss, dh, dh_accumulate, dU, dU_accumulate, ws,
+                      ws_bytes, static_cast<hipStream_t>(stream)), stream, "nc_softcap_xent_bwd");
 }

@@ -51,6 +51,7 @@ class nc_grads(ctypes.Structure):
 _SIGS = {
     "nc_last_error": (ctypes.c_char_p, []),
     "nc_version": (ctypes.c_char_p, []),
+    "nc_debug_mode": (ctypes.c_int, []),
     "nc_sync_status": (c_int, [c_p, c_p]),
     "nc_adamw_step": (c_int, [c_p, c_p, c_p, c_p, c_p, c_i64, c_int, c_f, c_f, c_f, c_f, c_f, c_f, c_p]),
     "nc_probe_start": (c_int, [c_int, c_int]),
@@ -153,6 +154,10 @@ def make_config(cfg) -> nc_config:
 
 def nc_version() -> str:
     return load().nc_version().decode()
+
+
+def nc_debug_mode() -> bool:
+    return bool(load().nc_debug_mode())
 
 
 def nc_last_error() -> str:

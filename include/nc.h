@@ -109,6 +109,14 @@ const char* nc_last_error(void);
 /* Library version string. Static storage. */
 const char* nc_version(void);
 
+/* 1 if debug mode is on, else 0.  Debug mode is switched on by the
+ * environment variable NC_DEBUG=1, read once per process: every entry point
+ * that takes a stream then synchronizes that stream before it returns and
+ * returns NC_ERR_HIP (with the HIP error in nc_last_error) if a kernel of the
+ * call, or anything queued before it, failed.  It must not be used while the
+ * stream is being captured into a graph. */
+int nc_debug_mode(void);
+
 /* Synchronizes `stream`, then reads the int32 device flag at `flag`.
  * Returns NC_ERR_DEVICE_FLAG if it is nonzero, NC_OK otherwise.  The step's
  * flag is the first int32 of its workspace. */

@@ -126,3 +126,40 @@ def test_inference_size_queries_and_validation():
     assert rc == nc.NC_ERR_UNSUPPORTED
     rc = lib.nc_mqa_decode_attn(fake, fake, fake, fake, 2, 10, 128, 64, 0.1, fake, fake, 16, None)
     assert rc == nc.NC_ERR_WORKSPACE
+
+
+def _debug_mode_in_child(env_value):
+    """nc_debug_mode() and a host-rejected call in a fresh process (the switch is read once per process)."""
+    import subprocess
+    import sys
+    code = ("import ctypes, sys; sys.path.insert(0, %r); from dense_decoder_only_amd import nc; lib = nc.load(); "
+            "rc = lib.nc_gemm_bf16(0, 1, 256, 256, 256, None, 256, None, 256, None, nc.NC_F32, 256, 0.0, "
+            "nc.NC_EPI_STORE, None, None, nc.NC_BF16, None, 0, None); "
+            "print(lib.nc_debug_mode(), rc == nc.NC_ERR_INVALID_ARG)" % ROOT)
+    env = dict(os.environ)
+    env.pop("NC_DEBUG", None)
+    if env_value is not None:
+        env["NC_DEBUG"] = env_value
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    return out.stdout.split()
+
+
+def test_debug_mode_follows_the_environment():
+    assert _debug_mode_in_child(None) == ["0", "True"]
+    assert _debug_mode_in_child("0") == ["0", "True"]
+    # on: argument errors are still reported as such (nothing was enqueued to check)
+    assert _debug_mode_in_child("1") == ["1", "True"]
+
+
+def test_noalloc_decode_attention_host_validation():
+    from dense_decoder_only_amd import nc
+    lib = nc.load()
+    fake = ctypes.c_void_p(256)
+    # 128 sequences x 32 heads x 4096 positions need more partials than the fixed scratch holds
+    assert nc.nc_mqa_decode_workspace_bytes(128, 32, 4096) > 16 << 20
+    rc = lib.nc_mqa_decode_attn_noalloc(fake, fake, fake, fake, 128, 32, 128, 4096, 0.1, fake, None)
+    assert rc == nc.NC_ERR_WORKSPACE and "scratch" in nc.nc_last_error()
+    # unsupported shape: rejected before any scratch is touched
+    rc = lib.nc_mqa_decode_attn_noalloc(fake, fake, fake, fake, 0, 32, 128, 4096, 0.1, fake, None)
+    assert rc != nc.NC_OK

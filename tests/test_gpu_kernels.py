@@ -478,3 +478,26 @@ def test_softcap_xent_two_vocab_chunks():
     assert abs(lhs - rhs) <= 1e-4 * max(abs(rhs), 1e-30), (lhs, rhs)
     per_chunk = [float(np.sum(U64[a:b] * dU64[a:b])) for a, b in ((0, 65536), (65536, V))]
     assert all(np.isfinite(per_chunk)) and abs(per_chunk[1]) > 0.0
+
+
+def test_debug_mode_checks_each_call():
+    """NC_DEBUG=1 (read once per process, so in a child): calls synchronize and still return NC_OK with the same
+    result as a library matmul."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys, torch; sys.path.insert(0, %r); from dense_decoder_only_amd import nc; nc.load(); "
+        "assert nc.nc_debug_mode(); g = torch.Generator().manual_seed(5); "
+        "A = torch.randn(296, 256, generator=g).to(torch.bfloat16).cuda(); "
+        "B = torch.randn(264, 256, generator=g).to(torch.bfloat16).cuda(); C = torch.empty(296, 264, device='cuda'); "
+        "nc.nc_gemm_bf16(0, 1, 296, 264, 256, A, 256, B, 256, C, 264); "
+        "ref = A.double().cpu() @ B.double().cpu().T; err = ((C.double().cpu() - ref).abs().max() / ref.abs().max()).item(); "
+        "print('ok', err)" % root)
+    env = dict(os.environ, NC_DEBUG="1")
+    print("[debug-mode child] 296x264x256 GEMM with NC_DEBUG=1", flush=True)
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=100)
+    assert out.returncode == 0, out.stderr[-2000:]
+    word, err = out.stdout.split()[-2:]
+    assert word == "ok" and float(err) < 1e-5
