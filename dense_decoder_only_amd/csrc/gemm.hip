@@ -122,11 +122,16 @@ __device__ __forceinline__ float row16_sum(float s) {
 
 // Forward cross-entropy epilogue: a 16-lane group (one DPP row) holds one
 // row's 64 columns (4 per lane); every lane of the group must call this.  y is
-// the row's target column relative to xv0 (-1 for rows past M).  With
-// th = tanh(z / c) = sign(z) (1 - t) / (1 + t), t = e^{-2|z|/c}, the capped
-// logit is c th, exp(c th - c) = 2^{(th - 1) c log2(e)}, and the stored code
-// is round(32767 th).
-__device__ __forceinline__ void xent_fwd4(const MfmaParams& p, float4 v, int row, int col, int gcol64, int y) {
+// the row's target column relative to xv0 (-1 for rows past M); code points
+// at the row's stored code for column col (unused when p.C is null: no codes
+// are stored).
+// With th = tanh(z / c) = sign(z) (1 - t) / (1 + t), t = e^{-2|z|/c}, the
+// capped logit is c th, exp(c th - c) = 2^{(th - 1) c log2(e)}, and the stored
+// code is th in signed 16-bit normalized form, round(32767 th), from one
+// v_cvt_pknorm_i16_f32 per two columns (it rounds exact ties away from zero;
+// either way the code is within half a step of 32767 th).
+__device__ __forceinline__ void xent_fwd4(const MfmaParams& p, float4 v, int row, int col, int gcol64, int y,
+                                          int16_t* code) {
   const bool ok = row < p.M;
   const bool in = col < p.N;  // N is a multiple of 8: the 4 columns are all in range or none is
   const float zz[4] = {v.x, v.y, v.z, v.w};
@@ -143,10 +148,10 @@ __device__ __forceinline__ void xent_fwd4(const MfmaParams& p, float4 v, int row
   const unsigned d = (unsigned)(y - col);
   if (ok && in && d < 4u) p.xztgt[row] = p.xc * (d == 0 ? th[0] : d == 1 ? th[1] : d == 2 ? th[2] : th[3]);
   if (p.C && ok && in) {
-    const int q0 = __float2int_rn(th[0] * 32767.f), q1 = __float2int_rn(th[1] * 32767.f);
-    const int q2 = __float2int_rn(th[2] * 32767.f), q3 = __float2int_rn(th[3] * 32767.f);
-    *reinterpret_cast<uint2*>(static_cast<int16_t*>(p.C) + (int64_t)row * p.ldc + col) =
-        make_uint2((uint32_t)(q0 & 0xffff) | ((uint32_t)q1 << 16), (uint32_t)(q2 & 0xffff) | ((uint32_t)q3 << 16));
+    typedef short short2_t __attribute__((ext_vector_type(2)));
+    const short2_t lo = __builtin_amdgcn_cvt_pknorm_i16(th[0], th[1]);
+    const short2_t hi = __builtin_amdgcn_cvt_pknorm_i16(th[2], th[3]);
+    *reinterpret_cast<uint2*>(code) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
   }
   s = row16_sum(s);
   if (ok && (threadIdx.x & 15) == 0 && gcol64 < p.N)
@@ -1129,6 +1134,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // land before the reads (no block barrier, whose fence would also wait for
     // the previous slab's global stores)
     wave_lds_sync();
+    // stored codes of the cross-entropy epilogue: this lane's element of
+    // iteration it is 4 rows further than that of it - 1
+    int16_t* code = nullptr;
+    if constexpr (EPI == E_XENT_FWD)
+      code = static_cast<int16_t*>(p.C) + (int64_t)(m0 + wm * 128 + i * 32 + (lane >> 4)) * p.ldc + n0 + wn * 64 +
+             (lane & 15) * 4;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int idx = it * 64 + lane;
@@ -1136,7 +1147,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float4 v = *reinterpret_cast<const float4*>(stage + row * SROW + c4);
       const int grow = m0 + wm * 128 + i * 32 + row, gcol = n0 + wn * 64 + c4;
       if constexpr (EPI == E_XENT_FWD) {
-        xent_fwd4(p, v, grow, gcol, n0 + wn * 64, s_xt[grow - m0]);
+        xent_fwd4(p, v, grow, gcol, n0 + wn * 64, s_xt[grow - m0], code);
+        code += 4 * p.ldc;
       } else if (grow < p.M && gcol < p.N) {
         const int64_t off = (int64_t)grow * p.ldc + gcol;
         if constexpr (EPI == E_XENT_BWD) {
