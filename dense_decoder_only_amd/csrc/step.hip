@@ -326,6 +326,10 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
   // In bf16 the activation gradients dX = dY W use the transposed weights so
   // that every product runs in the K-contiguous (x W^T) form.
   const bool tw = dt == NC_BF16;
+  // The gradients w.r.t. the pre-attention and pre-MLP norm outputs (products
+  // of bf16 operands) are stored in the config dtype: the norm backward reads
+  // them once, and in bf16 that halves their write and read.
+  const int dyt = dt == NC_BF16 ? NC_BF16 : NC_F32;
   char* wt = static_cast<char*>(w.wt);
   void* WqkvT = wt;
   void* WoT = wt + (size_t)Q * d * e;
@@ -364,10 +368,10 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
     NC_TRY(wgrad(mk(1, 0, F, d, M, du, F, ly.m, d, gr->w_fc + (size_t)l * F * d, NC_F32, d, dt)));
     NC_TRY(mark_read(B_DU, uv));
     ++uv;
-    NC_TRY(gemm(tw ? mk(0, 1, M, d, F, du, F, W1T, F, w.dm, NC_F32, d, dt) : mk(0, 0, M, d, F, du, F, W1, d, w.dm, NC_F32, d, dt), s));
+    NC_TRY(gemm(tw ? mk(0, 1, M, d, F, du, F, W1T, F, w.dm, dyt, d, dt) : mk(0, 0, M, d, F, du, F, W1, d, w.dm, dyt, d, dt), s));
     ++gv;
     NC_TRY(reuse(B_G, gv));
-    NC_TRY(rmsnorm_bwd(w.dm, NC_F32, ly.m, dt, ly.rstd_m, M, (int)d, g, 1, glp_out(gv), s));
+    NC_TRY(rmsnorm_bwd(w.dm, dyt, ly.m, dt, ly.rstd_m, M, (int)d, g, 1, glp_out(gv), s));
     // attention: x_mid = x_in + mqa(...) Wo^T
     gop = gop_of(gv);
     NC_TRY(fork());
@@ -390,10 +394,10 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
     NC_TRY(wgrad(mk(1, 0, Q, d, M, dqkv, Q, ly.a, d, gr->w_qkv + (size_t)l * Q * d, NC_F32, d, dt)));
     NC_TRY(mark_read(B_DQ, qv));
     ++qv;
-    NC_TRY(gemm(tw ? mk(0, 1, M, d, Q, dqkv, Q, WqkvT, Q, w.dm, NC_F32, d, dt) : mk(0, 0, M, d, Q, dqkv, Q, Wqkv, d, w.dm, NC_F32, d, dt), s));
+    NC_TRY(gemm(tw ? mk(0, 1, M, d, Q, dqkv, Q, WqkvT, Q, w.dm, dyt, d, dt) : mk(0, 0, M, d, Q, dqkv, Q, Wqkv, d, w.dm, dyt, d, dt), s));
     ++gv;
     NC_TRY(reuse(B_G, gv));
-    NC_TRY(rmsnorm_bwd(w.dm, NC_F32, ly.a, dt, ly.rstd_a, M, (int)d, g, 1, glp_out(gv), s));
+    NC_TRY(rmsnorm_bwd(w.dm, dyt, ly.a, dt, ly.rstd_a, M, (int)d, g, 1, glp_out(gv), s));
   }
   NC_TRY(join());
   // embedding norm and scatter-add
