@@ -69,6 +69,14 @@ def test_rmsnorm_fwd_bwd(dtype, rows, d):
     n.nc_rmsnorm_bwd(gg, y, rstd, dx2, accumulate=1)
     sync()
     assert_close(dev_to_f64(dx2), 2 * dev_to_f64(dx), 1e-6, 0, "rmsnorm dx accumulate")
+    if dtype == BF16:
+        # the training step's form: the incoming gradient in bf16 as well
+        gb = to_dev(g, BF16)
+        dx3 = torch.empty(rows, d, dtype=F32, device=DEV)
+        n.nc_rmsnorm_bwd(gb, y, rstd, dx3, accumulate=0)
+        sync()
+        ref3 = oracle.rms_norm_bwd(dev_to_f64(gb), dev_to_f64(y), dev_to_f64(rstd)[:, None])
+        assert_close(dev_to_f64(dx3), ref3, 1e-5, 1e-6, "rmsnorm dx (bf16 gradient)")
 
 
 # ---------------------------------------------------------------- embedding --
