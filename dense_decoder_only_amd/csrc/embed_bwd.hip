@@ -121,29 +121,63 @@ __global__ void colscan_kernel(int32_t* __restrict__ hist, int64_t C, int64_t V,
   }
 }
 
-// Exclusive scan of in[0, n) into out[0, n]; out[n] = total.  One block.
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ in, int64_t n,
-                                                    int32_t* __restrict__ out) {
-  __shared__ int32_t part[1024];
-  const int tid = threadIdx.x;
-  const int64_t per = cdiv(n, 1024);
-  const int64_t b = tid * per, e = std::min<int64_t>(n, b + per);
-  int32_t s = 0;
-  for (int64_t i = b; i < e; ++i) s += in[i];
-  part[tid] = s;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
-    const int32_t v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+// Exclusive scans of in[k][0, n) into out[k][0, n], out[k][n] = total, one
+// 1024-thread block per array k.  The input is taken in spans of 64 Ki
+// elements: every thread first issues all 64 of its loads of a span (tile j,
+// elements j*4096 + 4*tid .. +3), then the 16 tiles are scanned in order with
+// a wavefront shuffle scan and one barrier per tile.
+struct Scan3 {
+  const int32_t* in[3];
+  int32_t* out[3];
+};
+
+__global__ __launch_bounds__(1024) void scan_kernel(Scan3 a, int64_t n) {
+  constexpr int TILE = 4096, NT = 16;
+  __shared__ int32_t wsum[2][16];
+  const int32_t* __restrict__ in = a.in[blockIdx.x];
+  int32_t* __restrict__ out = a.out[blockIdx.x];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int32_t carry = 0;
+  int buf = 0;
+  for (int64_t base = 0; base < n; base += (int64_t)TILE * NT) {
+    int32_t v[NT][4];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t i = base + (int64_t)j * TILE + tid * 4 + q;
+        v[j][q] = i < n ? in[i] : 0;
+      }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int32_t t = v[j][0] + v[j][1] + v[j][2] + v[j][3];
+      int32_t x = t;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (lane == 63) wsum[buf][wid] = x;
+      __syncthreads();
+      int32_t pre = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        const int32_t ws = wsum[buf][w];
+        pre += w < wid ? ws : 0;
+        tot += ws;
+      }
+      int32_t run = carry + pre + x - t;
+      const int64_t i0 = base + (int64_t)j * TILE + tid * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (i0 + q < n) out[i0 + q] = run;
+        run += v[j][q];
+      }
+      carry += tot;
+      buf ^= 1;  // the next tile writes the other buffer, so one barrier per tile suffices
+    }
   }
-  int32_t run = tid ? part[tid - 1] : 0;
-  for (int64_t i = b; i < e; ++i) {
-    out[i] = run;
-    run += in[i];
-  }
-  if (tid == 1023) out[n] = part[1023];
+  if (tid == 0) out[n] = carry;
 }
 
 __global__ void place_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t V, const int32_t* __restrict__ rank,
@@ -204,6 +238,9 @@ __global__ __launch_bounds__(256) void piece_sum_kernel(const float* __restrict_
   }
 }
 
+// One wavefront per (id, 256-column chunk): the head ids have over a hundred
+// pieces, so the chunks of one row go to separate waves, and the loads of 8
+// pieces are issued together before they are added in piece order.
 __global__ __launch_bounds__(256) void finish_kernel(const int32_t* __restrict__ count,
                                                      const int32_t* __restrict__ npieces,
                                                      const int32_t* __restrict__ ppoff,
@@ -211,27 +248,38 @@ __global__ __launch_bounds__(256) void finish_kernel(const int32_t* __restrict__
                                                      float* __restrict__ dtable, int accumulate) {
   const int lane = threadIdx.x & 63;
   const int64_t v = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (v >= V) return;
+  const int c = (int)blockIdx.y * 256 + lane * 4;
+  if (v >= V || c >= d) return;
   const int32_t np = npieces[v];
   if (np == 1) return;  // written by piece_sum_kernel
-  float* dst = dtable + v * d;
+  float4* dst = reinterpret_cast<float4*>(dtable + v * d + c);
   if (count[v] == 0) {
-    if (!accumulate)
-      for (int c = lane * 4; c < d; c += 256) *reinterpret_cast<float4*>(dst + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!accumulate) *dst = make_float4(0.f, 0.f, 0.f, 0.f);
     return;
   }
-  const float* src = partial + (int64_t)ppoff[v] * d;
-  for (int c = lane * 4; c < d; c += 256) {
-    float4 s = accumulate ? *reinterpret_cast<const float4*>(dst + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int32_t p = 0; p < np; ++p) {
-      const float4 x = *reinterpret_cast<const float4*>(src + (int64_t)p * d + c);
-      s.x += x.x;
-      s.y += x.y;
-      s.z += x.z;
-      s.w += x.w;
+  const float* src = partial + (int64_t)ppoff[v] * d + c;
+  float4 s = accumulate ? *dst : make_float4(0.f, 0.f, 0.f, 0.f);
+  int32_t p = 0;
+  for (; p + 8 <= np; p += 8) {
+    float4 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const float4*>(src + (int64_t)(p + u) * d);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      s.x += x[u].x;
+      s.y += x[u].y;
+      s.z += x[u].z;
+      s.w += x[u].w;
     }
-    *reinterpret_cast<float4*>(dst + c) = s;
   }
+  for (; p < np; ++p) {
+    const float4 x = *reinterpret_cast<const float4*>(src + (int64_t)p * d);
+    s.x += x.x;
+    s.y += x.y;
+    s.z += x.z;
+    s.w += x.w;
+  }
+  *dst = s;
 }
 
 }  // namespace
@@ -265,9 +313,8 @@ int embed_bwd(const int32_t* ids, int64_t n, const float* de, int d, float* dtab
   const unsigned vb = (unsigned)std::min<int64_t>(cdiv(V, 256), 4096);
   colscan_kernel<<<vb, 256, 0, s>>>(w.hist, C, V, w.count, w.npieces, w.nmulti);
   NC_TRY(check_launch("colscan_kernel"));
-  scan_kernel<<<1, 1024, 0, s>>>(w.count, V, w.offset);
-  scan_kernel<<<1, 1024, 0, s>>>(w.npieces, V, w.poff);
-  scan_kernel<<<1, 1024, 0, s>>>(w.nmulti, V, w.ppoff);
+  Scan3 sc{{w.count, w.npieces, w.nmulti}, {w.offset, w.poff, w.ppoff}};
+  scan_kernel<<<3, 1024, 0, s>>>(sc, V);
   NC_TRY(check_launch("scan_kernel"));
   if (n > 0) {
     place_kernel<<<(unsigned)std::min<int64_t>(cdiv(n, 256), 4096), 256, 0, s>>>(ids, n, V, w.rank, w.hist, w.offset,
@@ -281,7 +328,7 @@ int embed_bwd(const int32_t* ids, int64_t n, const float* de, int d, float* dtab
                                                             w.ppoff, w.piece_v, V, w.partial, dtable, accumulate);
     NC_TRY(check_launch("piece_sum_kernel"));
   }
-  finish_kernel<<<(unsigned)cdiv(V, 4), 256, 0, s>>>(w.count, w.npieces, w.ppoff, w.partial, V, d, dtable, accumulate);
+  finish_kernel<<<dim3((unsigned)cdiv(V, 4), (unsigned)cdiv(d, 256)), 256, 0, s>>>(w.count, w.npieces, w.ppoff, w.partial, V, d, dtable, accumulate);
   return check_launch("finish_kernel");
 }
 

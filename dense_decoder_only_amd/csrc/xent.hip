@@ -135,8 +135,18 @@ __global__ void xent_finish_kernel(const float* __restrict__ partial, int nch, i
                                    const float* __restrict__ ztgt, float* __restrict__ lse,
                                    float* __restrict__ ltok_ws, float* __restrict__ loss_tok) {
   for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < M; r += (int64_t)gridDim.x * blockDim.x) {
+    // Sequential sum over the parts; the loads of 16 parts are issued
+    // together so one wave per SIMD keeps enough reads in flight.
     float s = 0.f;
-    for (int k = 0; k < nch; ++k) s += partial[(int64_t)k * M + r];
+    int k = 0;
+    for (; k + 16 <= nch; k += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = partial[(int64_t)(k + u) * M + r];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) s += v[u];
+    }
+    for (; k < nch; ++k) s += partial[(int64_t)k * M + r];
     const float L = c + logf(s);
     lse[r] = L;
     const float lt = L - ztgt[r];

@@ -116,7 +116,7 @@ def test_embed_fwd_flags_out_of_range_ids():
     assert torch.equal(rows[4], table[63])
 
 
-@pytest.mark.parametrize("n_tok,V,d", [(5000, 1000, 264), (1, 16, 128), (70000, 65536, 128)])
+@pytest.mark.parametrize("n_tok,V,d", [(5000, 1000, 264), (1, 16, 128), (70000, 65536, 128), (20000, 131075, 8)])
 def test_embed_bwd_matches_scatter_add(n_tok, V, d):
     n = nc()
     r = rng(n_tok + V)
