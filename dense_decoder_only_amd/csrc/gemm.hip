@@ -81,6 +81,29 @@ constexpr float kLog2e = 1.4426950408889634f;
 // moves no memory access across this point.  Global stores stay in flight.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Non-temporal (streaming) global accesses, for the epilogues' outputs and
+// their read-once inputs: every CU writes its tile at about the same time, and
+// as ordinary stores those tens of MB displaced the operand panels that the
+// next tiles read from L2.
+typedef float ntf4 __attribute__((ext_vector_type(4)));
+typedef unsigned ntu2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_nt(float* p, float4 v) {
+  const ntf4 t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<ntf4*>(p));
+}
+__device__ __forceinline__ void st_nt(bf16* p, uint2 v) {
+  const ntu2 t = {v.x, v.y};
+  __builtin_nontemporal_store(t, reinterpret_cast<ntu2*>(p));
+}
+__device__ __forceinline__ float4 ld_nt(const float* p) {
+  const ntf4 t = __builtin_nontemporal_load(reinterpret_cast<const ntf4*>(p));
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ uint2 ld_nt(const bf16* p) {
+  const ntu2 t = __builtin_nontemporal_load(reinterpret_cast<const ntu2*>(p));
+  return make_uint2(t.x, t.y);
+}
+
 // c tanh(z / c) from one hardware exp2 and reciprocal:
 // tanh|x| = (1 - e^{-2|x|}) / (1 + e^{-2|x|}).
 __device__ __forceinline__ float softcap_of(float z, float c, float inv_c) {
@@ -151,7 +174,8 @@ __device__ __forceinline__ void xent_fwd4(const MfmaParams& p, float4 v, int row
     typedef short short2_t __attribute__((ext_vector_type(2)));
     const short2_t lo = __builtin_amdgcn_cvt_pknorm_i16(th[0], th[1]);
     const short2_t hi = __builtin_amdgcn_cvt_pknorm_i16(th[2], th[3]);
-    *reinterpret_cast<uint2*>(code) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    const ntu2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    __builtin_nontemporal_store(w, reinterpret_cast<ntu2*>(code));
   }
   s = row16_sum(s);
   if (ok && (threadIdx.x & 15) == 0 && gcol64 < p.N)
@@ -1093,8 +1117,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int grow = er0 + i * 32 + 4 * it;
-      dst[it] = grow < p.M && ec < p.N ? *reinterpret_cast<const uint2*>(p.aux + (int64_t)grow * p.ldc + ec)
-                                       : make_uint2(0, 0);
+      dst[it] = grow < p.M && ec < p.N ? ld_nt(p.aux + (int64_t)grow * p.ldc + ec) : make_uint2(0, 0);
     }
   };
   if constexpr (PF_AUX) load_aux(0, pa[0]);
@@ -1102,9 +1125,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int grow = er0 + 4 * it;
-      pc[0][it] = grow < p.M && ec < p.N
-                      ? *reinterpret_cast<const float4*>(static_cast<const float*>(p.C) + (int64_t)grow * p.ldc + ec)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      pc[0][it] = grow < p.M && ec < p.N ? ld_nt(static_cast<const float*>(p.C) + (int64_t)grow * p.ldc + ec)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
 #pragma unroll
@@ -1118,9 +1140,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int it = 0; it < 8; ++it) {
           const int grow = er0 + (i + 1) * 32 + 4 * it;
           pc[(i + 1) & 1][it] =
-              grow < p.M && ec < p.N
-                  ? *reinterpret_cast<const float4*>(static_cast<const float*>(p.C) + (int64_t)grow * p.ldc + ec)
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
+              grow < p.M && ec < p.N ? ld_nt(static_cast<const float*>(p.C) + (int64_t)grow * p.ldc + ec)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
         }
       }
     }
@@ -1159,8 +1180,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const float r1 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.x >> 16)));
           const float r2 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.y & 0xffffu)));
           const float r3 = __builtin_amdgcn_sqrtf(bf2f((bf16)(q.y >> 16)));
-          *reinterpret_cast<uint2*>(static_cast<bf16*>(p.C) + off) =
-              make_uint2(pack_bf16x2(v.x * 2.f * r0, v.y * 2.f * r1), pack_bf16x2(v.z * 2.f * r2, v.w * 2.f * r3));
+          st_nt(static_cast<bf16*>(p.C) + off,
+              make_uint2(pack_bf16x2(v.x * 2.f * r0, v.y * 2.f * r1), pack_bf16x2(v.z * 2.f * r2, v.w * 2.f * r3)));
         } else if constexpr (EPI == E_RELU2_BWD) {
           const uint2 u = pa[i & 1][it];
           const float u0 = bf2f((bf16)(u.x & 0xffffu)), u1 = bf2f((bf16)(u.x >> 16));
@@ -1170,10 +1191,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                          pack_bf16x2(v.z * 2.f * fmaxf(u2, 0.f), v.w * 2.f * fmaxf(u3, 0.f)));
         } else if constexpr (EPI == E_ACC_F32) {
           const float4 o = pc[i & 1][it];
-          *reinterpret_cast<float4*>(static_cast<float*>(p.C) + off) =
-              make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+          st_nt(static_cast<float*>(p.C) + off, make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w));
         } else if constexpr (EPI == E_PARTIAL) {
-          *reinterpret_cast<float4*>(cpart + (int64_t)grow * p.N + gcol) = v;
+          st_nt(cpart + (int64_t)grow * p.N + gcol, v);
+        } else if constexpr (EPI == E_STORE_F32) {
+          st_nt(static_cast<float*>(p.C) + off, v);
+        } else if constexpr (EPI == E_STORE_BF16) {
+          st_nt(static_cast<bf16*>(p.C) + off, make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)));
+        } else if constexpr (EPI == E_RELU2_SQ) {
+          const float a = fmaxf(v.x, 0.f), b = fmaxf(v.y, 0.f), c = fmaxf(v.z, 0.f), d = fmaxf(v.w, 0.f);
+          st_nt(static_cast<bf16*>(p.C) + off, make_uint2(pack_bf16x2(a * a, b * b), pack_bf16x2(c * c, d * d)));
         } else {
           epilogue4<EPI>(p, v, grow, gcol);
         }
