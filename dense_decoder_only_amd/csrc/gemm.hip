@@ -671,6 +671,37 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
   }
 }
 
+// The same sum four columns at a time (N, ldc and both buffers 16-byte
+// aligned), the loads of four splits issued together and added in order.
+__global__ void splitk_reduce4_kernel(const float* __restrict__ part, int splits, int M, int N,
+                                      float* __restrict__ C, int64_t ldc, int beta) {
+  const int64_t total = (int64_t)M * N, total4 = total >> 2;
+  for (int64_t i4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i4 < total4;
+       i4 += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = i4 * 4;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    int z = 0;
+    for (; z + 4 <= splits; z += 4) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = ld_nt(part + (int64_t)(z + u) * total + i);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s = make_float4(s.x + v[u].x, s.y + v[u].y, s.z + v[u].z, s.w + v[u].w);
+    }
+    for (; z < splits; ++z) {
+      const float4 v = ld_nt(part + (int64_t)z * total + i);
+      s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
+    }
+    const int64_t m = i / N, n = i - m * N;
+    float4* c = reinterpret_cast<float4*>(C + m * ldc + n);
+    if (beta) {
+      const float4 o = *c;
+      s = make_float4(o.x + s.x, o.y + s.y, o.z + s.z, o.w + s.w);
+    }
+    *c = s;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 path: a plain LDS-tiled SIMT kernel over generic strides (the fp32
 // configuration is small; this path is about exactness, not speed).
@@ -1494,6 +1525,13 @@ int gemm(const GemmDesc& g, hipStream_t stream) {
 
   if (splits > 1) {
     const int64_t total = g.M * g.N;
+    const uintptr_t align = reinterpret_cast<uintptr_t>(g.ws) | reinterpret_cast<uintptr_t>(final_c);
+    if (g.N % 4 == 0 && g.ldc % 4 == 0 && align % 16 == 0) {
+      const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(total / 4, 256), 4096);
+      splitk_reduce4_kernel<<<blocks, 256, 0, stream>>>(static_cast<const float*>(g.ws), splits, p.M, p.N,
+                                                        final_c, g.ldc, final_beta);
+      return check_launch("splitk_reduce4_kernel");
+    }
     const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(total, 256), 4096);
     splitk_reduce_kernel<<<blocks, 256, 0, stream>>>(static_cast<const float*>(g.ws), splits, p.M, p.N,
                                                      final_c, g.ldc, final_beta);

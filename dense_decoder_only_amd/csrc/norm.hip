@@ -13,15 +13,26 @@
 namespace nc {
 namespace {
 
-__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+// Rows are read and written once: non-temporal (streaming) accesses keep them
+// from displacing what the neighbouring GEMMs hold in L2.
+typedef float nf4 __attribute__((ext_vector_type(4)));
+typedef unsigned nu2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float4 load4(const float* p) {
+  const nf4 t = __builtin_nontemporal_load(reinterpret_cast<const nf4*>(p));
+  return make_float4(t.x, t.y, t.z, t.w);
+}
 __device__ __forceinline__ float4 load4(const bf16* p) {
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  const nu2 u = __builtin_nontemporal_load(reinterpret_cast<const nu2*>(p));
   return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                      __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
-__device__ __forceinline__ void store4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ void store4(float* p, float4 v) {
+  const nf4 t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<nf4*>(p));
+}
 __device__ __forceinline__ void store4(bf16* p, float4 v) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  const nu2 t = {pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+  __builtin_nontemporal_store(t, reinterpret_cast<nu2*>(p));
 }
 __device__ __forceinline__ float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
 __device__ __forceinline__ float4 scale4(float4 a, float s) { return make_float4(a.x * s, a.y * s, a.z * s, a.w * s); }

@@ -128,8 +128,12 @@ __global__ __launch_bounds__(256) void rope_qknorm_fwd_bf16_kernel(bf16* __restr
   const int t = (int)(tok % Tlen);
   bf16* x = qkv + tok * (int64_t)(H + 2) * 128 + (int64_t)head * 128 + 4 * j;
   float a[4], b[4];
-  unpack4(*reinterpret_cast<const uint2*>(x), a);
-  unpack4(*reinterpret_cast<const uint2*>(x + 64), b);
+  // read and written once, in place: streaming (non-temporal) accesses
+  typedef unsigned nu2 __attribute__((ext_vector_type(2)));
+  const nu2 la = __builtin_nontemporal_load(reinterpret_cast<const nu2*>(x));
+  const nu2 lb = __builtin_nontemporal_load(reinterpret_cast<const nu2*>(x + 64));
+  unpack4(make_uint2(la.x, la.y), a);
+  unpack4(make_uint2(lb.x, lb.y), b);
   const float4* tb = reinterpret_cast<const float4*>(table + ((int64_t)t * 64 + 4 * j) * 2);
   const float4 cs0 = tb[0], cs1 = tb[1];  // (cos, sin) of pairs 4j .. 4j+3
   const float c[4] = {cs0.x, cs0.z, cs1.x, cs1.z}, sn[4] = {cs0.y, cs0.w, cs1.y, cs1.w};
@@ -142,8 +146,10 @@ __global__ __launch_bounds__(256) void rope_qknorm_fwd_bf16_kernel(bf16* __restr
   }
   ss = group16_sum(ss);
   const float r = 1.f / sqrtf(ss / 128.f + eps);
-  *reinterpret_cast<uint2*>(x) = make_uint2(pack_bf16x2(ya[0] * r, ya[1] * r), pack_bf16x2(ya[2] * r, ya[3] * r));
-  *reinterpret_cast<uint2*>(x + 64) = make_uint2(pack_bf16x2(yb[0] * r, yb[1] * r), pack_bf16x2(yb[2] * r, yb[3] * r));
+  const nu2 sa = {pack_bf16x2(ya[0] * r, ya[1] * r), pack_bf16x2(ya[2] * r, ya[3] * r)};
+  const nu2 sb = {pack_bf16x2(yb[0] * r, yb[1] * r), pack_bf16x2(yb[2] * r, yb[3] * r)};
+  __builtin_nontemporal_store(sa, reinterpret_cast<nu2*>(x));
+  __builtin_nontemporal_store(sb, reinterpret_cast<nu2*>(x + 64));
   if (j == 0) {
     if (head < H) rstd_q[tok * H + head] = r;
     else rstd_k[tok] = r;
