@@ -199,8 +199,28 @@ __global__ void piece_table_kernel(const int32_t* __restrict__ npieces, const in
   }
 }
 
-__global__ __launch_bounds__(256) void piece_sum_kernel(const float* __restrict__ de, int d,
-                                                        const int32_t* __restrict__ sorted,
+// Row sources of the segmented sums: fp32 rows, or bf16 rows times a
+// per-position factor (mul * scale[t]).
+struct F32Rows {
+  const float* p;
+  __device__ float4 at(int32_t t, int d, int c) const {
+    return *reinterpret_cast<const float4*>(p + (int64_t)t * d + c);
+  }
+};
+struct ScaledBf16Rows {
+  const bf16* p;
+  const float* scale;
+  float mul;
+  __device__ float4 at(int32_t t, int d, int c) const {
+    const uint2 u = *reinterpret_cast<const uint2*>(p + (int64_t)t * d + c);
+    const float f = mul * scale[t];
+    return make_float4(f * __uint_as_float(u.x << 16), f * __uint_as_float(u.x & 0xffff0000u),
+                       f * __uint_as_float(u.y << 16), f * __uint_as_float(u.y & 0xffff0000u));
+  }
+};
+
+template <class Src>
+__global__ __launch_bounds__(256) void piece_sum_kernel(Src de, int d, const int32_t* __restrict__ sorted,
                                                         const int32_t* __restrict__ offset,
                                                         const int32_t* __restrict__ count,
                                                         const int32_t* __restrict__ npieces,
@@ -219,7 +239,7 @@ __global__ __launch_bounds__(256) void piece_sum_kernel(const float* __restrict_
   for (int c = threadIdx.x * 4; c < d; c += 1024) {
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int32_t k = beg; k < end; ++k) {
-      const float4 x = *reinterpret_cast<const float4*>(de + (int64_t)sorted[k] * d + c);
+      const float4 x = de.at(sorted[k], d, c);
       s.x += x.x;
       s.y += x.y;
       s.z += x.z;
@@ -294,9 +314,11 @@ int fill_zero(void* p, size_t bytes, hipStream_t s) {
 
 size_t embed_bwd_workspace_bytes(int64_t n, int64_t V, int d) { return carve(n, V, d, nullptr, nullptr); }
 
-int embed_bwd(const int32_t* ids, int64_t n, const float* de, int d, float* dtable, int64_t V, int accumulate,
-              void* ws, size_t ws_bytes, hipStream_t s) {
-  NC_REQUIRE(ids && de && dtable, NC_ERR_INVALID_ARG, "embed_bwd: null pointer");
+namespace {
+
+template <class Src>
+int embed_bwd_impl(const int32_t* ids, int64_t n, Src de, int d, float* dtable, int64_t V, int accumulate, void* ws,
+                   size_t ws_bytes, hipStream_t s) {
   NC_REQUIRE(n >= 0 && V > 0 && d > 0, NC_ERR_INVALID_ARG, "embed_bwd: bad shape");
   NC_REQUIRE(d % 8 == 0, NC_ERR_UNSUPPORTED, "embed_bwd: d must be a multiple of 8");
   NC_REQUIRE(n < (1ll << 31) && V < (1ll << 31), NC_ERR_UNSUPPORTED, "embed_bwd: sizes must be below 2^31");
@@ -324,12 +346,26 @@ int embed_bwd(const int32_t* ids, int64_t n, const float* de, int d, float* dtab
   piece_table_kernel<<<vb, 256, 0, s>>>(w.npieces, w.poff, V, w.piece_v);
   NC_TRY(check_launch("piece_table_kernel"));
   if (n > 0) {
-    piece_sum_kernel<<<(unsigned)w.max_pieces, 256, 0, s>>>(de, d, w.sorted, w.offset, w.count, w.npieces, w.poff,
+    piece_sum_kernel<Src><<<(unsigned)w.max_pieces, 256, 0, s>>>(de, d, w.sorted, w.offset, w.count, w.npieces, w.poff,
                                                             w.ppoff, w.piece_v, V, w.partial, dtable, accumulate);
     NC_TRY(check_launch("piece_sum_kernel"));
   }
   finish_kernel<<<dim3((unsigned)cdiv(V, 4), (unsigned)cdiv(d, 256)), 256, 0, s>>>(w.count, w.npieces, w.ppoff, w.partial, V, d, dtable, accumulate);
   return check_launch("finish_kernel");
+}
+
+}  // namespace
+
+int embed_bwd(const int32_t* ids, int64_t n, const float* de, int d, float* dtable, int64_t V, int accumulate,
+              void* ws, size_t ws_bytes, hipStream_t s) {
+  NC_REQUIRE(ids && de && dtable, NC_ERR_INVALID_ARG, "embed_bwd: null pointer");
+  return embed_bwd_impl(ids, n, F32Rows{de}, d, dtable, V, accumulate, ws, ws_bytes, s);
+}
+
+int embed_bwd_scaled(const int32_t* ids, int64_t n, const bf16* rows, const float* scale, float mul, int d,
+                     float* dtable, int64_t V, int accumulate, void* ws, size_t ws_bytes, hipStream_t s) {
+  NC_REQUIRE(ids && rows && scale && dtable, NC_ERR_INVALID_ARG, "embed_bwd: null pointer");
+  return embed_bwd_impl(ids, n, ScaledBf16Rows{rows, scale, mul}, d, dtable, V, accumulate, ws, ws_bytes, s);
 }
 
 }  // namespace nc

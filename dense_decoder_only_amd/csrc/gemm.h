@@ -28,7 +28,9 @@ struct GemmDesc {
   //             64 g .. 64 g + 63) xpart[g * M + row] = sum of exp(z' - c),
   //             z' = c tanh(z / c); xztgt[row] = z' at the row's target when
   //             the target is one of these columns.  If C is not null it
-  //             receives z' as int16 fixed point, round(z' / c * 32767).
+  //             receives u = exp(z' - c) (1 - (z'/c)^2) in bf16 (the logit
+  //             gradient up to a row scale and the target's one-hot term),
+  //             and xerr[row] = u - bf16(u) at the row's target.
   //   xent = 2: C (bf16) = xdl (exp(z' - xlse[row]) - [col == target])
   //             (1 - (z'/c)^2).
   int xent = 0;
@@ -37,6 +39,7 @@ struct GemmDesc {
   const float* xlse = nullptr;
   float* xpart = nullptr;
   float* xztgt = nullptr;
+  float* xerr = nullptr;
   int xv0 = 0;
   // capc > 0: C (fp32) = capc tanh(acc / capc), the logit softcap; only for
   // the small-M form (bf16, x W^T, M <= 128), which decoding uses.

@@ -67,6 +67,7 @@ struct MfmaParams {
   const float* xlse;
   float* xpart;
   float* xztgt;
+  float* xerr;
   // > 0: split-K launched as one flat grid of tiles x kxcd blocks, split s
   // on XCD s mod 8 (gemm_pipe_kernel only; kxcd a multiple of 8)
   int kxcd = 0;
@@ -145,37 +146,47 @@ __device__ __forceinline__ float row16_sum(float s) {
 
 // Forward cross-entropy epilogue: a 16-lane group (one DPP row) holds one
 // row's 64 columns (4 per lane); every lane of the group must call this.  y is
-// the row's target column relative to xv0 (-1 for rows past M); code points
-// at the row's stored code for column col (unused when p.C is null: no codes
-// are stored).
+// the row's target column relative to xv0 (-1 for rows past M); ust points at
+// the row's stored value for column col (unused when p.C is null: nothing is
+// stored).
 // With th = tanh(z / c) = sign(z) (1 - t) / (1 + t), t = e^{-2|z|/c}, the
-// capped logit is c th, exp(c th - c) = 2^{(th - 1) c log2(e)}, and the stored
-// code is th in signed 16-bit normalized form, round(32767 th), from one
-// v_cvt_pknorm_i16_f32 per two columns (it rounds exact ties away from zero;
-// either way the code is within half a step of 32767 th).
+// capped logit is c th and e = exp(c th - c) = 2^{(th - 1) c log2(e)}.  The
+// stored value is u = e (1 - th^2) in bf16: the logit gradient is
+// dloss (e / S - [col == y]) (1 - th^2) with S the row's sum of e, so the
+// backward needs only the row scale dloss / S and the target's term.  The
+// target's rounding error u - bf16(u) is kept so that the one-hot term
+// cancels against the fp32 value.
 __device__ __forceinline__ void xent_fwd4(const MfmaParams& p, float4 v, int row, int col, int gcol64, int y,
-                                          int16_t* code) {
+                                          bf16* ust) {
   const bool ok = row < p.M;
   const bool in = col < p.N;  // N is a multiple of 8: the 4 columns are all in range or none is
   const float zz[4] = {v.x, v.y, v.z, v.w};
   const float ka = -2.f * kLog2e * p.xinv_c, cl = p.xc * kLog2e;
-  float th[4];
+  float th[4], e[4];
   float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float t = __builtin_amdgcn_exp2f(ka * fabsf(zz[e]));
-    th[e] = copysignf((1.f - t) * __builtin_amdgcn_rcpf(1.f + t), zz[e]);
-    s += __builtin_amdgcn_exp2f(fmaf(th[e], cl, -cl));
+  for (int k = 0; k < 4; ++k) {
+    const float t = __builtin_amdgcn_exp2f(ka * fabsf(zz[k]));
+    th[k] = copysignf((1.f - t) * __builtin_amdgcn_rcpf(1.f + t), zz[k]);
+    e[k] = __builtin_amdgcn_exp2f(fmaf(th[k], cl, -cl));
+    s += e[k];
   }
   if (!in) s = 0.f;
   const unsigned d = (unsigned)(y - col);
-  if (ok && in && d < 4u) p.xztgt[row] = p.xc * (d == 0 ? th[0] : d == 1 ? th[1] : d == 2 ? th[2] : th[3]);
+  const bool here = ok && in && d < 4u;
+  if (here) p.xztgt[row] = p.xc * (d == 0 ? th[0] : d == 1 ? th[1] : d == 2 ? th[2] : th[3]);
   if (p.C && ok && in) {
-    typedef short short2_t __attribute__((ext_vector_type(2)));
-    const short2_t lo = __builtin_amdgcn_cvt_pknorm_i16(th[0], th[1]);
-    const short2_t hi = __builtin_amdgcn_cvt_pknorm_i16(th[2], th[3]);
-    const ntu2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-    __builtin_nontemporal_store(w, reinterpret_cast<ntu2*>(code));
+    float u[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) u[k] = e[k] * fmaf(-th[k], th[k], 1.f);
+    const uint32_t lo = pack_bf16x2(u[0], u[1]), hi = pack_bf16x2(u[2], u[3]);
+    const ntu2 w = {lo, hi};
+    __builtin_nontemporal_store(w, reinterpret_cast<ntu2*>(ust));
+    if (here) {
+      const uint32_t pair = d < 2 ? lo : hi;
+      const float rounded = __uint_as_float((d & 1) ? (pair & 0xffff0000u) : (pair << 16));
+      p.xerr[row] = (d == 0 ? u[0] : d == 1 ? u[1] : d == 2 ? u[2] : u[3]) - rounded;
+    }
   }
   s = row16_sum(s);
   if (ok && (threadIdx.x & 15) == 0 && gcol64 < p.N)
@@ -1186,11 +1197,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // land before the reads (no block barrier, whose fence would also wait for
     // the previous slab's global stores)
     wave_lds_sync();
-    // stored codes of the cross-entropy epilogue: this lane's element of
+    // stored values of the cross-entropy epilogue: this lane's element of
     // iteration it is 4 rows further than that of it - 1
-    int16_t* code = nullptr;
+    bf16* code = nullptr;
     if constexpr (EPI == E_XENT_FWD)
-      code = static_cast<int16_t*>(p.C) + (int64_t)(m0 + wm * 128 + i * 32 + (lane >> 4)) * p.ldc + n0 + wn * 64 +
+      code = static_cast<bf16*>(p.C) + (int64_t)(m0 + wm * 128 + i * 32 + (lane >> 4)) * p.ldc + n0 + wn * 64 +
              (lane & 15) * 4;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
@@ -1381,7 +1392,7 @@ int gemm_xent(const GemmDesc& g, hipStream_t stream) {
   NC_REQUIRE(g.xv0 % 64 == 0, NC_ERR_INVALID_ARG, "gemm: vocabulary offset must be a multiple of 64");
   if (g.xent == 1) {
     NC_REQUIRE(g.xpart && g.xztgt, NC_ERR_INVALID_ARG, "gemm: null cross-entropy output");
-    if (g.C) NC_REQUIRE(g.ldc >= g.N && g.ldc % 4 == 0, NC_ERR_INVALID_ARG, "gemm: bad stored-logit layout");
+    if (g.C) NC_REQUIRE(g.xerr && g.ldc >= g.N && g.ldc % 4 == 0, NC_ERR_INVALID_ARG, "gemm: bad stored-logit layout");
   }
   else NC_REQUIRE(g.C && g.xlse && g.cdt == NC_BF16 && g.ldc >= g.N, NC_ERR_INVALID_ARG, "gemm: bad dz output");
   MfmaParams p{};
@@ -1404,6 +1415,7 @@ int gemm_xent(const GemmDesc& g, hipStream_t stream) {
   p.xlse = g.xlse;
   p.xpart = g.xpart;
   p.xztgt = g.xztgt;
+  p.xerr = g.xerr;
   p.xv0 = g.xv0;
   const double flops = 2.0 * p.M * p.N * p.K;
   probe_begin(NC_PROBE_GEMM_NT, stream);

@@ -14,6 +14,10 @@ int embed_fwd(const int32_t* ids, int64_t n, const void* table, int dtype, int64
 size_t embed_bwd_workspace_bytes(int64_t n, int64_t V, int d);
 int embed_bwd(const int32_t* ids, int64_t n, const float* de, int d, float* dtable, int64_t V, int accumulate,
               void* ws, size_t ws_bytes, hipStream_t s);
+// dtable[v] (+)= sum over t with ids[t] = v of mul * scale[t] * rows[t] (bf16
+// rows), with embed_bwd's workspace, order and accumulate semantics.
+int embed_bwd_scaled(const int32_t* ids, int64_t n, const bf16* rows, const float* scale, float mul, int d,
+                     float* dtable, int64_t V, int accumulate, void* ws, size_t ws_bytes, hipStream_t s);
 
 int rope_table(float* table, int T, int hd, float base, hipStream_t s);
 int rope_qknorm_fwd(void* qkv, int dtype, int B, int T, int H, int hd, const float* table, float eps,
@@ -39,10 +43,11 @@ int mqa_attn_bwd(const void* qkv, const void* o, const void* dout, const float* 
                  const AttnRopeBwd* fuse = nullptr);
 
 size_t xent_workspace_bytes(int64_t M, int d, int V);
-// store_logits: keep the softcapped logits in ws (16-bit fixed point) when the
+// store_logits: keep u = exp(z' - c) (1 - (z'/c)^2) in ws (bf16) when the
 // fused path covers the vocabulary in one chunk; xent_bwd with from_stored
-// then forms dz from them instead of recomputing the logit product (same ws,
-// untouched in between).  Returns whether they were stored via *stored.
+// then takes the logit gradient from it (a row scale and the target's term)
+// instead of recomputing the logit product (same ws, untouched in between;
+// dh_acc must be 0).  Returns whether it was stored via *stored.
 // Targets outside [0, V) set *flag to 1 (flag = nullptr: the first int32 of
 // ws, cleared first); such rows have no target logit and count no bytes.
 int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* token_bytes, int64_t M, int d,

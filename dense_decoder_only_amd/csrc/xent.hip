@@ -19,6 +19,12 @@
 // dz = dloss (softmax(z') - onehot(y)) (1 - (z'/c)^2) in bf16 directly, then
 // dh (+)= dz U and dU (+)= dz^T h.  The vocabulary is one chunk unless the
 // bf16 dz would exceed 8 GiB.
+// The training step instead keeps u = exp(z' - c) (1 - (z'/c)^2) (bf16) from
+// the forward's epilogue.  With r_t = dloss exp(c - lse_t) and
+// q_t = dloss (1 - (z'_{t,y_t}/c)^2), dz = diag(r) u - q onehot(y), so
+//   dh_t = r_t (u U)_t - q_t U[y_t],
+//   dU   = u^T (diag(r) h) - sum_t q_t h_t e_{y_t}^T,
+// two plain products and row corrections, with no pass over [M, V].
 // fp32 (and other shapes): a GEMM writes one [M, Vc] fp32 logit chunk and a
 // row kernel folds it (forward) or forms dz from it (backward).
 // Partial sums are added in a fixed order and the loss sums in a fixed tree
@@ -58,6 +64,12 @@ struct XentWs {
   float* partial;  // [nparts, M]
   float* ztgt;     // [M]
   float* ltok;     // [M]
+  float* err;      // [M] u - bf16(u) at the target (stored path)
+  float* rs;       // [M] r_t (stored path)
+  float* qs;       // [M] q_t, less r_t err_t (stored path)
+  void* hs;        // [M, d] bf16 r_t h_t (stored path)
+  void* eb_ws;     // target-sorted segmented sums (stored path)
+  size_t eb_ws_bytes;
   void* gemm_ws;
   size_t gemm_ws_bytes;
   void* ut;        // U^T [d, V] (bf16 backward)
@@ -78,6 +90,12 @@ size_t carve(int64_t M, int d, int V, bool fused, XentWs* w, void* base) {
   const size_t o_p = take((size_t)nparts * M * 4);
   const size_t o_t = take((size_t)M * 4);
   const size_t o_l = take((size_t)M * 4);
+  const size_t o_e = take((size_t)M * 4);
+  const size_t o_rs = take(fused ? (size_t)M * 4 : 0);
+  const size_t o_qs = take(fused ? (size_t)M * 4 : 0);
+  const size_t o_hs = take(fused ? (size_t)M * d * 2 : 0);
+  const size_t ebb = fused ? embed_bwd_workspace_bytes(M, V, d) : 0;
+  const size_t o_eb = take(ebb);
   const size_t gwb = gemm_workspace_bytes(Vc, d, M);
   const size_t o_g = take(gwb);
   const size_t o_ut = take((size_t)V * d * 2);
@@ -89,6 +107,12 @@ size_t carve(int64_t M, int d, int V, bool fused, XentWs* w, void* base) {
     w->partial = reinterpret_cast<float*>(b + o_p);
     w->ztgt = reinterpret_cast<float*>(b + o_t);
     w->ltok = reinterpret_cast<float*>(b + o_l);
+    w->err = reinterpret_cast<float*>(b + o_e);
+    w->rs = reinterpret_cast<float*>(b + o_rs);
+    w->qs = reinterpret_cast<float*>(b + o_qs);
+    w->hs = b + o_hs;
+    w->eb_ws = ebb ? b + o_eb : nullptr;
+    w->eb_ws_bytes = ebb;
     w->gemm_ws = gwb ? b + o_g : nullptr;
     w->gemm_ws_bytes = gwb;
     w->ut = b + o_ut;
@@ -100,9 +124,10 @@ size_t carve(int64_t M, int d, int V, bool fused, XentWs* w, void* base) {
 // row whose target lies outside [0, V) (which no column matches) reads a
 // defined value; such rows raise the device flag.
 __global__ void xent_prep_kernel(const int32_t* __restrict__ tgt, int64_t M, int V, float* __restrict__ ztgt,
-                                 int32_t* __restrict__ flag) {
+                                 float* __restrict__ err, int32_t* __restrict__ flag) {
   for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < M; r += (int64_t)gridDim.x * blockDim.x) {
     ztgt[r] = 0.f;
+    err[r] = 0.f;
     if ((uint32_t)tgt[r] >= (uint32_t)V) *flag = 1;
   }
 }
@@ -207,56 +232,56 @@ __global__ __launch_bounds__(256) void xent_bwd_rows_kernel(const float* __restr
   }
 }
 
-// dz from the stored logits, in place: q = round(z'/c * 32767) (int16) ->
-// dz = dloss (exp(z' - lse) - [v == y]) (1 - (z'/c)^2) (bf16).  One chunk
-// covering the whole vocabulary (column = vocabulary id).  A block streams
-// rows (its row's log-sum-exp and target read once), each thread 8
-// consecutive columns per 16-byte access with DZ_UNROLL accesses in flight;
-// the logits are read once and dz written once, so both go around the caches.
-constexpr int DZ_UNROLL = 4;
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t dz_pair(uint32_t w, int col, int y, float L2, float c2, float inv, float dloss) {
-  float g2[2];
-#pragma unroll
-  for (int hlf = 0; hlf < 2; ++hlf) {
-    const int16_t qi = (int16_t)(hlf ? (w >> 16) : (w & 0xffffu));
-    const float th = (float)qi * inv;  // z' / c
-    const float pr = __builtin_amdgcn_exp2f(c2 * th - L2);  // exp(z' - lse) by the hardware exp2
-    g2[hlf] = dloss * (pr - (col + hlf == y ? 1.f : 0.f)) * (1.f - th * th);
+// Stored path, per row t (one wavefront, 4 rows per block):
+// r_t = dloss exp(c - lse_t); q_t = dloss (1 - (z'_{t,y}/c)^2) - r_t err_t for
+// a target in [0, V), else 0 (such a row has no one-hot term); hs_t = bf16(r_t h_t).
+// The err term makes r_t bf16(u_ty) - q_t equal the fp32 r_t u_ty - dloss (1 - th^2).
+__global__ __launch_bounds__(256) void xent_rowscale_kernel(const bf16* __restrict__ h, const float* __restrict__ lse,
+                                                            const float* __restrict__ ztgt,
+                                                            const float* __restrict__ err,
+                                                            const int32_t* __restrict__ tgt, int64_t M, int d, int V,
+                                                            float c, float dloss, float* __restrict__ rs,
+                                                            float* __restrict__ qs, bf16* __restrict__ hs) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float r = dloss * expf(c - lse[row]);
+  if (lane == 0) {
+    const float th = ztgt[row] / c;
+    rs[row] = r;
+    qs[row] = (uint32_t)tgt[row] < (uint32_t)V ? dloss * (1.f - th * th) - r * err[row] : 0.f;
   }
-  return pack_bf16x2(g2[0], g2[1]);
+  for (int col = lane * 4; col < d; col += 256) {
+    const uint2 u = *reinterpret_cast<const uint2*>(h + row * d + col);
+    *reinterpret_cast<uint2*>(hs + row * d + col) =
+        make_uint2(pack_bf16x2(r * __uint_as_float(u.x << 16), r * __uint_as_float(u.x & 0xffff0000u)),
+                   pack_bf16x2(r * __uint_as_float(u.y << 16), r * __uint_as_float(u.y & 0xffff0000u)));
+  }
 }
 
-__global__ __launch_bounds__(256) void xent_dz_stored_kernel(uint16_t* __restrict__ buf, int64_t M, int N, float c,
-                                                             const int32_t* __restrict__ tgt,
-                                                             const float* __restrict__ lse, float dloss) {
-  const float inv = 1.f / 32767.f;
-  const float c2 = c * 1.4426950408889634f;
-  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
-    const float L2 = lse[row] * 1.4426950408889634f;
-    const int y = tgt[row];
-    u32x4_t* rb = reinterpret_cast<u32x4_t*>(buf + row * N);
-    const int n16 = N >> 3;  // 16-byte groups in the row
-    for (int i0 = threadIdx.x; i0 < n16; i0 += 256 * DZ_UNROLL) {
-      u32x4_t q[DZ_UNROLL];
-#pragma unroll
-      for (int u = 0; u < DZ_UNROLL; ++u) {
-        const int i = i0 + u * 256;
-        q[u] = i < n16 ? __builtin_nontemporal_load(rb + i) : u32x4_t{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < DZ_UNROLL; ++u) {
-        const int i = i0 + u * 256;
-        if (i < n16) {
-          const int col = i * 8;
-          const uint32_t w0 = q[u].x, w1 = q[u].y, w2 = q[u].z, w3 = q[u].w;
-          const u32x4_t o = {dz_pair(w0, col, y, L2, c2, inv, dloss), dz_pair(w1, col + 2, y, L2, c2, inv, dloss),
-                             dz_pair(w2, col + 4, y, L2, c2, inv, dloss), dz_pair(w3, col + 6, y, L2, c2, inv, dloss)};
-          __builtin_nontemporal_store(o, rb + i);
-        }
-      }
+// Stored path: dh_t = r_t (u U)_t - q_t U[y_t], in place on the product.
+__global__ __launch_bounds__(256) void xent_dh_fix_kernel(float* __restrict__ dh, const float* __restrict__ rs,
+                                                          const float* __restrict__ qs,
+                                                          const int32_t* __restrict__ tgt,
+                                                          const bf16* __restrict__ U, int64_t M, int d, int V) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float r = rs[row], q = qs[row];
+  const int y = tgt[row];
+  const bool hit = (uint32_t)y < (uint32_t)V;
+  for (int col = lane * 4; col < d; col += 256) {
+    f32x4_t* p = reinterpret_cast<f32x4_t*>(dh + row * d + col);
+    f32x4_t v = __builtin_nontemporal_load(p) * r;
+    if (hit) {
+      const uint2 u = *reinterpret_cast<const uint2*>(U + (int64_t)y * d + col);
+      v.x -= q * __uint_as_float(u.x << 16);
+      v.y -= q * __uint_as_float(u.x & 0xffff0000u);
+      v.z -= q * __uint_as_float(u.y << 16);
+      v.w -= q * __uint_as_float(u.y & 0xffff0000u);
     }
+    __builtin_nontemporal_store(v, p);
   }
 }
 
@@ -294,7 +319,7 @@ int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
     flag = w.flag;
     NC_TRY(fill_zero(flag, 4, s));
   }
-  xent_prep_kernel<<<(unsigned)std::min<int64_t>(cdiv(M, 256), 1024), 256, 0, s>>>(tgt, M, V, w.ztgt, flag);
+  xent_prep_kernel<<<(unsigned)std::min<int64_t>(cdiv(M, 256), 1024), 256, 0, s>>>(tgt, M, V, w.ztgt, w.err, flag);
   NC_TRY(check_launch("xent_prep_kernel"));
   for (int k = 0; k < nch; ++k) {
     const int v0 = k * Vc;
@@ -319,6 +344,7 @@ int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
       g.xv0 = v0;
       if (store_logits && nch == 1) {
         g.C = w.dz;
+        g.xerr = w.err;
         g.ldc = n;
         if (stored) *stored = true;
       }
@@ -356,6 +382,52 @@ int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
   const int nch = (int)cdiv(V, Vc);
   const size_t esz = dtype == NC_BF16 ? 2 : 4;
   if (dtype == NC_BF16) NC_TRY(transpose(U, V, d, 2, w.ut, s));
+  if (fused && from_stored) {
+    NC_REQUIRE(nch == 1 && !dh_acc, NC_ERR_INVALID_ARG,
+               "softcap_xent_bwd: the stored path needs a one-chunk vocabulary and a fresh dh");
+    const unsigned rb = (unsigned)cdiv(M, 4);
+    xent_rowscale_kernel<<<rb, 256, 0, s>>>(static_cast<const bf16*>(h), lse, w.ztgt, w.err, tgt, M, d, V, softcap,
+                                            dloss, w.rs, w.qs, static_cast<bf16*>(w.hs));
+    NC_TRY(check_launch("xent_rowscale_kernel"));
+    // dh = r (u U) - q U[y]: the product through U^T (K-contiguous), then the row fix
+    GemmDesc gh;
+    gh.transA = 0;
+    gh.transB = 1;
+    gh.M = M;
+    gh.N = d;
+    gh.K = V;
+    gh.A = w.dz;
+    gh.lda = V;
+    gh.B = w.ut;
+    gh.ldb = V;
+    gh.C = dh;
+    gh.cdt = NC_F32;
+    gh.ldc = d;
+    gh.dtype = NC_BF16;
+    NC_TRY(gemm(gh, s));
+    xent_dh_fix_kernel<<<rb, 256, 0, s>>>(dh, w.rs, w.qs, tgt, static_cast<const bf16*>(U), M, d, V);
+    NC_TRY(check_launch("xent_dh_fix_kernel"));
+    // dU (+)= u^T (r h), then dU[y_t] -= q_t h_t in target order
+    GemmDesc gu;
+    gu.transA = 1;
+    gu.transB = 0;
+    gu.M = V;
+    gu.N = d;
+    gu.K = M;
+    gu.A = w.dz;
+    gu.lda = V;
+    gu.B = w.hs;
+    gu.ldb = d;
+    gu.C = dU;
+    gu.cdt = NC_F32;
+    gu.ldc = d;
+    gu.beta = dU_acc ? 1.f : 0.f;
+    gu.dtype = NC_BF16;
+    gu.ws = w.gemm_ws;
+    gu.ws_bytes = w.gemm_ws_bytes;
+    NC_TRY(gemm(gu, s));
+    return embed_bwd_scaled(tgt, M, static_cast<const bf16*>(h), w.qs, -1.f, d, dU, V, 1, w.eb_ws, w.eb_ws_bytes, s);
+  }
   for (int k = 0; k < nch; ++k) {
     const int v0 = k * Vc;
     const int n = std::min(Vc, V - v0);
@@ -371,12 +443,7 @@ int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
     g.B = Uc;
     g.ldb = d;
     g.dtype = dtype;
-    if (fused && from_stored) {
-      NC_REQUIRE(nch == 1, NC_ERR_INVALID_ARG, "softcap_xent_bwd: stored logits need a one-chunk vocabulary");
-      xent_dz_stored_kernel<<<(unsigned)std::min<int64_t>(M, 1 << 30), 256, 0, s>>>(
-          static_cast<uint16_t*>(w.dz), M, n, softcap, tgt, lse, dloss);
-      NC_TRY(check_launch("xent_dz_stored_kernel"));
-    } else if (fused) {
+    if (fused) {
       g.xent = 2;
       g.xc = softcap;
       g.xdl = dloss;
