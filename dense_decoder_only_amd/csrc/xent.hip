@@ -96,7 +96,8 @@ size_t carve(int64_t M, int d, int V, bool fused, XentWs* w, void* base) {
   const size_t o_hs = take(fused ? (size_t)M * d * 2 : 0);
   const size_t ebb = fused ? embed_bwd_workspace_bytes(M, V, d) : 0;
   const size_t o_eb = take(ebb);
-  const size_t gwb = gemm_workspace_bytes(Vc, d, M);
+  // split-K partials of dU (Vc x d, K = M) and of dh (M x d, K = Vc)
+  const size_t gwb = std::max(gemm_workspace_bytes(Vc, d, M), gemm_workspace_bytes(M, d, Vc));
   const size_t o_g = take(gwb);
   const size_t o_ut = take((size_t)V * d * 2);
   if (w) {
@@ -404,6 +405,8 @@ int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
     gh.cdt = NC_F32;
     gh.ldc = d;
     gh.dtype = NC_BF16;
+    gh.ws = w.gemm_ws;
+    gh.ws_bytes = w.gemm_ws_bytes;
     NC_TRY(gemm(gh, s));
     xent_dh_fix_kernel<<<rb, 256, 0, s>>>(dh, w.rs, w.qs, tgt, static_cast<const bf16*>(U), M, d, V);
     NC_TRY(check_launch("xent_dh_fix_kernel"));
@@ -489,6 +492,8 @@ int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
     gh.ldc = d;
     gh.beta = (k > 0 || dh_acc) ? 1.f : 0.f;
     gh.dtype = dtype;
+    gh.ws = w.gemm_ws;
+    gh.ws_bytes = w.gemm_ws_bytes;
     NC_TRY(gemm(gh, s));
     // dU_c (+)= dz^T h : [n, M] x [M, d]
     GemmDesc gu;
