@@ -9,6 +9,7 @@
 // registers between the reduction and the scaling pass; wider rows are read
 // twice.  These kernels are bound by HBM bandwidth.
 #include "common.h"
+#include "ops.h"
 
 namespace nc {
 namespace {
@@ -33,6 +34,13 @@ __device__ __forceinline__ void store4(float* p, float4 v) {
 __device__ __forceinline__ void store4(bf16* p, float4 v) {
   const nu2 t = {pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
   __builtin_nontemporal_store(t, reinterpret_cast<nu2*>(p));
+}
+// Cached loads, for the embedding gather: the Zipf head's rows recur.
+__device__ __forceinline__ float4 load4_cached(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4_cached(const bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 __device__ __forceinline__ float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
 __device__ __forceinline__ float4 scale4(float4 a, float s) { return make_float4(a.x * s, a.y * s, a.z * s, a.w * s); }
@@ -70,11 +78,11 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_reg_kernel(const TX* __restri
   if (lane == 0 && rstd) rstd[row] = r;
 }
 
-template <typename TG, typename TY>
+template <typename TG, typename TY, bool FIX = false>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(const TG* __restrict__ g, const TY* __restrict__ y,
                                                               const float* __restrict__ rstd, int64_t rows, int d,
                                                               float* __restrict__ dx, int accumulate,
-                                                              bf16* __restrict__ dx_bf16) {
+                                                              bf16* __restrict__ dx_bf16, GradRowFix fix = {}) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -92,6 +100,21 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(const TG* __restri
       gv[k] = load4(gr + c);
       yv[k] = load4(yr + c);
       pv[k] = accumulate ? load4(dr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  if constexpr (FIX) {
+    const float rs = fix.rs[row], qs = fix.qs[row];
+    const int32_t t = fix.tgt[row];
+    const bool hit = (uint32_t)t < (uint32_t)fix.V;
+    const bf16* ur = fix.U + (int64_t)(hit ? t : 0) * d;
+#pragma unroll
+    for (int k = 0; k < CV; ++k) {
+      const int c = lane * 4 + k * 256;
+      if (c < d) {
+        const float4 u = hit ? load4_cached(ur + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        gv[k] = make_float4(gv[k].x * rs - qs * u.x, gv[k].y * rs - qs * u.y, gv[k].z * rs - qs * u.z,
+                            gv[k].w * rs - qs * u.w);
+      }
     }
   }
 #pragma unroll
@@ -166,8 +189,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void embed_fwd_kernel(const int32_t* __restrict__ ids, int64_t n,
                                                         const T* __restrict__ table, int64_t V, int d,
                                                         T* __restrict__ rows_out, float* __restrict__ x_out,
-                                                        float* __restrict__ rstd, float eps,
-                                                        int32_t* __restrict__ flag) {
+                                                        float* __restrict__ x_copy, float* __restrict__ rstd,
+                                                        float eps, int32_t* __restrict__ flag) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n) return;
@@ -186,14 +209,15 @@ __global__ __launch_bounds__(256) void embed_fwd_kernel(const int32_t* __restric
   if (x_out) {
     float ss = 0.f;
     for (int c = lane * 4; c < d; c += 256) {
-      const float4 v = ok ? load4(src + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 v = ok ? load4_cached(src + c) : make_float4(0.f, 0.f, 0.f, 0.f);
       ss += dot4(v, v);
     }
     ss = wave_sum(ss);
     const float r = 1.f / sqrtf(ss / (float)d + eps);
     for (int c = lane * 4; c < d; c += 256) {
-      const float4 v = ok ? load4(src + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 v = ok ? load4_cached(src + c) : make_float4(0.f, 0.f, 0.f, 0.f);
       store4(x_out + row * d + c, scale4(v, r));
+      if (x_copy) store4(x_copy + row * d + c, scale4(v, r));
     }
     if (lane == 0 && rstd) rstd[row] = r;
   }
@@ -243,7 +267,7 @@ int rmsnorm_fwd(const void* x, int xdt, int64_t rows, int d, float eps, void* y,
 }
 
 int rmsnorm_bwd(const void* g, int gdt, const void* y, int ydt, const float* rstd, int64_t rows, int d,
-                float* dx, int accumulate, void* dx_bf16, hipStream_t s) {
+                float* dx, int accumulate, void* dx_bf16, hipStream_t s, const GradRowFix* fix) {
   NC_REQUIRE(g && y && rstd && dx, NC_ERR_INVALID_ARG, "rmsnorm_bwd: null pointer");
   NC_REQUIRE(rows >= 0 && d > 0, NC_ERR_INVALID_ARG, "rmsnorm_bwd: bad shape");
   NC_REQUIRE(d % 8 == 0, NC_ERR_UNSUPPORTED, "rmsnorm_bwd: d must be a multiple of 8");
@@ -251,6 +275,18 @@ int rmsnorm_bwd(const void* g, int gdt, const void* y, int ydt, const float* rst
              "rmsnorm_bwd: bad dtype");
   if (rows == 0) return NC_OK;
   bf16* dxb = static_cast<bf16*>(dx_bf16);
+  if (fix) {
+    NC_REQUIRE(gdt == NC_F32 && d <= 256 * CV && fix->rs && fix->qs && fix->tgt && fix->U, NC_ERR_INVALID_ARG,
+               "rmsnorm_bwd: the row fix needs an fp32 gradient, d <= 2048 and its arrays");
+    const unsigned blocks = (unsigned)cdiv(rows, 4);
+    if (ydt == NC_F32)
+      rmsnorm_bwd_reg_kernel<float, float, true><<<blocks, 256, 0, s>>>(
+          static_cast<const float*>(g), static_cast<const float*>(y), rstd, rows, d, dx, accumulate, dxb, *fix);
+    else
+      rmsnorm_bwd_reg_kernel<float, bf16, true><<<blocks, 256, 0, s>>>(
+          static_cast<const float*>(g), static_cast<const bf16*>(y), rstd, rows, d, dx, accumulate, dxb, *fix);
+    return check_launch("rmsnorm_bwd_reg_kernel");
+  }
   if (gdt == NC_F32 && ydt == NC_F32) return launch_bwd<float, float>(g, y, rstd, rows, d, dx, accumulate, dxb, s);
   if (gdt == NC_F32 && ydt == NC_BF16) return launch_bwd<float, bf16>(g, y, rstd, rows, d, dx, accumulate, dxb, s);
   if (gdt == NC_BF16 && ydt == NC_F32) return launch_bwd<bf16, float>(g, y, rstd, rows, d, dx, accumulate, dxb, s);
@@ -258,20 +294,20 @@ int rmsnorm_bwd(const void* g, int gdt, const void* y, int ydt, const float* rst
 }
 
 int embed_fwd(const int32_t* ids, int64_t n, const void* table, int dtype, int64_t V, int d, void* rows_out,
-              float* x_out, float* rstd, float eps, int32_t* flag, hipStream_t s) {
+              float* x_out, float* rstd, float eps, int32_t* flag, hipStream_t s, float* x_copy) {
   NC_REQUIRE(ids && table, NC_ERR_INVALID_ARG, "embed_fwd: null pointer");
   NC_REQUIRE(n >= 0 && V > 0 && d > 0, NC_ERR_INVALID_ARG, "embed_fwd: bad shape");
   NC_REQUIRE(d % 8 == 0, NC_ERR_UNSUPPORTED, "embed_fwd: d must be a multiple of 8");
   NC_REQUIRE(dtype == NC_F32 || dtype == NC_BF16, NC_ERR_INVALID_ARG, "embed_fwd: bad dtype");
-  NC_REQUIRE(!(rstd && !x_out), NC_ERR_INVALID_ARG, "embed_fwd: rstd needs x_out");
+  NC_REQUIRE(!((rstd || x_copy) && !x_out), NC_ERR_INVALID_ARG, "embed_fwd: rstd and x_copy need x_out");
   if (n == 0) return NC_OK;
   const unsigned blocks = (unsigned)cdiv(n, 4);
   if (dtype == NC_F32)
     embed_fwd_kernel<float><<<blocks, 256, 0, s>>>(ids, n, static_cast<const float*>(table), V, d,
-                                                   static_cast<float*>(rows_out), x_out, rstd, eps, flag);
+                                                   static_cast<float*>(rows_out), x_out, x_copy, rstd, eps, flag);
   else
     embed_fwd_kernel<bf16><<<blocks, 256, 0, s>>>(ids, n, static_cast<const bf16*>(table), V, d,
-                                                  static_cast<bf16*>(rows_out), x_out, rstd, eps, flag);
+                                                  static_cast<bf16*>(rows_out), x_out, x_copy, rstd, eps, flag);
   return check_launch("embed_fwd_kernel");
 }
 
@@ -292,5 +328,5 @@ extern "C" int nc_rmsnorm_bwd(const void* dy, int dydt, const void* y, int ydt, 
 extern "C" int nc_embed_fwd(const int32_t* ids, int64_t n, const void* table, int dtype, int64_t V, int d,
                             void* rows_out, float* x_out, float* rstd, float eps, int32_t* flag, void* stream) {
   return nc::api_done(nc::embed_fwd(ids, n, table, dtype, V, d, rows_out, x_out, rstd, eps, flag,
-                       static_cast<hipStream_t>(stream)), stream, "nc_embed_fwd");
+                       static_cast<hipStream_t>(stream), nullptr), stream, "nc_embed_fwd");
 }

@@ -7,10 +7,23 @@ namespace nc {
 
 int rmsnorm_fwd(const void* x, int xdt, int64_t rows, int d, float eps, void* y, int ydt, float* rstd,
                 hipStream_t s);
+// Row fix of a gradient as rmsnorm_bwd reads it: g_t <- rs[t] g_t - qs[t] U[tgt[t]]
+// (U bf16 [V, d]; a target outside [0, V) takes no U row).  The vocabulary
+// head's backward hands its dh over in this form.
+struct GradRowFix {
+  const float* rs;
+  const float* qs;
+  const int32_t* tgt;
+  const bf16* U;
+  int V;
+};
+// fix (optional): fp32 g and d <= 2048 only.
 int rmsnorm_bwd(const void* g, int gdt, const void* y, int ydt, const float* rstd, int64_t rows, int d,
-                float* dx, int accumulate, void* dx_bf16, hipStream_t s);
+                float* dx, int accumulate, void* dx_bf16, hipStream_t s, const GradRowFix* fix = nullptr);
+// x_copy (optional): a second copy of x_out.
 int embed_fwd(const int32_t* ids, int64_t n, const void* table, int dtype, int64_t V, int d, void* rows_out,
-              float* x_out, float* rstd, float eps, int32_t* flag, hipStream_t s);
+              float* x_out, float* rstd, float eps, int32_t* flag, hipStream_t s,
+              float* x_copy = nullptr);
 size_t embed_bwd_workspace_bytes(int64_t n, int64_t V, int d);
 int embed_bwd(const int32_t* ids, int64_t n, const float* de, int d, float* dtable, int64_t V, int accumulate,
               void* ws, size_t ws_bytes, hipStream_t s);
@@ -53,9 +66,12 @@ size_t xent_workspace_bytes(int64_t M, int d, int V);
 int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* token_bytes, int64_t M, int d,
              int V, float softcap, float* lse, float* loss_tok, float* loss, float* bpb, void* ws, size_t ws_bytes,
              hipStream_t s, bool store_logits = false, bool* stored = nullptr, int32_t* flag = nullptr);
+// defer_fix (stored path only): dh is left as u U and *defer_fix receives the
+// row fix that makes it dh (valid until ws is next used); the caller's
+// rmsnorm_bwd applies it.
 int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* lse, int64_t M, int d, int V,
              float softcap, float dloss, float* dh, int dh_acc, float* dU, int dU_acc, void* ws, size_t ws_bytes,
-             hipStream_t s, bool from_stored = false);
+             hipStream_t s, bool from_stored = false, GradRowFix* defer_fix = nullptr);
 
 int fill_zero(void* p, size_t bytes, hipStream_t s);
 

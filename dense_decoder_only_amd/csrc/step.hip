@@ -250,8 +250,8 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
   // ---------------------------------------------------------------- forward
   NC_TRY(fill_zero(w.flag, 4, s));
   NC_TRY(rope_table(w.table, T, hd, c->rope_base, s));
-  NC_TRY(embed_fwd(ids, M, p->embed, dt, V, (int)d, nullptr, w.x0, w.rstd0, c->eps, w.flag, s));
-  NC_CHECK_HIP(hipMemcpyAsync(w.x, w.x0, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s));
+  // x0 (kept for the embedding norm's backward) and the residual stream x start equal
+  NC_TRY(embed_fwd(ids, M, p->embed, dt, V, (int)d, nullptr, w.x0, w.rstd0, c->eps, w.flag, s, w.x));
 
   for (int l = 0; l < L; ++l) {
     Layer& ly = layers[l];
@@ -313,9 +313,14 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
   float* g = w.x;  // the residual stream is dead: reuse it for its gradient
   auto gop_of = [&](int v) -> void* { return dt == NC_BF16 ? w.g_lp[v % kRing] : static_cast<void*>(g); };
   auto glp_out = [&](int v) -> bf16* { return dt == NC_BF16 ? static_cast<bf16*>(w.g_lp[v % kRing]) : nullptr; };
+  // with the stored logits, dh comes as u U plus a row fix that the final
+  // norm's backward applies as it reads it
+  GradRowFix dh_fix{};
   NC_TRY(xent_bwd(w.h, p->unembed, dt, tgt, w.lse_ce, M, (int)d, V, c->softcap, 1.f / (float)M, w.dm, 0,
-                  gr->unembed, acc, w.xent_ws, w.xent_ws_bytes, s, logits_stored));
-  NC_TRY(rmsnorm_bwd(w.dm, NC_F32, w.h, dt, w.rstd_f, M, (int)d, g, 0, glp_out(gv), s));
+                  gr->unembed, acc, w.xent_ws, w.xent_ws_bytes, s, logits_stored,
+                  logits_stored && d <= 2048 ? &dh_fix : nullptr));
+  NC_TRY(rmsnorm_bwd(w.dm, NC_F32, w.h, dt, w.rstd_f, M, (int)d, g, 0, glp_out(gv), s,
+                     dh_fix.rs ? &dh_fix : nullptr));
   // In fp32 the gradient copy is the residual gradient itself, which the
   // main stream keeps updating: the side stream must then run in line.
   if (dt != NC_BF16 && side) {

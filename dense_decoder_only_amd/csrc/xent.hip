@@ -370,7 +370,7 @@ int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
 
 int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* lse, int64_t M, int d, int V,
              float softcap, float dloss, float* dh, int dh_acc, float* dU, int dU_acc, void* ws, size_t ws_bytes,
-             hipStream_t s, bool from_stored) {
+             hipStream_t s, bool from_stored, GradRowFix* defer_fix) {
   NC_TRY(validate(h, U, dtype, tgt, M, d, V));
   NC_REQUIRE(lse && dh && dU, NC_ERR_INVALID_ARG, "softcap_xent_bwd: null pointer");
   NC_REQUIRE(softcap > 0.f, NC_ERR_INVALID_ARG, "softcap_xent_bwd: softcap must be positive");
@@ -408,8 +408,12 @@ int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
     gh.ws = w.gemm_ws;
     gh.ws_bytes = w.gemm_ws_bytes;
     NC_TRY(gemm(gh, s));
-    xent_dh_fix_kernel<<<rb, 256, 0, s>>>(dh, w.rs, w.qs, tgt, static_cast<const bf16*>(U), M, d, V);
-    NC_TRY(check_launch("xent_dh_fix_kernel"));
+    if (defer_fix) {
+      *defer_fix = GradRowFix{w.rs, w.qs, tgt, static_cast<const bf16*>(U), V};
+    } else {
+      xent_dh_fix_kernel<<<rb, 256, 0, s>>>(dh, w.rs, w.qs, tgt, static_cast<const bf16*>(U), M, d, V);
+      NC_TRY(check_launch("xent_dh_fix_kernel"));
+    }
     // dU (+)= u^T (r h), then dU[y_t] -= q_t h_t in target order
     GemmDesc gu;
     gu.transA = 1;
