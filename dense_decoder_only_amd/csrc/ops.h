@@ -66,9 +66,9 @@ size_t xent_workspace_bytes(int64_t M, int d, int V);
 int xent_fwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* token_bytes, int64_t M, int d,
              int V, float softcap, float* lse, float* loss_tok, float* loss, float* bpb, void* ws, size_t ws_bytes,
              hipStream_t s, bool store_logits = false, bool* stored = nullptr, int32_t* flag = nullptr);
-// defer_fix (stored path only): dh is left as u U and *defer_fix receives the
-// row fix that makes it dh (valid until ws is next used); the caller's
-// rmsnorm_bwd applies it.
+// defer_fix (required on the stored path): dh is left as u U and *defer_fix
+// receives the row fix that makes it dh (valid until ws is next used); the
+// caller's rmsnorm_bwd applies it.
 int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const float* lse, int64_t M, int d, int V,
              float softcap, float dloss, float* dh, int dh_acc, float* dU, int dU_acc, void* ws, size_t ws_bytes,
              hipStream_t s, bool from_stored = false, GradRowFix* defer_fix = nullptr);

@@ -273,7 +273,7 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
   NC_TRY(rmsnorm_fwd(w.x, NC_F32, M, (int)d, c->eps, w.h, dt, w.rstd_f, s));
   bool logits_stored = false;
   NC_TRY(xent_fwd(w.h, p->unembed, dt, tgt, token_bytes, M, (int)d, V, c->softcap, w.lse_ce, loss_tok, loss, bpb,
-                  w.xent_ws, w.xent_ws_bytes, s, true, &logits_stored, w.flag));
+                  w.xent_ws, w.xent_ws_bytes, s, d <= 2048, &logits_stored, w.flag));
 
   // --------------------------------------------------------------- backward
   // Side stream: the weight-gradient products dW = dY^T X, which nothing in
@@ -317,8 +317,7 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
   // norm's backward applies as it reads it
   GradRowFix dh_fix{};
   NC_TRY(xent_bwd(w.h, p->unembed, dt, tgt, w.lse_ce, M, (int)d, V, c->softcap, 1.f / (float)M, w.dm, 0,
-                  gr->unembed, acc, w.xent_ws, w.xent_ws_bytes, s, logits_stored,
-                  logits_stored && d <= 2048 ? &dh_fix : nullptr));
+                  gr->unembed, acc, w.xent_ws, w.xent_ws_bytes, s, logits_stored, &dh_fix));
   NC_TRY(rmsnorm_bwd(w.dm, NC_F32, w.h, dt, w.rstd_f, M, (int)d, g, 0, glp_out(gv), s,
                      dh_fix.rs ? &dh_fix : nullptr));
   // In fp32 the gradient copy is the residual gradient itself, which the

@@ -260,32 +260,6 @@ __global__ __launch_bounds__(256) void xent_rowscale_kernel(const bf16* __restri
   }
 }
 
-// Stored path: dh_t = r_t (u U)_t - q_t U[y_t], in place on the product.
-__global__ __launch_bounds__(256) void xent_dh_fix_kernel(float* __restrict__ dh, const float* __restrict__ rs,
-                                                          const float* __restrict__ qs,
-                                                          const int32_t* __restrict__ tgt,
-                                                          const bf16* __restrict__ U, int64_t M, int d, int V) {
-  typedef float f32x4_t __attribute__((ext_vector_type(4)));
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
-  const float r = rs[row], q = qs[row];
-  const int y = tgt[row];
-  const bool hit = (uint32_t)y < (uint32_t)V;
-  for (int col = lane * 4; col < d; col += 256) {
-    f32x4_t* p = reinterpret_cast<f32x4_t*>(dh + row * d + col);
-    f32x4_t v = __builtin_nontemporal_load(p) * r;
-    if (hit) {
-      const uint2 u = *reinterpret_cast<const uint2*>(U + (int64_t)y * d + col);
-      v.x -= q * __uint_as_float(u.x << 16);
-      v.y -= q * __uint_as_float(u.x & 0xffff0000u);
-      v.z -= q * __uint_as_float(u.y << 16);
-      v.w -= q * __uint_as_float(u.y & 0xffff0000u);
-    }
-    __builtin_nontemporal_store(v, p);
-  }
-}
-
 int validate(const void* h, const void* U, int dtype, const int32_t* tgt, int64_t M, int d, int V) {
   NC_REQUIRE(h && U && tgt, NC_ERR_INVALID_ARG, "softcap_xent: null pointer");
   NC_REQUIRE(M > 0 && d > 0 && V > 0, NC_ERR_INVALID_ARG, "softcap_xent: bad shape");
@@ -384,13 +358,14 @@ int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
   const size_t esz = dtype == NC_BF16 ? 2 : 4;
   if (dtype == NC_BF16) NC_TRY(transpose(U, V, d, 2, w.ut, s));
   if (fused && from_stored) {
-    NC_REQUIRE(nch == 1 && !dh_acc, NC_ERR_INVALID_ARG,
-               "softcap_xent_bwd: the stored path needs a one-chunk vocabulary and a fresh dh");
+    NC_REQUIRE(nch == 1 && !dh_acc && defer_fix, NC_ERR_INVALID_ARG,
+               "softcap_xent_bwd: the stored path needs a one-chunk vocabulary, a fresh dh and a deferred row fix");
     const unsigned rb = (unsigned)cdiv(M, 4);
     xent_rowscale_kernel<<<rb, 256, 0, s>>>(static_cast<const bf16*>(h), lse, w.ztgt, w.err, tgt, M, d, V, softcap,
                                             dloss, w.rs, w.qs, static_cast<bf16*>(w.hs));
     NC_TRY(check_launch("xent_rowscale_kernel"));
-    // dh = r (u U) - q U[y]: the product through U^T (K-contiguous), then the row fix
+    // dh = r (u U) - q U[y]: the product through U^T (K-contiguous); the row
+    // fix goes to the caller, whose norm backward applies it as it reads dh
     GemmDesc gh;
     gh.transA = 0;
     gh.transB = 1;
@@ -408,12 +383,7 @@ int xent_bwd(const void* h, const void* U, int dtype, const int32_t* tgt, const 
     gh.ws = w.gemm_ws;
     gh.ws_bytes = w.gemm_ws_bytes;
     NC_TRY(gemm(gh, s));
-    if (defer_fix) {
-      *defer_fix = GradRowFix{w.rs, w.qs, tgt, static_cast<const bf16*>(U), V};
-    } else {
-      xent_dh_fix_kernel<<<rb, 256, 0, s>>>(dh, w.rs, w.qs, tgt, static_cast<const bf16*>(U), M, d, V);
-      NC_TRY(check_launch("xent_dh_fix_kernel"));
-    }
+    *defer_fix = GradRowFix{w.rs, w.qs, tgt, static_cast<const bf16*>(U), V};
     // dU (+)= u^T (r h), then dU[y_t] -= q_t h_t in target order
     GemmDesc gu;
     gu.transA = 1;
