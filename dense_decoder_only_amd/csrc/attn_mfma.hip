@@ -272,7 +272,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) bf16 Ds0[QTILE];
   __shared__ __attribute__((aligned(16))) bf16 Ds1[QTILE];
   // P of the current tile: [key wave][8 float4 of a lane][64 lanes]
-  __shared__ __attribute__((aligned(16))) float4 Pex[4 * 8 * 64];
+  __shared__ __attribute__((aligned(16))) float4 Pex[4 * (QT / 8) * 64];
   __shared__ __attribute__((aligned(16))) float lse_s[2][QT];
   __shared__ __attribute__((aligned(16))) float D_s[2][QT];
   __shared__ __attribute__((aligned(16))) int tpos_s[2][QT];
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               const float y = fmaf(x[qt][4 * g4 + e], a.scale_log2, -Lv[e]);
               x[qt][4 * g4 + e] = fexp2(myu > tv[e] ? -INFINITY : y);
             }
-            Pex[(w * 8 + qt * 4 + g4) * 64 + lane] =
+            Pex[(w * (4 * NQT) + qt * 4 + g4) * 64 + lane] =
                 make_float4(x[qt][4 * g4], x[qt][4 * g4 + 1], x[qt][4 * g4 + 2], x[qt][4 * g4 + 3]);
           }
       } else {
@@ -482,7 +482,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const float Lv[4] = {L.x, L.y, L.z, L.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[qt][4 * g4 + e] = fexp2(fmaf(x[qt][4 * g4 + e], a.scale_log2, -Lv[e]));
-            Pex[(w * 8 + qt * 4 + g4) * 64 + lane] =
+            Pex[(w * (4 * NQT) + qt * 4 + g4) * 64 + lane] =
                 make_float4(x[qt][4 * g4], x[qt][4 * g4 + 1], x[qt][4 * g4 + 2], x[qt][4 * g4 + 3]);
           }
       }
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 P4 = Pex[(w * 8 + qt * 4 + g4) * 64 + lane];
+          const float4 P4 = Pex[(w * (4 * NQT) + qt * 4 + g4) * 64 + lane];
           const float4 D4 = *reinterpret_cast<const float4*>(&D_s[cur][qt * 32 + 8 * g4 + 4 * h]);
           x[qt][4 * g4] = P4.x * (x[qt][4 * g4] - D4.x);
           x[qt][4 * g4 + 1] = P4.y * (x[qt][4 * g4 + 1] - D4.y);

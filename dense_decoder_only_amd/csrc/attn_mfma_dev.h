@@ -13,8 +13,11 @@ constexpr int HD = 128;
 constexpr int QB = 128;   // query rows per forward / dQ block (4 waves x 32)
 constexpr int KT = 64;    // keys per tile
 constexpr int KB = 128;   // keys per dK/dV block (4 waves x 32)
-constexpr int QT = 64;    // query rows per dK/dV tile
-constexpr int QCH_MIN = 5120;   // query rows per dK/dV split when the key blocks alone are too few
+constexpr int QT = 96;    // query rows per dK/dV tile (3 x 32)
+// query rows per dK/dV split when the key blocks alone are too few; a multiple
+// of QT, so that the splits of a key block cover its rows in whole tiles
+constexpr int QCH_MIN = 5184;
+static_assert(QCH_MIN % QT == 0, "dK/dV splits must be whole query tiles");
 constexpr int DKV_BLOCKS = 512; // dK/dV blocks aimed at: two rounds of one block per CU
 #ifndef NC_FWD_PF
 #define NC_FWD_PF 3       // forward: K fragments in the score read ring
