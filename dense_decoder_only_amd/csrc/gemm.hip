@@ -919,13 +919,10 @@ __device__ __forceinline__ void pipe_stage_buf(const MfmaParams& p, int m0, int 
   }
 }
 
-template <bool TN, int OP>
-__device__ __forceinline__ void pipe_stage_one(const MfmaParams& p, int r0, int k0, bf16* buf, int wave,
-                                               const uint32_t (&o)[4]) {
-  const bf16* P = OP == 0 ? p.A : p.B;
-  const int64_t ld = OP == 0 ? p.lda : p.ldb;
-  const bf16* pa = TN ? P + (int64_t)k0 * ld + r0 : P + (int64_t)r0 * ld + k0;
-  const __amdgpu_buffer_rsrc_t ra = tile_rsrc(pa);
+// One operand's half of a stage from a tile corner already offset to its k-tile.
+template <bool TN>
+__device__ __forceinline__ void pipe_stage_src(const bf16* src, bf16* buf, int wave, const uint32_t (&o)[4]) {
+  const __amdgpu_buffer_rsrc_t ra = tile_rsrc(src);
   const int step = TN ? 2 * TROW : 8 * BK;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -973,6 +970,42 @@ constexpr int pipe_nreads() { return TN ? 12 : 6; }
 // form below (pipe_stage_buf, stage_direct8, stage_tn).
 constexpr int kWaitFirstStage = 8 | (7 << 4) | (15 << 8);
 
+#ifndef NC_GEMM_XPF
+#define NC_GEMM_XPF 1  // persistent blocks DMA the next work item's first k-tiles under the current one's last
+#endif
+
+
+// Work item -> (tile row, tile column, k-split) of the persistent kernel.
+__device__ __forceinline__ void pipe_item(const MfmaParams& p, int item, int nb, int& tm, int& tn, int& split) {
+  int bid = item;
+#if NC_GEMM_XCD
+  if (p.kxcd) {
+    // Split-K with a multiple of 8 splits: give every XCD whole k-splits
+    // (split s on XCD s mod 8): an XCD then reads only its own k-ranges of
+    // the panels, and its tiles (in the grouped order below) share those
+    // ranges in its L2.
+    const int j = bid >> 3;
+    split = (bid & 7) + 8 * (j / nb);
+    bid = j % nb;
+  } else {
+    split = bid / nb;
+    bid -= split * nb;
+    const int per = nb >> 3;
+    if (bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
+  }
+  const int gsize = NC_GEMM_GROUP_M * p.tiles_n;
+  const int first_m = (bid / gsize) * NC_GEMM_GROUP_M;
+  const int gm = min(p.tiles_m - first_m, NC_GEMM_GROUP_M);
+  tm = first_m + (bid % gsize) % gm;
+  tn = (bid % gsize) / gm;
+#else
+  split = bid / nb;
+  bid -= split * nb;
+  tm = bid % p.tiles_m;
+  tn = bid / p.tiles_m;
+#endif
+}
+
 template <int EPI, bool TN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pipe_kernel(MfmaParams p) {
   // The two stages of each operand are separate LDS objects and the k loop
@@ -999,33 +1032,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // dealt round-robin to the 8 XCDs and gridDim.x is a multiple of 8, so
   // item f still runs on XCD f mod 8.
   const int nb = p.tiles_m * p.tiles_n;
-  for (int item = blockIdx.x; item < nb * p.splits; item += gridDim.x) {
-  int bid = item, split = 0;
+  const int nitems = nb * p.splits;
+  // pf_in: this item's first k-tile (stage 0) was DMA'd under the previous
+  // item's last k-tile.
+  bool pf_in = false;
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+  int tm, tn, split;
+  pipe_item(p, item, nb, tm, tn, split);
   float* cpart = static_cast<float*>(p.C);  // E_PARTIAL: this split's [M][N] slice
-#if NC_GEMM_XCD
-  if (p.kxcd) {
-    // Split-K with a multiple of 8 splits: give every XCD whole k-splits
-    // (split s on XCD s mod 8): an XCD then reads only its own k-ranges of
-    // the panels, and its tiles (in the grouped order below) share those
-    // ranges in its L2.
-    const int j = bid >> 3;
-    split = (bid & 7) + 8 * (j / nb);
-    bid = j % nb;
-  } else {
-    split = bid / nb;
-    bid -= split * nb;
-    const int per = nb >> 3;
-    if (bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
-  }
-  const int gsize = NC_GEMM_GROUP_M * p.tiles_n;
-  const int first_m = (bid / gsize) * NC_GEMM_GROUP_M;
-  const int gm = min(p.tiles_m - first_m, NC_GEMM_GROUP_M);
-  const int tm = first_m + (bid % gsize) % gm, tn = (bid % gsize) / gm;
-#else
-  split = bid / nb;
-  bid -= split * nb;
-  const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
-#endif
   if constexpr (EPI == E_PARTIAL) cpart += (int64_t)split * p.M * p.N;
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = split * p.k_per_split;
@@ -1033,6 +1047,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   kend = kend < p.K ? kend : p.K;
   const int nk = (kend - kbeg) / BK;
   const int klast = kbeg + (nk - 1) * BK;
+  // The k loop DMAs two k-tiles past its last one (into the stages the loop
+  // order gives them).  With an even k-tile count those are stage 0 (both
+  // operands) and stage 1 (A), where the next item's loop expects its first
+  // tile and its second tile's A: they then carry that item's data instead of
+  // repeating this item's last tile, and the next item starts its products
+  // without a prologue.  Both tiles must be whole, so that they share this
+  // item's per-lane offsets (the row clamps at the matrix edge are the only
+  // difference between tiles).
+  // Tile corners (at this item's first k-tile) and the step from one k-tile
+  // to the next, per operand.  The k loop DMAs two k-tiles past the last
+  // one: "nxt" is where the first of them reads (stage 0, which the next
+  // item's loop starts from: its first k-tile, or this item's last one again
+  // when there is no prefetch), and the second repeats this item's last
+  // k-tile (an L2 hit that the end of the loop waits for).
+  const int64_t ksa = TN ? (int64_t)BK * p.lda : BK, ksb = TN ? (int64_t)BK * p.ldb : BK;
+  const bf16* const a_cur = TN ? p.A + (int64_t)kbeg * p.lda + m0 : p.A + (int64_t)m0 * p.lda + kbeg;
+  const bf16* const b_cur = TN ? p.B + (int64_t)kbeg * p.ldb + n0 : p.B + (int64_t)n0 * p.ldb + kbeg;
+  const bf16* const a_last = a_cur + (nk - 1) * ksa;
+  const bf16* a_nxt = a_last;
+  const bf16* b_nxt = b_cur + (nk - 1) * ksb;
+  bool pf_out = false;
+#if NC_GEMM_XPF
+  if (item + (int)gridDim.x < nitems) {
+    int tmn, tnn, spn;
+    pipe_item(p, item + gridDim.x, nb, tmn, tnn, spn);
+    const int m0n = tmn * BM, n0n = tnn * BN, kbegn = spn * p.k_per_split;
+    // even k-tile count: the first DMA past the end lands in stage 0.  Whole
+    // tiles: the next item's per-lane offsets equal this item's (the row
+    // clamps at the matrix edge are the only difference between tiles).
+    pf_out = (nk & 1) == 0 && kbegn < p.K && m0 + BM <= p.M && n0 + BN <= p.N && m0n + BM <= p.M &&
+             n0n + BN <= p.N;
+    if (pf_out) {
+      a_nxt = TN ? p.A + (int64_t)kbegn * p.lda + m0n : p.A + (int64_t)m0n * p.lda + kbegn;
+      b_nxt = TN ? p.B + (int64_t)kbegn * p.ldb + n0n : p.B + (int64_t)n0n * p.ldb + kbegn;
+    }
+  }
+#endif
+  // corner of virtual k-tile v of this item (v >= nk: past its end)
+  auto src_a = [&](int v) { return v < nk ? a_cur + v * ksa : (v == nk ? a_nxt : a_last); };
+  auto src_b = [&](int v) { return v < nk ? b_cur + v * ksb : b_nxt; };
   if constexpr (XENT) {
     if (tid < BM) {
       const int r = m0 + tid;
@@ -1051,15 +1105,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   StageOff so;
   stage_offsets<TN>(p, m0, n0, wave, lane, so);
-  pipe_stage_buf<TN>(p, m0, n0, kbeg, sA0, sB0, wave, so);
-  pipe_stage_buf<TN>(p, m0, n0, nk > 1 ? kbeg + BK : kbeg, sA1, sB1, wave, so);
-  // Only the first stage has to have landed here (vmcnt <= the 8 DMAs of the
-  // second stage per wave, expcnt and lgkmcnt not waited on): the second
-  // one is waited for at the barrier inside the first k-tile.  A plain
-  // s_barrier, not __syncthreads: the latter's release fence would wait for
-  // every outstanding load, the second stage's DMA included.  The empty asm
-  // keeps the compiler from moving the first fragment reads above it.
-  __builtin_amdgcn_s_waitcnt(kWaitFirstStage);
+  if (!pf_in) {
+    pipe_stage_buf<TN>(p, m0, n0, kbeg, sA0, sB0, wave, so);
+    pipe_stage_buf<TN>(p, m0, n0, nk > 1 ? kbeg + BK : kbeg, sA1, sB1, wave, so);
+    // Only the first stage has to have landed here (vmcnt <= the 8 DMAs of
+    // the second stage per wave, expcnt and lgkmcnt not waited on): the
+    // second one is waited for at the barrier inside the first k-tile.
+    __builtin_amdgcn_s_waitcnt(kWaitFirstStage);
+  } else {
+    // the first stage arrived under the previous item's last k-tile
+    pipe_stage_buf<TN>(p, m0, n0, nk > 1 ? kbeg + BK : kbeg, sA1, sB1, wave, so);
+  }
+  // A plain s_barrier, not __syncthreads: the latter's release fence would
+  // wait for every outstanding load, the second stage's DMA included.  The
+  // empty asm keeps the compiler from moving the first fragment reads above
+  // it.
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
@@ -1073,14 +1133,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // the block is past its last reads: A right after the barrier in tile kt's
   // last k-step, B in tile kt + 1's first k-step (where this lambda issues B
   // of tile kt + 1 into b_o, released at the previous tile's barrier).
-  auto k_tile = [&](const int kt, bf16* a_c, bf16* b_c, bf16* a_o, bf16* b_o) {
+  auto k_tile = [&](const int kt, bf16* a_c, bf16* b_c, bf16* a_o, bf16* b_o, const bf16* src_b1,
+                    const bf16* src_a2) {
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
       const int c = ks & 1;
-      if (ks == 0) {  // (tile 1's B repeats the prologue's DMA: same data)
-        const int k1 = kt + 1 < nk ? kbeg + (kt + 1) * BK : klast;
-        pipe_stage_one<TN, 1>(p, n0, k1, b_o, wave, so.b);
-      }
+      if (ks == 0)  // (tile 1's B repeats the prologue's DMA: same data)
+        pipe_stage_src<TN>(src_b1, b_o, wave, so.b);
       pipe_frags<TN>(a_c, b_c, ks + 1, wm, wn, lane, fa[c ^ 1], fb[c ^ 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -1119,8 +1178,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    const int k2 = kt + 2 < nk ? kbeg + (kt + 2) * BK : klast;
-    pipe_stage_one<TN, 0>(p, m0, k2, a_c, wave, so.a);
+    pipe_stage_src<TN>(src_a2, a_c, wave, so.a);
     pipe_frags<TN>(a_o, b_o, 0, wm, wn, lane, fa[0], fb[0]);
 #pragma unroll
     for (int q = NC_GEMM_PIPE_PRE; q < 8; ++q)
@@ -1135,17 +1193,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    k_tile(kt, sA0, sB0, sA1, sB1);
-    k_tile(kt + 1, sA1, sB1, sA0, sB0);
+    k_tile(kt, sA0, sB0, sA1, sB1, src_b(kt + 1), src_a(kt + 2));
+    k_tile(kt + 1, sA1, sB1, sA0, sB0, src_b(kt + 2), src_a(kt + 3));
   }
-  if (kt < nk) k_tile(kt, sA0, sB0, sA1, sB1);
+  if (kt < nk) k_tile(kt, sA0, sB0, sA1, sB1, src_b(kt + 1), src_a(kt + 2));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // epilogue staging: 32 x SROW floats per wave, three waves per 32 KB stage
+  // Epilogue staging: each 32-row block of a wave's accumulators goes through
+  // LDS.  With the cross-item prefetch, stage 0 holds the next item's first
+  // k-tile while this epilogue runs, so the staging is stage 1 (waves 0-3 in
+  // its A, 4-7 in its B): 32 rows x 64 floats per wave, the 16-byte chunks of
+  // row r XOR-swizzled by r mod 16.  Otherwise 32 rows of 68 floats, three
+  // waves per stage.
+#if NC_GEMM_XPF
+  constexpr int SROW = 64;
+  static_assert(4 * 32 * SROW * 4 <= BM * BK * 2, "epilogue staging does not fit stage 1");
+  float* stage = reinterpret_cast<float*>(wave < 4 ? sA1 : sB1) + (wave & 3) * (32 * SROW);
+  auto sidx = [](int row, int c4) { return row * SROW + (((c4 >> 2) ^ (row & 15)) << 2); };
+#else
   constexpr int SROW = 68;
   static_assert(3 * 32 * SROW * 4 <= BM * BK * 2, "epilogue staging does not fit a stage");
   float* stage = reinterpret_cast<float*>(wave < 3 ? sA0 : (wave < 6 ? sA1 : sB0)) + (wave % 3) * (32 * SROW);
+  auto sidx = [](int row, int c4) { return row * SROW + c4; };
+#endif
   // Epilogue inputs read from memory are loaded one 32-row slab ahead of
   // their use, so that their latency overlaps the LDS staging: the relu^2
   // backward's stored activation and the accumulated fp32 C.  Element (i, it) of this lane is row
@@ -1191,7 +1262,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(stage + (lane & 31) * SROW + j * 32 + 8 * q + 4 * (lane >> 5)) =
+        *reinterpret_cast<float4*>(stage + sidx(lane & 31, j * 32 + 8 * q + 4 * (lane >> 5))) =
             make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
     // the staging area is this wave's own: only its lanes' LDS writes have to
     // land before the reads (no block barrier, whose fence would also wait for
@@ -1207,7 +1278,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int it = 0; it < 8; ++it) {
       const int idx = it * 64 + lane;
       const int row = idx >> 4, c4 = (idx & 15) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(stage + row * SROW + c4);
+      const float4 v = *reinterpret_cast<const float4*>(stage + sidx(row, c4));
       const int grow = m0 + wm * 128 + i * 32 + row, gcol = n0 + wn * 64 + c4;
       if constexpr (EPI == E_XENT_FWD) {
         xent_fwd4(p, v, grow, gcol, n0 + wn * 64, s_xt[grow - m0], code);
@@ -1256,6 +1327,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  pf_in = pf_out;
   }
 }
 

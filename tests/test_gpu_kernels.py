@@ -313,6 +313,63 @@ def test_gemm_relu2_epilogues(dtype, K):
                  "relu2 bwd from square")
 
 
+def _sample_rows(M):
+    """Rows spread over every 256-row tile: both wave rows, every 32-row
+    block and both 16-row halves of the epilogue's staging."""
+    rows = [t * 256 + o for t in range((M + 255) // 256) for o in (0, 15, 16, 47, 100, 130, 177, 240, 255)]
+    return np.array(sorted({r for r in rows if r < M}))
+
+
+@pytest.mark.parametrize("ta,tb,M,N,K", [
+    (0, 1, 8192, 4096, 1280),   # 512 whole tiles: two per persistent block, 20 k-tiles (even)
+    (0, 1, 4400, 4160, 1344),   # ragged last tile row and column, 21 k-tiles (odd)
+    (0, 1, 4352, 4608, 640),    # whole tiles, 306 items: some blocks carry two, 10 k-tiles
+    (1, 0, 4608, 4096, 1024),   # both operands with K as rows (weight-gradient form), 288 tiles
+])
+def test_gemm_persistent_blocks_many_items(ta, tb, M, N, K):
+    """Products with more work items than the persistent grid has blocks, so a
+    block runs several tiles in a row (and, where both tiles are whole and the
+    k-tile count is even, DMAs the next tile's first k-tiles under the
+    current one's last).  Sampled rows against a float64 product of the same
+    bf16 operands, for the store, accumulate, bf16 and relu^2 epilogues."""
+    n = nc()
+    r = rng(M + N + K)
+    A = r.standard_normal((K, M) if ta else (M, K))
+    Bm = r.standard_normal((N, K) if tb else (K, N))
+    Ad, Bd = to_dev(A, BF16), to_dev(Bm, BF16)
+    rows = _sample_rows(M)
+    A64 = dev_to_f64(Ad)
+    A_rows = (A64.T if ta else A64)[rows]
+    B64 = dev_to_f64(Bd)
+    ref = A_rows @ (B64.T if tb else B64)
+    lda, ldb = (M if ta else K), (K if tb else N)
+    C = torch.full((M, N), float("nan"), dtype=F32, device=DEV)
+    n.nc_gemm_bf16(ta, tb, M, N, K, Ad, lda, Bd, ldb, C, N)
+    sync()
+    assert_close(dev_to_f64(C[rows]), ref, 1e-4, 1e-5, "gemm fp32 out, many items")
+    assert torch.isfinite(C).all(), "unwritten output elements"
+    C0 = to_dev(r.standard_normal((M, N)), F32)
+    C1 = C0.clone()
+    n.nc_gemm_bf16(ta, tb, M, N, K, Ad, lda, Bd, ldb, C1, N, beta=1.0)
+    sync()
+    assert_close(dev_to_f64(C1[rows]), dev_to_f64(C0[rows]) + ref, 1e-4, 1e-5, "gemm accumulate, many items")
+    Cb = torch.empty((M, N), dtype=BF16, device=DEV)
+    n.nc_gemm_bf16(ta, tb, M, N, K, Ad, lda, Bd, ldb, Cb, N)
+    sync()
+    assert_close(dev_to_f64(Cb[rows]), ref, 2 ** -8, 1e-5, "gemm bf16 out, many items")
+    if ta == 0 and tb == 1:
+        a2s = torch.empty((M, N), dtype=BF16, device=DEV)
+        n.nc_gemm_bf16(0, 1, M, N, K, Ad, K, Bd, K, a2s, N, epilogue=n.NC_EPI_RELU2_SQ)
+        sync()
+        assert_close(dev_to_f64(a2s[rows]), oracle.relu2(ref), 2 ** -7, 1e-5, "relu2 square only, many items")
+        aux_sq = to_dev(oracle.relu2(r.standard_normal((M, N))), BF16)
+        Cg = torch.empty((M, N), dtype=BF16, device=DEV)
+        n.nc_gemm_bf16(0, 1, M, N, K, Ad, K, Bd, K, Cg, N, epilogue=n.NC_EPI_RELU2_BWD_SQ, aux=aux_sq)
+        sync()
+        assert_close(dev_to_f64(Cg[rows]), oracle.relu2_bwd(ref, np.sqrt(dev_to_f64(aux_sq[rows]))), 2 ** -8, 1e-5,
+                     "relu2 bwd from square, many items")
+
+
 def test_gemm_split_k_is_deterministic():
     n = nc()
     M, N, K = 256, 520, 16384
