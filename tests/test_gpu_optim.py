@@ -92,6 +92,7 @@ def _loop(cfg, batch, steps, lr):
     om = {k: np.zeros_like(op[k]) for k in PARAM_NAMES}
     ov = {k: np.zeros_like(op[k]) for k in PARAM_NAMES}
     olosses = []
+    g1 = None  # the oracle's first-step gradients
     for t in range(1, steps + 1):
         nc.nc_step_fwd_bwd(ccfg, params, grads, 0, ids, tgt, tb, ws, loss, bpb)
         losses.append(float(loss))
@@ -99,14 +100,16 @@ def _loop(cfg, batch, steps, lr):
             nc.nc_adamw_step(master[k], m[k], v[k], grads[k], params[k] if bf16 else None, t, lr, **HP)
         ref = oracle.step(c, op, inp["ids"], inp["targets"], inp["token_bytes"])
         olosses.append(ref["loss"])
+        if g1 is None:
+            g1 = ref["grads"]
         for k in PARAM_NAMES:
             op[k], om[k], ov[k] = oracle.adamw_step(op[k], ref["grads"][k], om[k], ov[k], t, lr, **HP)
     assert nc.nc_sync_status(ws) == nc.NC_OK
-    return np.array(losses), np.array(olosses), master, op
+    return np.array(losses), np.array(olosses), master, op, g1
 
 
 def test_training_loop_tiny_fp32():
-    losses, olosses, master, op = _loop(CONFIGS["tiny"], CONFIGS["tiny"].batch, 5, 1e-3)
+    losses, olosses, master, op, _ = _loop(CONFIGS["tiny"], CONFIGS["tiny"].batch, 5, 1e-3)
     np.testing.assert_allclose(losses, olosses, rtol=1e-4)
     assert np.all(np.diff(olosses) < 0) and np.all(np.diff(losses) < 0), losses  # same batch: loss falls
     w0 = oracle.to_f64_params(make_inputs(CONFIGS["tiny"])["weights"])
@@ -125,18 +128,31 @@ def test_training_loop_tiny_fp32():
 
 
 def test_training_loop_small_bf16():
-    losses, olosses, master, op = _loop(CONFIGS["small"], 1, 3, 1e-3)
+    losses, olosses, master, op, g1 = _loop(CONFIGS["small"], 1, 3, 1e-3)
     np.testing.assert_allclose(losses, olosses, rtol=3e-3)
     assert np.all(np.diff(losses) < 0), losses
+    w0 = oracle.to_f64_params(make_inputs(CONFIGS["small"], 1)["weights"])
     for k in PARAM_NAMES:
         # Adam steps are ~lr in size whatever the gradient, so a weight whose
-        # gradient is near zero may step either way: compare the updates in
-        # aggregate (cosine) and bound the largest difference by a few lr.
-        d_got = dev_to_f64(master[k]) - oracle.to_f64_params(make_inputs(CONFIGS["small"], 1)["weights"])[k]
-        d_ref = op[k] - oracle.to_f64_params(make_inputs(CONFIGS["small"], 1)["weights"])[k]
+        # gradient is near zero (below the bf16 step's rounding of it) may
+        # step either way: over all weights the updates are compared in
+        # aggregate and the largest difference is bounded by a few lr.  Where
+        # the first step's gradient is at least a tenth of the tensor's RMS
+        # gradient, its sign is not in doubt, and there the updates must agree
+        # closely.
+        d_got, d_ref = dev_to_f64(master[k]) - w0[k], op[k] - w0[k]
         cos = float(np.sum(d_got * d_ref) / np.sqrt(np.sum(d_got ** 2) * np.sum(d_ref ** 2)))
-        assert cos > 0.95, (k, cos)
+        sel = np.abs(g1[k]) >= 0.1 * np.sqrt(np.mean(g1[k] ** 2))
+        a, b = d_got[sel], d_ref[sel]
+        cos_sel = float(np.sum(a * b) / np.sqrt(np.sum(a ** 2) * np.sum(b ** 2)))
+        print(k, "cos", cos, "confident fraction", sel.mean(), "cos there", cos_sel,
+              "max diff there / lr", np.abs(a - b).max() / 1e-3)
+        # measured: cos 0.99903-0.99991, there 0.99997-0.999996, at most 0.66 lr
+        assert cos > 0.998, (k, cos)
         assert np.max(np.abs(d_got - d_ref)) <= 6 * 1e-3 + 1e-6, k
+        assert sel.sum() >= 1000, (k, int(sel.sum()))  # (the embedding's gradient is sparse: few rows)
+        assert cos_sel > 0.9995, (k, cos_sel)
+        assert np.abs(a - b).max() <= 1e-3, k
 
 
 def test_gradient_accumulation_tiny():
