@@ -58,5 +58,7 @@ bool skinny_ok(const GemmDesc& g);
 int gemm_skinny(const GemmDesc& g, hipStream_t stream);
 // dst [C, R] = src [R, C]^T for 2- or 4-byte elements.
 int transpose(const void* src, int64_t R, int64_t C, int elem_bytes, void* dst, hipStream_t s);
+// n (1..4) bf16 matrices [R_i, C_i] -> [C_i, R_i] in one launch (sides multiples of 8, 16-byte aligned).
+int transpose4(const void* const* src, const int64_t* R, const int64_t* C, void* const* dst, int n, hipStream_t s);
 
 }  // namespace nc

@@ -862,7 +862,7 @@ __device__ __forceinline__ bf16x8_t frag_tn(const bf16* S, int ks, int col0, int
 // full.
 // ---------------------------------------------------------------------------
 #ifndef NC_GEMM_PIPE_PRE
-#define NC_GEMM_PIPE_PRE 2  // MFMAs of the last k-step issued before the barrier
+#define NC_GEMM_PIPE_PRE 1  // MFMAs of the last k-step issued before the barrier
 #endif
 
 // Staging of the pipelined kernel: per stage a scalar buffer resource at the
@@ -1689,10 +1689,38 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
 // 8-element pieces t and t + 256 of the tile: on the way in, piece id is
 // row id / 8 of the tile, columns 8 (id % 8) ..; on the way out, output row
 // id / 8 (a tile column), output columns 8 (id % 8) .. (eight tile rows).
+// Up to four 2-byte matrices transposed by one launch (a layer's weights):
+// block b takes 64 x 64 tile b - first[i] of the job i whose range holds b.
+struct TransposeJobs {
+  const uint16_t* src[4];
+  uint16_t* dst[4];
+  int64_t R[4], C[4];
+  int first[5];  // first block of each job; first[n] = blocks in all
+  int tiles_c[4];
+};
+
+__device__ __forceinline__ void transpose_b16x8_tile(const uint16_t* __restrict__ src, int64_t R, int64_t C,
+                                                     uint16_t* __restrict__ dst, int64_t r0, int64_t c0,
+                                                     uint16_t (&tile)[64][72]);
+
+__global__ __launch_bounds__(256) void transpose_b16x8_batch_kernel(TransposeJobs jb) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+  const int b = blockIdx.x;
+  const int i = b < jb.first[1] ? 0 : (b < jb.first[2] ? 1 : (b < jb.first[3] ? 2 : 3));
+  const int k = b - jb.first[i];
+  const int64_t r0 = (int64_t)(k / jb.tiles_c[i]) * 64, c0 = (int64_t)(k % jb.tiles_c[i]) * 64;
+  transpose_b16x8_tile(jb.src[i], jb.R[i], jb.C[i], jb.dst[i], r0, c0, tile);
+}
+
 __global__ __launch_bounds__(256) void transpose_b16x8_kernel(const uint16_t* __restrict__ src, int64_t R, int64_t C,
                                                               uint16_t* __restrict__ dst) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // rows 144 bytes apart
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  transpose_b16x8_tile(src, R, C, dst, (int64_t)blockIdx.y * 64, (int64_t)blockIdx.x * 64, tile);
+}
+
+__device__ __forceinline__ void transpose_b16x8_tile(const uint16_t* __restrict__ src, int64_t R, int64_t C,
+                                                     uint16_t* __restrict__ dst, int64_t r0, int64_t c0,
+                                                     uint16_t (&tile)[64][72]) {
   const int t = threadIdx.x;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -1714,6 +1742,34 @@ __global__ __launch_bounds__(256) void transpose_b16x8_kernel(const uint16_t* __
 }
 
 }  // namespace
+
+int transpose4(const void* const* src, const int64_t* R, const int64_t* C, void* const* dst, int n, hipStream_t s) {
+  NC_REQUIRE(n >= 1 && n <= 4, NC_ERR_INVALID_ARG, "transpose4: 1 to 4 matrices");
+  bool whole = true;  // every matrix fits the 16-byte form
+  for (int i = 0; i < n; ++i) {
+    NC_REQUIRE(src[i] && dst[i] && R[i] > 0 && C[i] > 0, NC_ERR_INVALID_ARG, "transpose4: bad arguments");
+    whole = whole && R[i] % 8 == 0 && C[i] % 8 == 0 && aligned16(src[i]) && aligned16(dst[i]) &&
+            cdiv(R[i], 64) * cdiv(C[i], 64) < ((int64_t)1 << 28);
+  }
+  if (!whole) {
+    for (int i = 0; i < n; ++i) NC_TRY(transpose(src[i], R[i], C[i], 2, dst[i], s));
+    return NC_OK;
+  }
+  TransposeJobs jb{};
+  int blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    jb.src[i] = static_cast<const uint16_t*>(src[i]);
+    jb.dst[i] = static_cast<uint16_t*>(dst[i]);
+    jb.R[i] = R[i];
+    jb.C[i] = C[i];
+    jb.tiles_c[i] = (int)cdiv(C[i], 64);
+    jb.first[i] = blocks;
+    blocks += (int)(cdiv(R[i], 64) * jb.tiles_c[i]);
+  }
+  for (int i = n; i <= 4; ++i) jb.first[i] = blocks;
+  transpose_b16x8_batch_kernel<<<blocks, 256, 0, s>>>(jb);
+  return check_launch("transpose_b16x8_batch_kernel");
+}
 
 int transpose(const void* src, int64_t R, int64_t C, int elem_bytes, void* dst, hipStream_t s) {
   NC_REQUIRE(src && dst && R > 0 && C > 0, NC_ERR_INVALID_ARG, "transpose: bad arguments");

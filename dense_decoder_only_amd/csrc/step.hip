@@ -352,10 +352,10 @@ int step_fwd_bwd(const nc_config* c, const nc_params* p, const nc_grads* gr, con
     const void* W1 = wl(p->w_fc, l, F * d);
     const void* W2 = wl(p->w_proj, l, d * F);
     if (tw) {
-      NC_TRY(transpose(Wqkv, Q, d, 2, WqkvT, s));
-      NC_TRY(transpose(Wo, d, HD, 2, WoT, s));
-      NC_TRY(transpose(W1, F, d, 2, W1T, s));
-      NC_TRY(transpose(W2, d, F, 2, W2T, s));
+      const void* srcs[4] = {Wqkv, Wo, W1, W2};
+      void* dsts[4] = {WqkvT, WoT, W1T, W2T};
+      const int64_t rs[4] = {Q, d, F, d}, cs[4] = {d, HD, d, F};
+      NC_TRY(transpose4(srcs, rs, cs, dsts, 4, s));
     }
     // MLP: x_out = x_mid + relu(m W1^T)^2 W2^T
     void* gop = gop_of(gv);
